@@ -1,0 +1,171 @@
+"""Python binding of librmsq (fused RMSNorm + FP8 / FP4 quantization on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of librmsq.so, reached through the C ABI declared in include/rmsq.h.
+torch provides device memory and the current stream.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+
+Functions mirror the C entry points:
+  rmsnorm_fp8(x, gamma, ...)                   -> (codes, scales)
+  residual_rmsnorm_fp8(x, residual, gamma, ...) -> (codes, scales, residual_out)
+  rmsnorm_fp4(x, gamma, ...)                   -> (packed_codes, block_scales)
+  convert(kind, src, dst)
+Tensors may have any number of leading dimensions; the last one is hidden.
+Outputs are allocated (uint8 / scale dtype) when not given.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librmsq.so")
+
+# enums of include/rmsq.h
+F32, F16, BF16 = 0, 1, 2
+E4M3FN, E4M3FNUZ = 0, 1
+CVT_F32_TO_E4M3FN, CVT_F32_TO_E4M3FNUZ, CVT_F32_TO_E2M1, CVT_F32_TO_BF16, CVT_F32_TO_F16, CVT_E4M3FN_TO_F32 = range(6)
+STATUS = {0: "RMSQ_OK", -1: "RMSQ_ERR_NULL", -2: "RMSQ_ERR_DTYPE", -3: "RMSQ_ERR_SHAPE", -4: "RMSQ_ERR_ALIGN",
+          -5: "RMSQ_ERR_VALUE", -6: "RMSQ_ERR_ALIAS", -7: "RMSQ_ERR_UNSUPPORTED", -8: "RMSQ_ERR_LAUNCH"}
+
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_FMT = {"e4m3fn": E4M3FN, "e4m3fnuz": E4M3FNUZ}
+
+_lib = None
+
+
+class RmsqError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{fn} failed: {STATUS.get(status, status)}"
+        if status == -8:
+            msg += f" (hipError_t {hip_error})"
+        super().__init__(msg)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librmsq.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m fp4_activation_quantization_amd.build` "
+                           "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.rmsnorm_fp8.argtypes = [I64, I64, I, P, P, F, F, F, I, P, I, P, P]
+    L.residual_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, P, F, F, F, I, P, I, P, P]
+    L.rmsnorm_fp4.argtypes = [I64, I64, I, P, P, F, F, P, P, P, P]
+    L.rmsq_convert.argtypes = [I, P, P, I64, P]
+    L.rmsq_set_tuning.argtypes = [I, I, I]
+    L.rmsq_query_shape.argtypes = [I64, I64, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)]
+    L.rmsq_status_string.argtypes = [I]
+    L.rmsq_status_string.restype = ctypes.c_char_p
+    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsq_convert", "rmsq_set_tuning",
+               "rmsq_query_shape", "rmsq_abi_version", "rmsq_last_hip_error"):
+        getattr(L, fn).restype = I
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise RmsqError(fn, status, lib().rmsq_last_hip_error() if status == -8 else 0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows_hidden(x: torch.Tensor):
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    hidden = x.shape[-1] if x.dim() else 0
+    rows = x.numel() // hidden if hidden else 0
+    return rows, hidden
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    return t if t.dtype == torch.uint8 else t.view(torch.uint8)
+
+
+def rmsnorm_fp8(x, gamma, eps=1e-6, weight_offset=0.0, scale_ub=float("inf"), out_fp8="e4m3fn",
+                out=None, scales=None, scales_dtype=torch.float32, stream=None):
+    """RMSNorm + per-row dynamic FP8 (C: rmsnorm_fp8).  Returns (codes uint8 [..., H], scales [...])."""
+    rows, hidden = _rows_hidden(x)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=scales_dtype, device=x.device)
+    _check("rmsnorm_fp8", lib().rmsnorm_fp8(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset,
+                                            scale_ub, _FMT[out_fp8], _ptr(_u8(out)), _DT[scales.dtype],
+                                            _ptr(scales), _stream(x, stream)))
+    return out, scales
+
+
+def residual_rmsnorm_fp8(x, residual, gamma, eps=1e-6, weight_offset=0.0, scale_ub=float("inf"),
+                         out_fp8="e4m3fn", out=None, scales=None, residual_out=None,
+                         scales_dtype=torch.float32, stream=None):
+    """residual_out = x + residual (rounded to x.dtype), then RMSNorm + per-row FP8
+    (C: residual_rmsnorm_fp8).  Returns (codes, scales, residual_out)."""
+    rows, hidden = _rows_hidden(x)
+    if residual.dtype != x.dtype or residual.shape != x.shape:
+        raise ValueError("residual must match x in dtype and shape")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=scales_dtype, device=x.device)
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    _check("residual_rmsnorm_fp8",
+           lib().residual_rmsnorm_fp8(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out),
+                                      _ptr(gamma), eps, weight_offset, scale_ub, _FMT[out_fp8], _ptr(_u8(out)),
+                                      _DT[scales.dtype], _ptr(scales), _stream(x, stream)))
+    return out, scales, residual_out
+
+
+def rmsnorm_fp4(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, out=None, block_scales=None,
+                stream=None):
+    """RMSNorm + FP4 E2M1 with one E4M3 scale per 16 elements (C: rmsnorm_fp4).
+
+    global_scale: a float32 device tensor of one element, or None (1.0).
+    Returns (packed uint8 [..., H/2], block_scales uint8 [..., H/16]).
+    """
+    rows, hidden = _rows_hidden(x)
+    if out is None:
+        out = torch.empty((*x.shape[:-1], hidden // 2), dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        block_scales = torch.empty((*x.shape[:-1], hidden // 16), dtype=torch.uint8, device=x.device)
+    if global_scale is not None and (global_scale.dtype != torch.float32 or global_scale.numel() != 1):
+        raise ValueError("global_scale must be a one-element float32 tensor")
+    _check("rmsnorm_fp4", lib().rmsnorm_fp4(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset,
+                                            _ptr(global_scale), _ptr(_u8(out)), _ptr(_u8(block_scales)),
+                                            _stream(x, stream)))
+    return out, block_scales
+
+
+def convert(kind: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """Elementwise device conversion (C: rmsq_convert); n = src.numel()."""
+    _check("rmsq_convert", lib().rmsq_convert(kind, _ptr(src), _ptr(dst), src.numel(), _stream(src, stream)))
+    return dst
+
+
+def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, max_blocks: int = 0) -> None:
+    """Process-wide launch-shape override (0 = automatic)."""
+    _check("rmsq_set_tuning", lib().rmsq_set_tuning(waves_per_row, vectors_per_lane, max_blocks))
+
+
+def query_shape(rows: int, hidden: int, dtype: torch.dtype, fp4: bool = False) -> dict:
+    w, v, r = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check("rmsq_query_shape", lib().rmsq_query_shape(rows, hidden, _DT[dtype], int(fp4), ctypes.byref(w),
+                                                      ctypes.byref(v), ctypes.byref(r)))
+    return {"waves_per_row": w.value, "vectors_per_lane": v.value, "rows_per_block": r.value}

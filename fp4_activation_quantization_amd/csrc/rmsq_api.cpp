@@ -1,0 +1,278 @@
+// C ABI of librmsq: argument validation, launch-shape choice and dispatch.
+// Every check runs before the first HIP call, so each error path is testable
+// on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/rmsq.h"
+#include "rmsq_internal.h"
+
+namespace rmsq {
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+std::atomic<int> g_tune_waves{0};
+std::atomic<int> g_tune_vpt{0};
+std::atomic<int> g_tune_blocks{0};
+
+// Largest row the register-resident kernels hold: 16 waves x 64 lanes x 4
+// vectors of 16 bytes.
+constexpr int kMaxVec = 16 * 64 * 4;
+
+bool valid_dtype(int dt) { return dt == RMSQ_F32 || dt == RMSQ_F16 || dt == RMSQ_BF16; }
+int64_t elem_size(int dt) { return dt == RMSQ_F32 ? 4 : 2; }
+int64_t elems_per_vec(int dt) { return 16 / elem_size(dt); }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+    Span(const void* p, int64_t bytes)
+        : lo(reinterpret_cast<uintptr_t>(p)), hi(reinterpret_cast<uintptr_t>(p) + (uintptr_t)bytes) {}
+};
+bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// rows * hidden * esz must fit comfortably in int64 (and hidden in int32)
+bool size_ok(int64_t rows, int64_t hidden, int64_t esz) {
+    if (hidden > INT32_MAX / 2) return false;
+    return rows <= (INT64_MAX / 4) / (hidden * esz);
+}
+
+int check_scalars(float eps, float weight_offset, float scale_ub, bool check_ub) {
+    if (!(eps >= 0.0f) || !isfinite(eps)) return RMSQ_ERR_VALUE;
+    if (!isfinite(weight_offset)) return RMSQ_ERR_VALUE;
+    if (check_ub && !(scale_ub > 0.0f)) return RMSQ_ERR_VALUE;  // NaN fails too
+    return RMSQ_OK;
+}
+
+int launched(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return RMSQ_ERR_LAUNCH;
+    }
+    return RMSQ_OK;
+}
+
+int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
+               void* residual_out, bool resid, const void* gamma, float eps, float weight_offset,
+               float scale_ub, int out_fp8, void* out, int scales_dtype, void* scales, hipStream_t stream) {
+    if (!valid_dtype(in_dtype) || !valid_dtype(scales_dtype)) return RMSQ_ERR_DTYPE;
+    if (out_fp8 != RMSQ_E4M3FN && out_fp8 != RMSQ_E4M3FNUZ) return RMSQ_ERR_DTYPE;
+    const int64_t esz = elem_size(in_dtype);
+    if (rows < 0 || hidden <= 0 || hidden % elems_per_vec(in_dtype) != 0) return RMSQ_ERR_SHAPE;
+    if (!size_ok(rows, hidden, esz)) return RMSQ_ERR_SHAPE;
+    if (int rc = check_scalars(eps, weight_offset, scale_ub, true)) return rc;
+    const int nvec = (int)(hidden / elems_per_vec(in_dtype));
+    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    if (rows == 0) return RMSQ_OK;
+    if (!x || !gamma || !out || !scales) return RMSQ_ERR_NULL;
+    if (resid && (!residual || !residual_out)) return RMSQ_ERR_NULL;
+    const int64_t ssz = elem_size(scales_dtype);
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(out, 16) || !aligned(scales, (uintptr_t)ssz))
+        return RMSQ_ERR_ALIGN;
+    if (resid && (!aligned(residual, 16) || !aligned(residual_out, 16))) return RMSQ_ERR_ALIGN;
+
+    const int64_t tbytes = rows * hidden * esz;
+    const Span sx(x, tbytes), sg(gamma, hidden * esz), so(out, rows * hidden), ss(scales, rows * ssz);
+    // outputs never overlap inputs or each other ...
+    if (overlap(so, ss) || overlap(so, sx) || overlap(so, sg) || overlap(ss, sx) || overlap(ss, sg))
+        return RMSQ_ERR_ALIAS;
+    if (resid) {
+        const Span sr(residual, tbytes), sro(residual_out, tbytes);
+        if (overlap(so, sr) || overlap(ss, sr) || overlap(sro, so) || overlap(sro, ss) || overlap(sro, sg))
+            return RMSQ_ERR_ALIAS;
+        // ... except an in-place residual update at exactly the same address
+        if (residual_out != x && overlap(sro, sx)) return RMSQ_ERR_ALIAS;
+        if (residual_out != residual && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
+    }
+
+    Shape shape;
+    if (!choose_shape(rows, nvec, false, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    FusedArgs a{};
+    a.x = x;
+    a.residual = residual;
+    a.residual_out = residual_out;
+    a.gamma = gamma;
+    a.out = out;
+    a.scales = scales;
+    a.global_scale = nullptr;
+    a.rows = rows;
+    a.hidden = (int32_t)hidden;
+    a.nvec = nvec;
+    a.eps = eps;
+    a.weight_offset = weight_offset;
+    a.scale_ub = scale_ub;
+    a.scales_dtype = scales_dtype;
+    return launched(launch_fp8(a, in_dtype, resid, out_fp8, shape, stream));
+}
+
+}  // namespace
+
+bool choose_shape(int64_t rows, int nvec, bool fp4, Shape* s) {
+    (void)fp4;
+    int waves = g_tune_waves.load(std::memory_order_relaxed);
+    int vpt = g_tune_vpt.load(std::memory_order_relaxed);
+    if (waves == 0) {
+        // Aim for two 16-byte vectors per lane on large batches; spread small
+        // batches (latency bound) over more lanes, one vector each.
+        const int64_t target = rows <= 256 ? 1 : 2;
+        waves = 1;
+        while (waves < 16 && (int64_t)waves * 64 * target < nvec) waves *= 2;
+    }
+    const int64_t lanes = (int64_t)waves * 64;
+    const int64_t need = (nvec + lanes - 1) / lanes;
+    if (vpt == 0) {
+        vpt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
+        if (vpt == 0) return false;
+    } else if (vpt < need) {
+        return false;
+    }
+    s->waves = waves;
+    s->vpt = vpt;
+    s->wpb = waves >= 4 ? waves : 4;
+    s->grid = g_tune_blocks.load(std::memory_order_relaxed);
+    return true;
+}
+
+int persistent_blocks(const void* kernel, int block_threads) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto key = std::make_pair(dev, kernel);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block_threads, 0) != hipSuccess || per < 1)
+        per = 1;
+    const int blocks = cus * per;
+    cache[key] = blocks;
+    return blocks;
+}
+
+}  // namespace rmsq
+
+using namespace rmsq;
+
+extern "C" {
+
+int rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
+                float weight_offset, float scale_ub, int out_fp8, void* out, int scales_dtype, void* scales,
+                hipStream_t stream) {
+    return fp8_common(rows, hidden, in_dtype, x, nullptr, nullptr, false, gamma, eps, weight_offset, scale_ub,
+                      out_fp8, out, scales_dtype, scales, stream);
+}
+
+int residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
+                         void* residual_out, const void* gamma, float eps, float weight_offset, float scale_ub,
+                         int out_fp8, void* out, int scales_dtype, void* scales, hipStream_t stream) {
+    return fp8_common(rows, hidden, in_dtype, x, residual, residual_out, true, gamma, eps, weight_offset,
+                      scale_ub, out_fp8, out, scales_dtype, scales, stream);
+}
+
+int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
+                float weight_offset, const float* global_scale, void* out, void* block_scales,
+                hipStream_t stream) {
+    if (in_dtype != RMSQ_F16 && in_dtype != RMSQ_BF16) return RMSQ_ERR_DTYPE;
+    if (rows < 0 || hidden <= 0 || hidden % 16 != 0) return RMSQ_ERR_SHAPE;
+    if (!size_ok(rows, hidden, 2)) return RMSQ_ERR_SHAPE;
+    if (int rc = check_scalars(eps, weight_offset, 1.0f, false)) return rc;
+    const int nvec = (int)(hidden / 8);
+    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    if (rows == 0) return RMSQ_OK;
+    if (!x || !gamma || !out || !block_scales) return RMSQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(out, 16)) return RMSQ_ERR_ALIGN;
+    if (global_scale && !aligned(global_scale, 4)) return RMSQ_ERR_ALIGN;
+    const Span sx(x, rows * hidden * 2), sg(gamma, hidden * 2), so(out, rows * hidden / 2),
+        ss(block_scales, rows * hidden / 16);
+    if (overlap(so, ss) || overlap(so, sx) || overlap(so, sg) || overlap(ss, sx) || overlap(ss, sg))
+        return RMSQ_ERR_ALIAS;
+    if (global_scale) {
+        const Span sgs(global_scale, 4);
+        if (overlap(sgs, so) || overlap(sgs, ss)) return RMSQ_ERR_ALIAS;
+    }
+    Shape shape;
+    if (!choose_shape(rows, nvec, true, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    FusedArgs a{};
+    a.x = x;
+    a.gamma = gamma;
+    a.out = out;
+    a.scales = block_scales;
+    a.global_scale = global_scale;
+    a.rows = rows;
+    a.hidden = (int32_t)hidden;
+    a.nvec = nvec;
+    a.eps = eps;
+    a.weight_offset = weight_offset;
+    return launched(launch_fp4(a, in_dtype, shape, stream));
+}
+
+int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream) {
+    if (kind < RMSQ_CVT_F32_TO_E4M3FN || kind > RMSQ_CVT_E4M3FN_TO_F32) return RMSQ_ERR_DTYPE;
+    if (n < 0 || n > (INT64_MAX / 8)) return RMSQ_ERR_SHAPE;
+    if (kind == RMSQ_CVT_F32_TO_E2M1 && (n % 2) != 0) return RMSQ_ERR_SHAPE;
+    if (n == 0) return RMSQ_OK;
+    if (!in || !out) return RMSQ_ERR_NULL;
+    if (!aligned(in, 16) || !aligned(out, 16)) return RMSQ_ERR_ALIGN;
+    const int64_t in_bytes = kind == RMSQ_CVT_E4M3FN_TO_F32 ? n : 4 * n;
+    const int64_t out_bytes = kind == RMSQ_CVT_E4M3FN_TO_F32 ? 4 * n
+                              : kind == RMSQ_CVT_F32_TO_E2M1 ? n / 2
+                              : (kind == RMSQ_CVT_F32_TO_BF16 || kind == RMSQ_CVT_F32_TO_F16) ? 2 * n
+                                                                                                : n;
+    if (overlap(Span(in, in_bytes), Span(out, out_bytes))) return RMSQ_ERR_ALIAS;
+    return launched(launch_convert(kind, in, out, n, stream));
+}
+
+int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int max_blocks) {
+    const bool w_ok = waves_per_row == 0 || waves_per_row == 1 || waves_per_row == 2 || waves_per_row == 4 ||
+                      waves_per_row == 8 || waves_per_row == 16;
+    const bool v_ok = vectors_per_lane == 0 || vectors_per_lane == 1 || vectors_per_lane == 2 ||
+                      vectors_per_lane == 4;
+    if (!w_ok || !v_ok || max_blocks < 0) return RMSQ_ERR_VALUE;
+    g_tune_waves.store(waves_per_row);
+    g_tune_vpt.store(vectors_per_lane);
+    g_tune_blocks.store(max_blocks);
+    return RMSQ_OK;
+}
+
+int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int is_fp4, int* waves_per_row,
+                     int* vectors_per_lane, int* rows_per_block) {
+    if (!valid_dtype(in_dtype)) return RMSQ_ERR_DTYPE;
+    if (hidden <= 0 || hidden % elems_per_vec(in_dtype) != 0) return RMSQ_ERR_SHAPE;
+    const int64_t nvec = hidden / elems_per_vec(in_dtype);
+    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    Shape s;
+    if (!choose_shape(rows, (int)nvec, is_fp4 != 0, &s)) return RMSQ_ERR_UNSUPPORTED;
+    if (waves_per_row) *waves_per_row = s.waves;
+    if (vectors_per_lane) *vectors_per_lane = s.vpt;
+    if (rows_per_block) *rows_per_block = s.wpb / s.waves;
+    return RMSQ_OK;
+}
+
+const char* rmsq_status_string(int status) {
+    switch (status) {
+    case RMSQ_OK: return "ok";
+    case RMSQ_ERR_NULL: return "null pointer";
+    case RMSQ_ERR_DTYPE: return "unsupported dtype or format";
+    case RMSQ_ERR_SHAPE: return "invalid shape";
+    case RMSQ_ERR_ALIGN: return "misaligned pointer";
+    case RMSQ_ERR_VALUE: return "invalid scalar argument";
+    case RMSQ_ERR_ALIAS: return "overlapping buffers";
+    case RMSQ_ERR_UNSUPPORTED: return "hidden size not supported";
+    case RMSQ_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int rmsq_abi_version(void) { return RMSQ_ABI_VERSION; }
+
+int rmsq_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI layer (rmsq_api.cpp) and the kernel
+// translation units.  Not installed; the public interface is include/rmsq.h.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace rmsq {
+
+// Argument block passed by value to the fused kernels.  All checks are done
+// by the API layer before this is built.
+struct FusedArgs {
+    const void* x;
+    const void* residual;      // FP8 residual variant only
+    void* residual_out;        // FP8 residual variant only
+    const void* gamma;
+    void* out;                 // FP8: [rows, hidden]; FP4: [rows, hidden/2]
+    void* scales;              // FP8: [rows]; FP4: [rows, hidden/16]
+    const float* global_scale; // FP4 only; may be null (1.0)
+    int64_t rows;
+    int32_t hidden;
+    int32_t nvec;              // hidden / elements per 16-byte vector
+    float eps;
+    float weight_offset;
+    float scale_ub;            // FP8 only
+    int32_t scales_dtype;      // FP8 only (RMSQ_F32/F16/BF16)
+};
+
+// Launch shape: one row is handled by `waves` wavefronts (64 lanes each), each
+// lane holding `vpt` 16-byte vectors of the row; `wpb` waves per block.
+struct Shape {
+    int waves;
+    int vpt;
+    int wpb;
+    int grid;
+};
+
+// Pick the automatic shape for a row of nvec 16-byte vectors (or apply the
+// process-wide override).  Returns false if no supported shape holds the row.
+bool choose_shape(int64_t rows, int nvec, bool fp4, Shape* s);
+
+// Kernel launchers (no argument checks).  Return the hipError_t of the launch.
+hipError_t launch_fp8(const FusedArgs& a, int in_dtype, bool residual, int out_fp8,
+                      Shape shape, hipStream_t stream);
+hipError_t launch_fp4(const FusedArgs& a, int in_dtype, Shape shape, hipStream_t stream);
+hipError_t launch_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
+
+// Occupancy-based persistent grid size for a kernel (cached per kernel).
+int persistent_blocks(const void* kernel, int block_threads);
+
+}  // namespace rmsq

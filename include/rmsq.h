@@ -1,0 +1,181 @@
+/*
+ * rmsq.h -- C ABI of librmsq: fused (residual +) RMSNorm + dynamic FP8 /
+ * block-scaled FP4 quantization on AMD Instinct MI355X (gfx950).
+ *
+ * Operation (per row of a [rows, hidden] row-major tensor):
+ *   s  = x                      or  s = round_to_in_dtype(x + residual)
+ *   y  = s * rsqrt(mean(s^2) + eps) * (gamma + weight_offset)
+ *   FP8: scale = min(max|y| / FMAX, scale_ub)  (FMAX 448 e4m3fn, 240 e4m3fnuz)
+ *        out   = saturating round-to-nearest-even FP8 of y / scale
+ *   FP4: per 16 contiguous elements, scale = min(gs * max|y| / 6, 448)
+ *        rounded to E4M3; out = saturating RNE E2M1 of y * gs / scale.
+ *
+ * Sources: Mojo docs "rms_norm_fused_fp8" (parameters and arguments: dtype
+ * lists, epsilon, weight_offset, scale_ub, per-row scale output); Mojo docs
+ * "allreduce_residual_rmsnorm_fp8" (residual input, residual_output holding
+ * the pre-norm sum; one GPU's local share); FlashInfer "rmsnorm_fp4quant.py"
+ * (Constants; FP8 E4M3 / E2M1 conversion sections; kernel phases 2-3; the
+ * rmsnorm_fp4quant API docstring for shapes, global_scale and layouts).
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronizes.  Each call enqueues at most one
+ *    kernel on `stream` (NULL = the null stream) and returns; results are
+ *    valid once the caller has synchronized that stream.
+ *  - Tensors are dense and row-major; leading dimensions are flattened into
+ *    `rows` by the caller.  rows == 0 is a no-op returning RMSQ_OK.
+ *  - Every argument check happens before any HIP call; on an error nothing is
+ *    launched and outputs are untouched.  Input values are not checked:
+ *    non-finite inputs, or eps == 0 on an all-zero row, give unspecified codes.
+ *  - Calls are reentrant; concurrent calls on different streams are safe as
+ *    long as their output buffers do not overlap.
+ */
+#ifndef RMSQ_H
+#define RMSQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMSQ_ABI_VERSION 1
+
+/* Element types (in_dtype, scales_dtype). */
+enum { RMSQ_F32 = 0, RMSQ_F16 = 1, RMSQ_BF16 = 2 };
+/* FP8 output formats: OCP E4M3 (max 448, has -0) and E4M3FNUZ (bias 8,
+ * max 240, no negative zero, 0x80 is NaN and never produced). */
+enum { RMSQ_E4M3FN = 0, RMSQ_E4M3FNUZ = 1 };
+
+/* Status codes. */
+enum {
+    RMSQ_OK = 0,
+    RMSQ_ERR_NULL = -1,        /* a required pointer is NULL */
+    RMSQ_ERR_DTYPE = -2,       /* unknown enum or unsupported combination */
+    RMSQ_ERR_SHAPE = -3,       /* rows < 0, hidden <= 0, hidden not a multiple of the
+                                  16-byte vector width (8 for 16-bit, 4 for fp32 input),
+                                  FP4 hidden not a multiple of 16, or size overflow */
+    RMSQ_ERR_ALIGN = -4,       /* a tensor pointer is not aligned (16 B for x, residual,
+                                  residual_out, gamma, out; element size for scales) */
+    RMSQ_ERR_VALUE = -5,       /* eps < 0 or non-finite; scale_ub <= 0 or NaN;
+                                  weight_offset non-finite */
+    RMSQ_ERR_ALIAS = -6,       /* an output overlaps an input or another output
+                                  (other than residual_out == x or == residual) */
+    RMSQ_ERR_UNSUPPORTED = -7, /* hidden above the largest row the kernels hold
+                                  (32768 for 16-bit inputs, 16384 for fp32) */
+    RMSQ_ERR_LAUNCH = -8       /* the kernel launch failed; see rmsq_last_hip_error() */
+};
+
+/*
+ * rmsnorm_fp8 -- RMSNorm + per-row dynamic FP8 quantization
+ * (Mojo docs "rms_norm_fused_fp8", Args).
+ *   rows, hidden : tensor shape; normalization runs over the last dimension.
+ *   in_dtype     : RMSQ_F32 / RMSQ_F16 / RMSQ_BF16, the type of x and gamma.
+ *   x            : [rows, hidden] input.
+ *   gamma        : [hidden] weight; the multiplier is gamma + weight_offset,
+ *                  formed in fp32 (not rounded to in_dtype).
+ *   eps          : added to mean(s^2) before the reciprocal square root.
+ *   scale_ub     : upper bound of the per-row scale (+inf: no bound).
+ *   out_fp8      : RMSQ_E4M3FN or RMSQ_E4M3FNUZ.
+ *   out          : [rows, hidden] bytes, the FP8 codes.
+ *   scales_dtype : RMSQ_F32 / RMSQ_F16 / RMSQ_BF16 (RNE from the fp32 scale).
+ *   scales       : [rows] dequantization scales: y ~= decode(out) * scale.  The
+ *                  codes are computed with the stored (rounded) scale; a zero
+ *                  scale (all-zero y) gives zero codes.
+ */
+int rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype,
+                const void* x, const void* gamma,
+                float eps, float weight_offset, float scale_ub,
+                int out_fp8, void* out, int scales_dtype, void* scales,
+                hipStream_t stream);
+
+/*
+ * residual_rmsnorm_fp8 -- residual add + RMSNorm + per-row FP8 quantization:
+ * one GPU's share of Mojo docs "allreduce_residual_rmsnorm_fp8" (Args:
+ * residual, residual_output as the pre-norm sum).
+ *   residual     : [rows, hidden] in in_dtype.
+ *   residual_out : [rows, hidden] in in_dtype; receives s = x + residual
+ *                  rounded once to in_dtype (RNE).  The normalization uses
+ *                  exactly this stored s.  residual_out may be the same
+ *                  pointer as x or as residual (in-place update); any other
+ *                  overlap is RMSQ_ERR_ALIAS.
+ *   other arguments as for rmsnorm_fp8.
+ */
+int residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype,
+                         const void* x, const void* residual, void* residual_out,
+                         const void* gamma,
+                         float eps, float weight_offset, float scale_ub,
+                         int out_fp8, void* out, int scales_dtype, void* scales,
+                         hipStream_t stream);
+
+/*
+ * rmsnorm_fp4 -- RMSNorm + block-scaled FP4 (NVFP4-style) quantization:
+ * FlashInfer "rmsnorm_fp4quant.py" (rmsnorm_fp4quant, block_size 16, E4M3
+ * scale factors, row-major scale layout).
+ *   in_dtype     : RMSQ_F16 or RMSQ_BF16.
+ *   hidden       : multiple of 16.
+ *   weight_offset: added to gamma (0 gives the page's operation).
+ *   global_scale : DEVICE pointer to one fp32 value gs (read by the kernel,
+ *                  so it can change between graph replays), or NULL for 1.0.
+ *                  Block scale = min(gs * max|y_block| / 6, 448) rounded to
+ *                  E4M3; elements are quantized as y * gs / decoded_scale, so
+ *                  y ~= decode(code) * decoded_scale / gs.  A zero block
+ *                  scale gives zero codes.
+ *   out          : [rows, hidden/2] bytes; element 2k in the low nibble of
+ *                  byte k, E2M1 with the sign in bit 3.
+ *   block_scales : [rows, hidden/16] E4M3FN codes, row-major.
+ */
+int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype,
+                const void* x, const void* gamma,
+                float eps, float weight_offset, const float* global_scale,
+                void* out, void* block_scales, hipStream_t stream);
+
+/*
+ * rmsq_convert -- the device conversions the fused kernels use, applied
+ * elementwise (standalone quantizers; also used to check the hardware
+ * conversion semantics).  n elements of input, DEVICE pointers, 16-byte
+ * aligned; n >= 0.
+ *   RMSQ_CVT_F32_TO_E4M3FN   : float -> 1 byte, saturating RNE
+ *   RMSQ_CVT_F32_TO_E4M3FNUZ : float -> 1 byte, saturating RNE, no -0
+ *   RMSQ_CVT_F32_TO_E2M1     : float -> nibble, saturating RNE; n even,
+ *                              out has n/2 bytes, element 2k in the low nibble
+ *   RMSQ_CVT_F32_TO_BF16     : float -> bfloat16 bits (RNE)
+ *   RMSQ_CVT_F32_TO_F16      : float -> binary16 bits (RNE)
+ *   RMSQ_CVT_E4M3FN_TO_F32   : 1 byte -> float (exact decode)
+ */
+enum {
+    RMSQ_CVT_F32_TO_E4M3FN = 0,
+    RMSQ_CVT_F32_TO_E4M3FNUZ = 1,
+    RMSQ_CVT_F32_TO_E2M1 = 2,
+    RMSQ_CVT_F32_TO_BF16 = 3,
+    RMSQ_CVT_F32_TO_F16 = 4,
+    RMSQ_CVT_E4M3FN_TO_F32 = 5
+};
+int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
+
+/*
+ * rmsq_set_tuning -- process-wide launch-shape override for subsequent calls
+ * (tuning and shape cross-checks).  waves_per_row in {1,2,4,8,16},
+ * vectors_per_lane in {1,2,4} (each vector is 16 bytes of input), max_blocks
+ * caps the persistent grid.  0 for any field keeps the automatic choice.
+ * Returns RMSQ_ERR_VALUE for an unsupported value.  A call whose hidden does
+ * not fit the forced shape returns RMSQ_ERR_UNSUPPORTED.
+ */
+int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int max_blocks);
+
+/* Launch shape the next call with these arguments would use (for logs). */
+int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int is_fp4,
+                     int* waves_per_row, int* vectors_per_lane, int* rows_per_block);
+
+/* Diagnostics. */
+const char* rmsq_status_string(int status);
+int rmsq_abi_version(void);
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int rmsq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSQ_H */

@@ -1,0 +1,115 @@
+"""Helpers for the GPU tests: run the library through its binding (C ABI) on
+seeded inputs and check the result against the oracle with the comparator."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import fp4_activation_quantization_amd as rq
+import oracle
+import workloads
+from parity import compare_fp4, compare_fp8
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def run_fp8(w, inp, *, rows_idx=None, ub=None, out_fmt=None, scales_dtype=None, weight_offset=None,
+            in_place=None, stream=None):
+    """Run the FP8 path on the GPU; returns host numpy (codes, scale bits, residual_out bits) for
+    rows_idx (all rows if None) plus the torch outputs."""
+    out_fmt = out_fmt or w.out_fmt
+    sdt = scales_dtype or w.scales_dtype
+    ub = w.scale_ub if ub is None else ub
+    off = w.weight_offset if weight_offset is None else weight_offset
+    x, g = to_dev(inp["x"]), to_dev(inp["gamma"])
+    sc_t = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[sdt]
+    if inp.get("residual") is not None:
+        r = to_dev(inp["residual"])
+        ro = None
+        if in_place == "x":
+            ro = x
+        elif in_place == "residual":
+            ro = r
+        codes, scales, rout = rq.residual_rmsnorm_fp8(x, r, g, eps=w.eps, weight_offset=off, scale_ub=ub,
+                                                      out_fp8=out_fmt, scales_dtype=sc_t, residual_out=ro,
+                                                      stream=stream)
+    else:
+        codes, scales = rq.rmsnorm_fp8(x, g, eps=w.eps, weight_offset=off, scale_ub=ub, out_fp8=out_fmt,
+                                       scales_dtype=sc_t, stream=stream)
+        rout = None
+    torch.cuda.synchronize()
+    sel = slice(None) if rows_idx is None else torch.as_tensor(rows_idx, device=DEV)
+    c = codes[sel].cpu().numpy()
+    s = workloads.bits(scales[sel].cpu())
+    ro = workloads.bits(rout[sel].cpu()) if rout is not None else None
+    return c, s, ro
+
+
+def oracle_fp8(w, inp, *, rows_idx=None, ub=None, out_fmt=None, scales_dtype=None, weight_offset=None):
+    x = workloads.bits(inp["x"])
+    r = workloads.bits(inp["residual"]) if inp.get("residual") is not None else None
+    if rows_idx is not None:
+        x = x[rows_idx]
+        r = r[rows_idx] if r is not None else None
+    g = workloads.bits(inp["gamma"])
+    kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset if weight_offset is None else weight_offset)
+    ref = oracle.rmsnorm_fp8(x, g, scale_ub=w.scale_ub if ub is None else ub, out_fmt=out_fmt or w.out_fmt,
+                             scales_dtype=scales_dtype or w.scales_dtype, residual=r, **kw)
+    y = oracle.rmsnorm_y(x, g, residual=r, **kw)["y"]
+    return ref, y
+
+
+def check_fp8(w, inp, *, rows_idx=None, label="", **kw):
+    c, s, ro = run_fp8(w, inp, rows_idx=rows_idx, **kw)
+    kw.pop("in_place", None)
+    kw.pop("stream", None)
+    ref, y = oracle_fp8(w, inp, rows_idx=rows_idx, **kw)
+    rep = compare_fp8(c, s, ref, y, out_fmt=kw.get("out_fmt") or w.out_fmt,
+                      scales_dtype=kw.get("scales_dtype") or w.scales_dtype, gpu_residual_out=ro)
+    say(f"  parity {label or w.name}: {rep}")
+    return rep
+
+
+def run_fp4(w, inp, gs, *, rows_idx=None, weight_offset=None, stream=None):
+    x, g = to_dev(inp["x"]), to_dev(inp["gamma"])
+    gst = torch.tensor([gs], dtype=torch.float32, device=DEV) if gs is not None else None
+    packed, bs = rq.rmsnorm_fp4(x, g, eps=w.eps, weight_offset=w.weight_offset if weight_offset is None else weight_offset,
+                                global_scale=gst, stream=stream)
+    torch.cuda.synchronize()
+    sel = slice(None) if rows_idx is None else torch.as_tensor(rows_idx, device=DEV)
+    return packed[sel].cpu().numpy(), bs[sel].cpu().numpy()
+
+
+def check_fp4(w, inp, gs, *, rows_idx=None, label="", weight_offset=None):
+    p, bs = run_fp4(w, inp, gs, rows_idx=rows_idx, weight_offset=weight_offset)
+    x = workloads.bits(inp["x"])
+    if rows_idx is not None:
+        x = x[rows_idx]
+    g = workloads.bits(inp["gamma"])
+    off = w.weight_offset if weight_offset is None else weight_offset
+    kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=off)
+    gsv = 1.0 if gs is None else gs
+    ref = oracle.rmsnorm_fp4(x, g, global_scale=gsv, **kw)
+    y = oracle.rmsnorm_y(x, g, **kw)["y"]
+    rep = compare_fp4(p, bs, ref, y, global_scale=gsv)
+    say(f"  parity {label or w.name}: {rep}")
+    return rep
+
+
+def sample_rows(rows: int, k: int, seed: int, must=()):
+    rng = np.random.default_rng(seed)
+    pick = set(int(r) for r in must if 0 <= r < rows)
+    pick.update([0, rows - 1])
+    pick.update(int(v) for v in rng.choice(rows, size=min(k, rows), replace=False))
+    return np.array(sorted(pick), np.int64)

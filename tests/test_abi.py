@@ -1,0 +1,225 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/rmsq.h declares, and rejects each invalid argument with its status
+code before making any HIP call (so these run on a CPU-only machine).
+
+Fake device pointers below are never dereferenced.  A module-wide fixture
+forces a launch shape (one wave, one vector per lane) that cannot hold the
+rows used here (hidden >= 1024), so a call that passes every argument check
+stops with RMSQ_ERR_UNSUPPORTED instead of launching: that is how the tests
+show a check was passed.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import fp4_activation_quantization_amd as rq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsq.h")
+
+OK, NULL, DTYPE, SHAPE, ALIGN, VALUE, ALIAS, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7
+BASE = 1 << 32  # fake, 16-byte aligned addresses far apart
+MB = 1 << 28
+
+
+@pytest.fixture(autouse=True)
+def no_launch_possible():
+    rq.set_tuning(1, 1, 0)
+    yield
+    rq.set_tuning(0, 0, 0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsq_convert", "rmsq_set_tuning",
+              "rmsq_query_shape", "rmsq_status_string", "rmsq_abi_version", "rmsq_last_hip_error"):
+        assert f in fns, f
+
+
+def test_library_exports_every_declared_symbol():
+    L = rq.lib()
+    for f in declared_functions():
+        assert hasattr(L, f), f"{f} declared in rmsq.h but not exported"
+
+
+def test_abi_version_and_status_strings():
+    L = rq.lib()
+    assert L.rmsq_abi_version() == 1
+    for code in range(-8, 1):
+        assert L.rmsq_status_string(code) not in (None, b"", b"unknown status")
+    assert L.rmsq_status_string(42) == b"unknown status"
+    assert L.rmsq_last_hip_error() == 0
+
+
+def P(i):
+    return ctypes.c_void_p(BASE + i * MB)
+
+
+def fp8(rows=4, hidden=4096, dt=rq.BF16, x=None, g=None, eps=1e-6, off=0.0, ub=1200.0, fmt=rq.E4M3FN, out=None,
+        sdt=rq.F32, sc=None):
+    x = P(0) if x is None else x
+    g = P(1) if g is None else g
+    out = P(2) if out is None else out
+    sc = P(3) if sc is None else sc
+    return rq.lib().rmsnorm_fp8(rows, hidden, dt, x, g, eps, off, ub, fmt, out, sdt, sc, None)
+
+
+def rfp8(rows=4, hidden=4096, dt=rq.BF16, x=None, r=None, ro=None, g=None, out=None, sc=None, eps=1e-6):
+    x = P(0) if x is None else x
+    r = P(4) if r is None else r
+    ro = P(5) if ro is None else ro
+    g = P(1) if g is None else g
+    out = P(2) if out is None else out
+    sc = P(3) if sc is None else sc
+    return rq.lib().residual_rmsnorm_fp8(rows, hidden, dt, x, r, ro, g, eps, 0.0, 1200.0, rq.E4M3FN, out, rq.F32,
+                                         sc, None)
+
+
+def fp4(rows=4, hidden=4096, dt=rq.BF16, x=None, g=None, gs=None, out=None, bs=None, eps=1e-6, off=0.0):
+    x = P(0) if x is None else x
+    g = P(1) if g is None else g
+    out = P(2) if out is None else out
+    bs = P(3) if bs is None else bs
+    return rq.lib().rmsnorm_fp4(rows, hidden, dt, x, g, eps, off, gs, out, bs, None)
+
+
+def test_fp8_dtype_errors():
+    assert fp8(dt=7) == DTYPE
+    assert fp8(sdt=-1) == DTYPE
+    assert fp8(fmt=2) == DTYPE
+
+
+def test_fp8_shape_errors():
+    assert fp8(rows=-1) == SHAPE
+    assert fp8(hidden=0) == SHAPE
+    assert fp8(hidden=-8) == SHAPE
+    assert fp8(hidden=12) == SHAPE            # 16-bit input: multiple of 8
+    assert fp8(hidden=6, dt=rq.F32) == SHAPE  # fp32 input: multiple of 4
+    assert fp8(rows=1 << 62, hidden=1 << 20) == SHAPE
+
+
+def test_fp8_value_errors():
+    for eps in (-1e-6, math.inf, math.nan):
+        assert fp8(eps=eps) == VALUE
+    for ub in (0.0, -1.0, math.nan):
+        assert fp8(ub=ub) == VALUE
+    for off in (math.inf, math.nan):
+        assert fp8(off=off) == VALUE
+
+
+def test_fp8_unsupported_width():
+    assert fp8(hidden=8 * 4096 + 8) == UNSUP
+    assert fp8(hidden=4 * 4096 + 4, dt=rq.F32) == UNSUP
+
+
+def test_zero_rows_is_a_noop_even_with_null_pointers():
+    z = ctypes.c_void_p(0)
+    assert rq.lib().rmsnorm_fp8(0, 64, rq.BF16, z, z, 1e-6, 0.0, 1.0, rq.E4M3FN, z, rq.F32, z, None) == OK
+    assert rq.lib().residual_rmsnorm_fp8(0, 64, rq.BF16, z, z, z, z, 1e-6, 0.0, 1.0, rq.E4M3FN, z, rq.F32, z,
+                                         None) == OK
+    assert rq.lib().rmsnorm_fp4(0, 64, rq.BF16, z, z, 1e-6, 0.0, z, z, z, None) == OK
+    assert rq.lib().rmsq_convert(rq.CVT_F32_TO_E4M3FN, z, z, 0, None) == OK
+
+
+def test_fp8_null_errors():
+    z = ctypes.c_void_p(0)
+    assert fp8(x=z) == NULL
+    assert fp8(g=z) == NULL
+    assert fp8(out=z) == NULL
+    assert fp8(sc=z) == NULL
+    assert rfp8(r=z) == NULL
+    assert rfp8(ro=z) == NULL
+
+
+def test_fp8_alignment_errors():
+    odd = lambda i, k: ctypes.c_void_p(BASE + i * MB + k)
+    assert fp8(x=odd(0, 8)) == ALIGN
+    assert fp8(g=odd(1, 2)) == ALIGN
+    assert fp8(out=odd(2, 8)) == ALIGN
+    assert fp8(sc=odd(3, 2)) == ALIGN                  # fp32 scales need 4 bytes
+    assert fp8(sc=odd(3, 2), sdt=rq.BF16) == UNSUP     # bf16 scales need 2: all checks pass
+    assert rfp8(r=odd(4, 4)) == ALIGN
+    assert rfp8(ro=odd(5, 4)) == ALIGN
+
+
+def test_fp8_alias_errors():
+    near = lambda i, k: ctypes.c_void_p(BASE + i * MB + k)
+    assert fp8(out=near(0, 64)) == ALIAS     # codes inside x
+    assert fp8(sc=near(2, 16)) == ALIAS      # scales inside codes
+    assert fp8(out=near(1, 0)) == ALIAS      # codes over gamma
+    assert rfp8(ro=near(0, 16)) == ALIAS     # partial overlap of residual_out and x
+    assert rfp8(ro=near(4, 32)) == ALIAS     # partial overlap of residual_out and residual
+    assert rfp8(ro=near(2, 0)) == ALIAS      # residual_out over the codes
+    assert rfp8(ro=near(1, 0)) == ALIAS      # residual_out over gamma
+    # exact in-place residual updates pass every check
+    assert rfp8(ro=P(0)) == UNSUP
+    assert rfp8(ro=P(4)) == UNSUP
+    assert rfp8(x=P(4), r=P(4), ro=P(4)) == UNSUP
+    assert fp8() == UNSUP and rfp8() == UNSUP and fp4() == UNSUP
+    # in place over x while residual partially overlaps x
+    assert rfp8(ro=P(0), r=near(0, 32)) == ALIAS
+
+
+def test_fp4_errors():
+    assert fp4(dt=rq.F32) == DTYPE
+    assert fp4(dt=9) == DTYPE
+    assert fp4(hidden=24) == SHAPE
+    assert fp4(hidden=0) == SHAPE
+    assert fp4(rows=-2) == SHAPE
+    assert fp4(eps=-1.0) == VALUE
+    assert fp4(off=math.nan) == VALUE
+    assert fp4(hidden=16 * 2048 + 16) == UNSUP
+    z = ctypes.c_void_p(0)
+    assert fp4(x=z) == NULL and fp4(bs=z) == NULL and fp4(out=z) == NULL and fp4(g=z) == NULL
+    assert fp4(x=ctypes.c_void_p(BASE + 8)) == ALIGN
+    assert fp4(gs=ctypes.c_void_p(BASE + 9 * MB + 2)) == ALIGN
+    assert fp4(bs=ctypes.c_void_p(BASE + 2 * MB + 16)) == ALIAS
+    assert fp4(gs=ctypes.c_void_p(BASE + 3 * MB)) == ALIAS
+
+
+def test_convert_errors():
+    L = rq.lib()
+    assert L.rmsq_convert(99, P(0), P(1), 8, None) == DTYPE
+    assert L.rmsq_convert(rq.CVT_F32_TO_E2M1, P(0), P(1), 7, None) == SHAPE
+    assert L.rmsq_convert(rq.CVT_F32_TO_BF16, P(0), P(1), -1, None) == SHAPE
+    assert L.rmsq_convert(rq.CVT_F32_TO_BF16, ctypes.c_void_p(0), P(1), 8, None) == NULL
+    assert L.rmsq_convert(rq.CVT_F32_TO_BF16, ctypes.c_void_p(BASE + 4), P(1), 8, None) == ALIGN
+    assert L.rmsq_convert(rq.CVT_F32_TO_BF16, P(0), ctypes.c_void_p(BASE + 16), 8, None) == ALIAS
+
+
+def test_tuning_and_query_shape():
+    L = rq.lib()
+    assert L.rmsq_set_tuning(3, 0, 0) == VALUE
+    assert L.rmsq_set_tuning(0, 8, 0) == VALUE
+    assert L.rmsq_set_tuning(0, 0, -1) == VALUE
+    rq.set_tuning(0, 0, 0)
+    try:
+        s = rq.query_shape(8192, 4096, rq.torch.bfloat16)
+        assert s["waves_per_row"] * 64 * s["vectors_per_lane"] * 8 >= 4096
+        assert rq.query_shape(1, 8192, rq.torch.float16) == {"waves_per_row": 16, "vectors_per_lane": 1,
+                                                              "rows_per_block": 1}
+        rq.set_tuning(1, 1, 0)
+        with pytest.raises(rq.RmsqError):
+            rq.query_shape(8, 4096, rq.torch.bfloat16)  # 64 lanes x 1 vector cannot hold 512 vectors
+        rq.set_tuning(4, 4, 0)
+        assert rq.query_shape(8, 4096, rq.torch.bfloat16)["rows_per_block"] == 1
+    finally:
+        rq.set_tuning(1, 1, 0)
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    """With the library absent the binding raises instead of computing anything."""
+    monkeypatch.setattr(rq, "_lib", None)
+    monkeypatch.setattr(rq, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        rq.lib()

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+* Every workload at a reduced row count, element by element (sizes that span
+  several blocks of the persistent grid and leave ragged tails).
+* Every workload at its full size, in the launch configuration the benchmark
+  times, compared on sampled rows (rows are independent, so the oracle
+  computes just those).
+* Edge cases: empty input, ragged and minimal hidden sizes, the largest
+  hidden, constant / zero / gamma=0 rows, negative zeros, binding scale_ub,
+  in-place residual updates, every dtype/format/scale-dtype combination,
+  determinism, agreement across launch shapes, non-default streams.
+The comparison rule is in tests/parity.py.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_activation_quantization_amd as rq
+import oracle
+import workloads
+from gpu_common import DEV, check_fp4, check_fp8, run_fp8, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+W = workloads.WORKLOADS
+FP8_NAMES = [n for n, w in W.items() if w.op != "rmsnorm_fp4"]
+SMALL_ROWS = {"rmsnorm_fp8_bf16_16x512": 16, "residual_rmsnorm_fp8_bf16_8192x4096": 301,
+              "rmsnorm_fp8_f16_decode_1x8192": 1, "rmsnorm_fp8_f16_decode_8x8192": 8,
+              "rmsnorm_fp8_f16_decode_64x8192": 64, "residual_rmsnorm_fp8_bf16_32768x8192": 203,
+              "residual_rmsnorm_fp8_f32_32768x8192": 203, "rmsnorm_fp4_bf16_16384x7168": 157}
+
+
+def golden_gs():
+    return json.load(open(os.path.join(HERE, "golden", "fp4_global_scale.json")))["global_scale"]
+
+
+def fp4_gs_for(inp, w=None):
+    w = w or inp["workload"]
+    amax = oracle.absmax(workloads.bits(inp["x"]), workloads.bits(inp["gamma"]), in_dtype=w.in_dtype, eps=w.eps,
+                         weight_offset=w.weight_offset)
+    return float(np.float32(448 * 6 / amax))
+
+
+@pytest.fixture(autouse=True)
+def default_shape():
+    rq.set_tuning(0, 0, 0)
+    yield
+    rq.set_tuning(0, 0, 0)
+
+
+@pytest.mark.parametrize("name", list(SMALL_ROWS))
+def test_workload_small_all_elements(name):
+    w = W[name]
+    inp = workloads.make(name, rows=SMALL_ROWS[name])
+    say(f"[small] {name} rows={SMALL_ROWS[name]} shape={rq.query_shape(SMALL_ROWS[name], w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.op == 'rmsnorm_fp4')}")
+    if w.op == "rmsnorm_fp4":
+        check_fp4(w, inp, fp4_gs_for(inp))
+    else:
+        check_fp8(w, inp)
+
+
+@pytest.mark.parametrize("name", list(W))
+def test_workload_full_size_sampled_rows(name):
+    w = W[name]
+    say(f"[full] {name} rows={w.rows} hidden={w.hidden}")
+    inp = workloads.make(name)
+    must = []
+    sel = inp.get("selection") or {}
+    if sel.get("outlier_rows") is not None:
+        must = list(sel["outlier_rows"][:8])
+    rows = sample_rows(w.rows, 40, seed=17, must=must)
+    if w.op == "rmsnorm_fp4":
+        check_fp4(w, inp, golden_gs(), rows_idx=rows)
+    else:
+        check_fp8(w, inp, rows_idx=rows)
+
+
+def _rand_inputs(rows, hidden, dt, seed=0, resid=False, gamma=None, scale=1.0):
+    rng = np.random.default_rng(seed)
+    td = workloads.TORCH_DTYPES[dt]
+    x = torch.from_numpy(rng.standard_normal((rows, hidden)) * scale).to(td)
+    r = torch.from_numpy(rng.standard_normal((rows, hidden))).to(td) if resid else None
+    g = torch.from_numpy(rng.uniform(0.5, 1.5, hidden) if gamma is None else np.broadcast_to(gamma, hidden).copy()).to(td)
+    return {"x": x, "residual": r, "gamma": g}
+
+
+def _wl(op, rows, hidden, dt, **kw):
+    return workloads.Workload("custom", op, rows, hidden, dt, 99, eps=kw.pop("eps", 1e-6), **kw)
+
+
+def test_zero_rows_is_a_noop():
+    x = torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(512, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((0, 512), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((0,), dtype=torch.float32, device=DEV)
+    rq.rmsnorm_fp8(x, g, out=out, scales=sc)
+    rq.residual_rmsnorm_fp8(x, x, g, out=out, scales=sc, residual_out=x)
+    rq.rmsnorm_fp4(x, g)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dt,hiddens", [("bf16", [8, 16, 24, 520, 1576, 4104, 8200]),
+                                        ("f16", [8, 136, 2056]),
+                                        ("f32", [4, 12, 1028, 4100])])
+@pytest.mark.parametrize("rows", [1, 3, 67])
+def test_ragged_hidden_and_rows(dt, hiddens, rows):
+    for h in hiddens:
+        for resid in (False, True):
+            op = "residual_rmsnorm_fp8" if resid else "rmsnorm_fp8"
+            w = _wl(op, rows, h, dt)
+            say(f"[ragged] {op} {dt} rows={rows} hidden={h}")
+            check_fp8(w, _rand_inputs(rows, h, dt, seed=h + rows, resid=resid), label=f"{op} {dt} {rows}x{h}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("rows,hidden", [(1, 16), (3, 32), (67, 528), (5, 7168 + 16), (129, 1024)])
+def test_fp4_ragged(dt, rows, hidden):
+    w = _wl("rmsnorm_fp4", rows, hidden, dt)
+    inp = _rand_inputs(rows, hidden, dt, seed=rows * hidden)
+    say(f"[fp4 ragged] {dt} rows={rows} hidden={hidden}")
+    check_fp4(w, inp, fp4_gs_for(inp, w), label=f"fp4 {dt} {rows}x{hidden}")
+    check_fp4(w, inp, None, label=f"fp4 {dt} {rows}x{hidden} gs=None")
+
+
+@pytest.mark.parametrize("dt,hidden", [("bf16", 32768), ("f16", 32768), ("f32", 16384)])
+def test_largest_hidden(dt, hidden):
+    w = _wl("residual_rmsnorm_fp8", 5, hidden, dt)
+    say(f"[max hidden] {dt} {hidden}")
+    check_fp8(w, _rand_inputs(5, hidden, dt, seed=3, resid=True), label=f"max {dt} {hidden}")
+    if dt != "f32":
+        w4 = _wl("rmsnorm_fp4", 5, hidden, dt)
+        inp = _rand_inputs(5, hidden, dt, seed=4)
+        check_fp4(w4, inp, fp4_gs_for(inp, w4), label=f"fp4 max {dt} {hidden}")
+
+
+def test_special_rows():
+    h = 1024
+    rows = []
+    rows.append(np.full(h, 3.0))                      # constant row
+    rows.append(np.zeros(h))                          # zero row (eps > 0): scale 0
+    neg0 = np.zeros(h); neg0[::2] = -0.0              # negative zeros
+    rows.append(neg0)
+    big = np.random.default_rng(1).standard_normal(h) * 1e4
+    rows.append(big)                                  # large values
+    tiny = np.random.default_rng(2).standard_normal(h) * 1e-3
+    rows.append(tiny)                                 # eps comparable to mean(x^2)
+    onehot = np.zeros(h); onehot[17] = -5.0
+    rows.append(onehot)
+    x = torch.from_numpy(np.stack(rows)).to(torch.bfloat16)
+    for dt in ("bf16", "f32"):
+        inp = {"x": x.to(workloads.TORCH_DTYPES[dt]), "residual": None,
+               "gamma": torch.from_numpy(np.random.default_rng(3).uniform(0.5, 1.5, h)).to(workloads.TORCH_DTYPES[dt])}
+        for fmt in ("e4m3fn", "e4m3fnuz"):
+            w = _wl("rmsnorm_fp8", len(rows), h, dt, out_fmt=fmt)
+            say(f"[special] {dt} {fmt}")
+            check_fp8(w, inp, label=f"special {dt} {fmt}")
+        inp0 = dict(inp, gamma=torch.zeros(h, dtype=workloads.TORCH_DTYPES[dt]))
+        check_fp8(_wl("rmsnorm_fp8", len(rows), h, dt), inp0, label=f"gamma=0 {dt}")
+        w4 = _wl("rmsnorm_fp4", len(rows), h, "bf16")
+        if dt == "bf16":
+            check_fp4(w4, inp, 1.0, label="fp4 special gs=1")
+            check_fp4(w4, inp0, 1.0, label="fp4 gamma=0")
+
+
+@pytest.mark.parametrize("ub", [1e-3, 1e-2, 0.05])
+def test_scale_ub_binds(ub):
+    w = _wl("residual_rmsnorm_fp8", 33, 2048, "bf16", scale_ub=ub)
+    inp = _rand_inputs(33, 2048, "bf16", seed=11, resid=True)
+    say(f"[ub] {ub}")
+    check_fp8(w, inp, label=f"ub={ub}")
+    c, s, _ = run_fp8(w, inp)
+    if ub <= 1e-3:  # below every row's natural scale: the bound binds everywhere
+        assert np.all(s == np.float32(ub))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e4m3fnuz"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
+def test_dtype_format_scale_matrix(dt, fmt, sdt):
+    for resid in (False, True):
+        op = "residual_rmsnorm_fp8" if resid else "rmsnorm_fp8"
+        w = _wl(op, 70, 2048, dt, out_fmt=fmt, scales_dtype=sdt, weight_offset=0.5)
+        say(f"[matrix] {op} {dt} {fmt} {sdt}")
+        check_fp8(w, _rand_inputs(70, 2048, dt, seed=5, resid=resid), label=f"{op} {dt} {fmt} {sdt}")
+
+
+@pytest.mark.parametrize("where", ["x", "residual"])
+def test_in_place_residual(where):
+    w = W["residual_rmsnorm_fp8_bf16_8192x4096"]
+    inp = workloads.make(w.name, rows=130)
+    say(f"[in place] residual_out = {where}")
+    check_fp8(w, inp, in_place=where, label=f"in place over {where}")
+
+
+def test_deterministic_and_shape_independent():
+    w = W["residual_rmsnorm_fp8_bf16_8192x4096"]
+    inp = workloads.make(w.name, rows=257)
+    base = run_fp8(w, inp)
+    again = run_fp8(w, inp)
+    assert all(np.array_equal(a, b) for a, b in zip(base[:2], again[:2]))
+    for waves in (1, 2, 4, 8, 16):
+        for vpt in (1, 2, 4):
+            if waves * 64 * vpt * 8 < w.hidden:
+                continue
+            for blocks in (0, 7):
+                rq.set_tuning(waves, vpt, blocks)
+                say(f"[shape] waves={waves} vpt={vpt} max_blocks={blocks}")
+                rep = check_fp8(w, inp, label=f"shape {waves}x{vpt}/{blocks}")
+                c, s, ro = run_fp8(w, inp)
+                assert np.array_equal(ro, base[2])
+                # codes may differ from the default shape only at rounding boundaries
+                assert (c != base[0]).mean() <= 1e-4
+    rq.set_tuning(0, 0, 0)
+
+
+def test_fp4_shapes_and_offset():
+    w = W["rmsnorm_fp4_bf16_16384x7168"]
+    inp = workloads.make(w.name, rows=90)
+    gs = fp4_gs_for(inp)
+    for waves, vpt in ((4, 4), (8, 2), (8, 4), (16, 1), (16, 2)):
+        if waves * 64 * vpt * 8 < w.hidden:
+            continue
+        rq.set_tuning(waves, vpt, 5)
+        say(f"[fp4 shape] waves={waves} vpt={vpt}")
+        check_fp4(w, inp, gs, label=f"fp4 shape {waves}x{vpt}")
+    rq.set_tuning(0, 0, 0)
+    check_fp4(w, inp, gs, weight_offset=0.25, label="fp4 weight_offset=0.25")
+
+
+def test_non_default_stream_and_3d_input():
+    w = W["rmsnorm_fp8_bf16_16x512"]
+    inp = workloads.make(w.name)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        rep = check_fp8(w, inp, stream=s, label="side stream")
+    x3 = inp["x"].reshape(4, 4, 512).to(DEV)
+    g = inp["gamma"].to(DEV)
+    c3, s3 = rq.rmsnorm_fp8(x3, g, eps=w.eps, scale_ub=w.scale_ub)
+    c2, s2 = rq.rmsnorm_fp8(x3.reshape(16, 512), g, eps=w.eps, scale_ub=w.scale_ub)
+    torch.cuda.synchronize()
+    assert c3.shape == (4, 4, 512) and s3.shape == (4, 4)
+    assert torch.equal(c3.reshape(16, 512), c2) and torch.equal(s3.reshape(16), s2)
