@@ -1,0 +1,289 @@
+"""Benchmark of the fused (residual +) RMSNorm + FP8 / FP4 quantization path on one MI355X.
+
+One step = one call of the fused kernel over one batch of seeded synthetic
+activations already resident in HBM.  The headline workload is the residual
+path at Llama-3-8B width (8192 rows x 4096, bf16 in, e4m3fn out, fp32
+scales, bf16 residual_out); the metric is algorithmic HBM bytes per second.
+
+Timing: W untimed warm-up steps, then K back-to-back steps between two HIP
+events recorded on the stream the kernel runs on, bracketed by device
+synchronizations.  A step is one kernel launch, so the average step time is
+the kernel's average launch duration (including the ~1 us dispatch gap
+between launches); per-launch event pairs are not used because they add
+several microseconds to every launch.  Buffers rotate through enough
+independent copies (>= 1 GiB in total) that the 256 MB Infinity Cache cannot
+serve a step from a previous one.
+
+Printed: one JSON line.  Other workloads are reported in its "workloads"
+object; --workloads selects them (the headline leads when it is selected).
+The CPU baseline is the float64 oracle timed on the whole headline workload.
+--copy-calibration runs only a plain copy of known size, the reference that
+rocprofv3's FETCH_SIZE / WRITE_SIZE readings are scaled by.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp4_activation_quantization_amd as rq  # noqa: E402
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+CACHE_DEFEAT_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["rmsq_fp8.hip", "rmsq_fp4.hip", "rmsq_device.h", "rmsq_api.cpp"]
+SC_T = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "fp4_activation_quantization_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w: workloads.Workload) -> int:
+    """One read of every input element, one write of every output, gamma once."""
+    esz = {"bf16": 2, "f16": 2, "f32": 4}[w.in_dtype]
+    n = w.rows * w.hidden
+    if w.op == "rmsnorm_fp4":
+        return n * esz + n // 2 + n // 16 + w.hidden * esz + 4
+    ssz = {"f32": 4, "bf16": 2, "f16": 2}[w.scales_dtype]
+    b = n * esz + n + w.rows * ssz + w.hidden * esz
+    if w.residual:
+        b += 2 * n * esz  # residual read + residual_out write
+    return b
+
+
+class Case:
+    """Device buffers (rotated copies) and pre-marshalled C-ABI arguments for one workload."""
+
+    def __init__(self, w: workloads.Workload, copies: int, gs: float | None):
+        inp = workloads.make(w)
+        dev = "cuda:0"
+        self.w = w
+        x0 = inp["x"].to(dev)
+        g = inp["gamma"].to(dev)
+        r0 = inp["residual"].to(dev) if inp["residual"] is not None else None
+        self.keep = [g]
+        self.calls = []
+        L = rq.lib()
+        dt = {"bf16": rq.BF16, "f16": rq.F16, "f32": rq.F32}[w.in_dtype]
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        for i in range(copies):
+            x = x0 if i == 0 else x0.clone()
+            if w.op == "rmsnorm_fp4":
+                out = torch.empty((w.rows, w.hidden // 2), dtype=torch.uint8, device=dev)
+                bs = torch.empty((w.rows, w.hidden // 16), dtype=torch.uint8, device=dev)
+                gst = torch.tensor([gs], dtype=torch.float32, device=dev)
+                self.keep += [x, out, bs, gst]
+                args = (w.rows, w.hidden, dt, P(x), P(g), w.eps, w.weight_offset, P(gst), P(out), P(bs), stream)
+                self.calls.append((L.rmsnorm_fp4, args))
+                continue
+            out = torch.empty((w.rows, w.hidden), dtype=torch.uint8, device=dev)
+            sc = torch.empty((w.rows,), dtype=SC_T[w.scales_dtype], device=dev)
+            fmt = {"e4m3fn": rq.E4M3FN, "e4m3fnuz": rq.E4M3FNUZ}[w.out_fmt]
+            sdt = {"f32": rq.F32, "bf16": rq.BF16, "f16": rq.F16}[w.scales_dtype]
+            if w.residual:
+                r = r0 if i == 0 else r0.clone()
+                ro = torch.empty_like(x)
+                self.keep += [x, r, ro, out, sc]
+                args = (w.rows, w.hidden, dt, P(x), P(r), P(ro), P(g), w.eps, w.weight_offset, w.scale_ub, fmt,
+                        P(out), sdt, P(sc), stream)
+                self.calls.append((L.residual_rmsnorm_fp8, args))
+            else:
+                self.keep += [x, out, sc]
+                args = (w.rows, w.hidden, dt, P(x), P(g), w.eps, w.weight_offset, w.scale_ub, fmt, P(out), sdt,
+                        P(sc), stream)
+                self.calls.append((L.rmsnorm_fp8, args))
+
+    def step(self, i: int) -> None:
+        fn, args = self.calls[i % len(self.calls)]
+        rc = fn(*args)
+        if rc != 0:
+            raise rq.RmsqError(fn.__name__, rc, rq.lib().rmsq_last_hip_error())
+
+
+def time_case(case: Case, steps: int, warmup: int) -> dict:
+    """W untimed steps, then K back-to-back steps between two HIP events recorded
+    on the kernel's stream, bracketed by device synchronizations.  The average
+    launch duration is the elapsed time over K: it includes the dispatch gap
+    between consecutive kernels (about a microsecond), so it is an upper bound
+    on the kernel's own duration."""
+    for i in range(warmup):
+        case.step(i)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        case.step(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = t0.elapsed_time(t1)
+    per_us = total_ms * 1e3 / steps
+    b = algorithmic_bytes(case.w)
+    return {"steps": steps, "ms_per_step": total_ms / steps, "wall_s": wall, "launch_us": per_us, "bytes": b,
+            "gbps": b / (per_us * 1e-6) / 1e9, "rows_per_s": case.w.rows / (per_us * 1e-6)}
+
+
+def fp4_global_scale() -> float:
+    p = os.path.join(ROOT, "tests", "golden", "fp4_global_scale.json")
+    return json.load(open(p))["global_scale"]
+
+
+def copies_for(w: workloads.Workload) -> int:
+    b = algorithmic_bytes(w)
+    if b < (16 << 20):
+        return 1  # latency-sized: reported warm (served from cache)
+    return max(1, -(-CACHE_DEFEAT_BYTES // b))
+
+
+def traffic_from_profiles(name: str) -> float | None:
+    """HBM bytes per launch measured by rocprofv3 counters for this workload, if they
+    were taken on the current kernel sources (else None)."""
+    p = os.path.join(PROFILES, f"traffic_{name}.md")
+    if not os.path.exists(p):
+        return None
+    for line in open(p):
+        if line.startswith("traffic_json:"):
+            d = json.loads(line.split(":", 1)[1])
+            if d.get("kernel_source_hash") == kernel_source_hash():
+                return d.get("hbm_bytes_per_launch")
+    return None
+
+
+def cpu_baseline(min_seconds: float) -> dict:
+    """The float64 oracle over the whole headline workload on host cores, repeated
+    until min_seconds have elapsed (at least one pass)."""
+    import oracle
+
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    inp = workloads.make(w)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    x, r, g = workloads.bits(inp["x"]), workloads.bits(inp["residual"]), workloads.bits(inp["gamma"])
+    oracle.lib()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.rmsnorm_fp8(x, g, in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset, scale_ub=w.scale_ub,
+                           out_fmt=w.out_fmt, scales_dtype=w.scales_dtype, residual=r, threads=threads, want_q=False)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    per_pass = dt / passes
+    return {"value": round(algorithmic_bytes(w) / per_pass / 1e9, 6), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "rows_per_s": round(w.rows / per_pass, 1), "seconds": round(dt, 2),
+            "sample": f"the whole {w.name} workload ({w.rows} rows), {passes} pass(es), float64 C oracle "
+                      f"split by rows over {threads} threads"}
+
+
+def copy_calibration(nbytes: int, steps: int) -> None:
+    """A plain device-to-device copy of nbytes (torch's copy kernel), for scaling
+    rocprofv3's FETCH_SIZE / WRITE_SIZE counters: it reads and writes nbytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "steps": steps}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workloads", default="all", help="'all', 'headline' or comma-separated workload names")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (for counter scaling) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across GPUs "
+              "without communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return 0
+    rq.lib()
+
+    if args.workloads == "all":
+        names = list(workloads.WORKLOADS)
+    elif args.workloads == "headline":
+        names = [workloads.HEADLINE]
+    else:
+        names = args.workloads.split(",")
+    lead = workloads.HEADLINE if workloads.HEADLINE in names else names[0]
+
+    results = {}
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        k = copies_for(w)
+        case = Case(w, k, fp4_global_scale() if w.op == "rmsnorm_fp4" else None)
+        steps = args.steps if name == workloads.HEADLINE else max(10, args.steps // 2)
+        res = time_case(case, steps, args.warmup)
+        res["buffer_sets"] = k
+        res["launch"] = rq.query_shape(w.rows, w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.op == "rmsnorm_fp4")
+        results[name] = res
+        print(f"# {name}: {res['launch_us']:.2f} us/launch, {res['gbps']:.0f} GB/s, {k} buffer set(s), "
+              f"launch {res['launch']}", file=sys.stderr, flush=True)
+        del case
+        torch.cuda.empty_cache()
+
+    h = results[lead]
+    w = workloads.WORKLOADS[lead]
+    line = {
+        "metric": "GB/s (algorithmic HBM bytes) for fused residual+RMSNorm+FP8 quant, 1 GPU"
+                  if lead == workloads.HEADLINE else f"GB/s (algorithmic HBM bytes) for {w.op}, 1 GPU",
+        "value": round(h["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": h["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded PCG64 activations; see workloads.py)",
+        "config": {"workload": w.name, "rows": w.rows, "hidden": w.hidden, "in_dtype": w.in_dtype,
+                   "op": w.op, "global_batch": w.rows, "buffer_sets": h["buffer_sets"], "launch": h["launch"]},
+        "rows_per_s": round(h["rows_per_s"], 1),
+        "pct_hbm_peak": round(100.0 * h["gbps"] / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(h["gbps"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(h["gbps"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles(w.name),
+                     "launch_us": round(h["launch_us"], 3), "bytes_per_launch": h["bytes"]},
+        "workloads": {n: {"launch_us": round(r["launch_us"], 3), "gbps": round(r["gbps"], 1),
+                          "frac_hbm": round(r["gbps"] / HBM_PEAK_GBS, 4), "rows_per_s": round(r["rows_per_s"], 1),
+                          "bytes": r["bytes"], "buffer_sets": r["buffer_sets"], "launch": r["launch"]}
+                      for n, r in results.items()},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -159,9 +159,9 @@ def convert(kind: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> tor
     return dst
 
 
-def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, max_blocks: int = 0) -> None:
+def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, grid_blocks: int = 0) -> None:
     """Process-wide launch-shape override (0 = automatic)."""
-    _check("rmsq_set_tuning", lib().rmsq_set_tuning(waves_per_row, vectors_per_lane, max_blocks))
+    _check("rmsq_set_tuning", lib().rmsq_set_tuning(waves_per_row, vectors_per_lane, grid_blocks))
 
 
 def query_shape(rows: int, hidden: int, dtype: torch.dtype, fp4: bool = False) -> dict:

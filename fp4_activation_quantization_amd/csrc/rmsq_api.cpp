@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -103,6 +104,7 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
     a.global_scale = nullptr;
     a.rows = rows;
     a.hidden = (int32_t)hidden;
+    a.inv_hidden = 1.0 / (double)hidden;
     a.nvec = nvec;
     a.eps = eps;
     a.weight_offset = weight_offset;
@@ -113,39 +115,60 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
 
 }  // namespace
 
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Vectors per lane for a given wave count: the smallest supported one that
+// holds the row, or 0.
+int vpt_for(int nvec, int waves) {
+    const int64_t need = ceil_div(nvec, (int64_t)waves * 64);
+    return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
+}
+
+}  // namespace
+
 bool choose_shape(int64_t rows, int nvec, bool fp4, Shape* s) {
     (void)fp4;
     int waves = g_tune_waves.load(std::memory_order_relaxed);
     int vpt = g_tune_vpt.load(std::memory_order_relaxed);
-    if (waves == 0) {
-        // Aim for two 16-byte vectors per lane on large batches; spread small
-        // batches (latency bound) over more lanes, one vector each.
-        const int64_t target = rows <= 256 ? 1 : 2;
-        waves = 1;
-        while (waves < 16 && (int64_t)waves * 64 * target < nvec) waves *= 2;
+    if (waves == 0 && vpt == 0) {
+        if (rows <= 256) {
+            // small batches are latency bound: spread the row, one vector per lane
+            waves = (int)std::min<int64_t>(16, ceil_div(nvec, 64));
+        } else {
+            // large batches: the fewest waves whose lanes hold the row exactly
+            // with 4, 2 or 1 vectors each (no idle lanes); otherwise 4 vectors
+            // per lane with the last ones partly idle
+            waves = 0;
+            for (int v : {4, 2, 1}) {
+                const int64_t w = ceil_div(nvec, 64 * v);
+                if (w <= 16 && w * 64 * v == nvec) {
+                    waves = (int)w;
+                    break;
+                }
+            }
+            if (waves == 0) waves = (int)std::min<int64_t>(16, ceil_div(nvec, 256));
+        }
+    } else if (waves == 0) {
+        waves = (int)std::min<int64_t>(16, ceil_div(nvec, 64 * (int64_t)vpt));
     }
-    const int64_t lanes = (int64_t)waves * 64;
-    const int64_t need = (nvec + lanes - 1) / lanes;
-    if (vpt == 0) {
-        vpt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
-        if (vpt == 0) return false;
-    } else if (vpt < need) {
-        return false;
-    }
+    if (vpt == 0) vpt = vpt_for(nvec, waves);
+    if (vpt == 0 || (int64_t)vpt * waves * 64 < nvec) return false;
     s->waves = waves;
     s->vpt = vpt;
-    s->wpb = waves >= 4 ? waves : 4;
+    s->rpb = waves >= 4 ? 1 : 4 / waves;
     s->grid = g_tune_blocks.load(std::memory_order_relaxed);
     return true;
 }
 
 int persistent_blocks(const void* kernel, int block_threads) {
     static std::mutex mu;
-    static std::map<std::pair<int, const void*>, int> cache;
+    static std::map<std::pair<std::pair<int, int>, const void*>, int> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     std::lock_guard<std::mutex> lock(mu);
-    auto key = std::make_pair(dev, kernel);
+    auto key = std::make_pair(std::make_pair(dev, block_threads), kernel);
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
     int cus = 0, per = 0;
@@ -208,6 +231,7 @@ int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const
     a.global_scale = global_scale;
     a.rows = rows;
     a.hidden = (int32_t)hidden;
+    a.inv_hidden = 1.0 / (double)hidden;
     a.nvec = nvec;
     a.eps = eps;
     a.weight_offset = weight_offset;
@@ -230,15 +254,14 @@ int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t str
     return launched(launch_convert(kind, in, out, n, stream));
 }
 
-int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int max_blocks) {
-    const bool w_ok = waves_per_row == 0 || waves_per_row == 1 || waves_per_row == 2 || waves_per_row == 4 ||
-                      waves_per_row == 8 || waves_per_row == 16;
+int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks) {
+    const bool w_ok = waves_per_row >= 0 && waves_per_row <= 16;
     const bool v_ok = vectors_per_lane == 0 || vectors_per_lane == 1 || vectors_per_lane == 2 ||
                       vectors_per_lane == 4;
-    if (!w_ok || !v_ok || max_blocks < 0) return RMSQ_ERR_VALUE;
+    if (!w_ok || !v_ok || grid_blocks < 0) return RMSQ_ERR_VALUE;
     g_tune_waves.store(waves_per_row);
     g_tune_vpt.store(vectors_per_lane);
-    g_tune_blocks.store(max_blocks);
+    g_tune_blocks.store(grid_blocks);
     return RMSQ_OK;
 }
 
@@ -252,7 +275,7 @@ int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int is_fp4, int
     if (!choose_shape(rows, (int)nvec, is_fp4 != 0, &s)) return RMSQ_ERR_UNSUPPORTED;
     if (waves_per_row) *waves_per_row = s.waves;
     if (vectors_per_lane) *vectors_per_lane = s.vpt;
-    if (rows_per_block) *rows_per_block = s.wpb / s.waves;
+    if (rows_per_block) *rows_per_block = s.rpb;
     return RMSQ_OK;
 }
 

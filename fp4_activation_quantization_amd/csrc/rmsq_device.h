@@ -15,6 +15,29 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 struct BF16 {};
 struct F16 {};
 
+// ---- streaming global memory access -----------------------------------------
+// Activations are read once and outputs written once, so their accesses carry
+// the non-temporal hint (they should not displace gamma and other reused lines
+// in L2 / Infinity Cache).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream(const void* base, int64_t i16) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + i16);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(void* base, int64_t i16, const uint4& v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(base) + i16);
+}
+__device__ __forceinline__ void store_stream(void* base, int64_t i8, const uint2& v) {
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(base) + i8);
+}
+__device__ __forceinline__ void store_stream(void* base, int64_t i4, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(base) + i4);
+}
+
 // ---- one 16-byte vector of input elements --------------------------------
 template <typename T>
 struct Vec;
@@ -33,6 +56,12 @@ struct Vec<float> {
     __device__ __forceinline__ static uint4 pack(const float* f) {
         return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
                           __float_as_uint(f[3]));
+    }
+    // Sum of squares of the vector's elements (fp32 fused multiply-adds).
+    __device__ __forceinline__ static float sumsq(const uint4& v) {
+        float f[4];
+        unpack(v, f);
+        return fmaf(f[3], f[3], fmaf(f[2], f[2], fmaf(f[1], f[1], f[0] * f[0])));
     }
 };
 
@@ -57,6 +86,18 @@ struct Vec<BF16> {
     }
     __device__ __forceinline__ static uint4 pack(const float* f) {
         return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+    }
+    // Sum of squares straight from the packed pairs: v_dot2c_f32_bf16 (each
+    // bf16 square is exact in fp32; accumulation in fp32).
+    __device__ __forceinline__ static float sumsq(const uint4& v) {
+        float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), __builtin_bit_cast(bf16x2, v.x),
+                                                    0.0f, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), __builtin_bit_cast(bf16x2, v.y), acc,
+                                              false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), __builtin_bit_cast(bf16x2, v.z), acc,
+                                              false);
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), __builtin_bit_cast(bf16x2, v.w), acc,
+                                               false);
     }
 };
 
@@ -83,28 +124,99 @@ struct Vec<F16> {
     __device__ __forceinline__ static uint4 pack(const float* f) {
         return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
     }
+    // Sum of squares from the packed pairs: v_dot2c_f32_f16 (each fp16 square
+    // is exact in fp32; accumulation in fp32).
+    __device__ __forceinline__ static float sumsq(const uint4& v) {
+        float acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, v.x), __builtin_bit_cast(f16x2, v.x), 0.0f, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, v.y), __builtin_bit_cast(f16x2, v.y), acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, v.z), __builtin_bit_cast(f16x2, v.z), acc, false);
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, v.w), __builtin_bit_cast(f16x2, v.w), acc, false);
+    }
 };
 
+// Largest |t_e| of a vector of fp32 values, folded into m (v_max3_f32 with
+// absolute-value source modifiers, two elements per instruction).
+template <int N>
+__device__ __forceinline__ float abs_max(float m, const float* t) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) m = fmaxf(m, fabsf(t[e]));
+    return m;
+}
+
+// ---- per-row scalars in fp64 --------------------------------------------------
+// 1/sqrt(m) and 1/d: the hardware estimate (v_rsq_f64 / v_rcp_f64) refined by
+// one Newton step, which squares its relative error to far below fp32's
+// resolution.  Computed once per row, so fp64 costs nothing measurable.
+__device__ __forceinline__ double rsqrt_refined(double m) {
+    const double r = __builtin_amdgcn_rsq(m);
+    return r * (1.5 - 0.5 * m * r * r);
+}
+__device__ __forceinline__ double rcp_refined(double d) {
+    const double r = __builtin_amdgcn_rcp(d);
+    return r * (2.0 - d * r);
+}
+
 // ---- wavefront (64-lane) reductions ----------------------------------------
-// Butterfly exchanges: every lane ends with the same value because each step
-// combines the same pair of operands (addition and max are commutative).
+// DPP permutations inside each 16-lane row (every lane has a source, so no
+// bound control is involved), then the four row results are read out of
+// lanes 0, 16, 32 and 48.  Each step combines the same pair of operands in
+// every lane it reaches (addition and max are commutative), so all lanes end
+// with bit-identical results.
+enum : int {
+    DPP_SWAP1 = 0xB1,         // quad_perm [1,0,3,2]: lane ^ 1
+    DPP_SWAP2 = 0x4E,         // quad_perm [2,3,0,1]: lane ^ 2
+    DPP_HALF_MIRROR = 0x141,  // lane i <-> 7 - i within 8 lanes
+    DPP_MIRROR = 0x140        // lane i <-> 15 - i within 16 lanes
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f64<DPP_SWAP1>(v);
+    v += dpp_f64<DPP_SWAP2>(v);
+    v += dpp_f64<DPP_HALF_MIRROR>(v);
+    v += dpp_f64<DPP_MIRROR>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
-__device__ __forceinline__ float max_nonneg(float a, float b) { return a > b ? a : b; }
+// Max of non-negative floats, taken on their bit patterns: for values >= 0
+// the integer order is the floating-point order, and integer max needs no
+// NaN canonicalization.
+__device__ __forceinline__ int max_bits(int a, int b) { return a > b ? a : b; }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max_nonneg(v, __shfl_xor(v, o, 64));
-    return v;
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    int b = __float_as_int(v);
+    b = max_bits(b, dpp_i32<DPP_SWAP1>(b));
+    b = max_bits(b, dpp_i32<DPP_SWAP2>(b));
+    b = max_bits(b, dpp_i32<DPP_HALF_MIRROR>(b));
+    b = max_bits(b, dpp_i32<DPP_MIRROR>(b));
+    const int r = max_bits(max_bits(__builtin_amdgcn_readlane(b, 0), __builtin_amdgcn_readlane(b, 16)),
+                           max_bits(__builtin_amdgcn_readlane(b, 32), __builtin_amdgcn_readlane(b, 48)));
+    return __int_as_float(r);
 }
 
-// Lane l exchanges with lane l^1 (DPP quad_perm [1,0,3,2]).
-__device__ __forceinline__ float swap_adjacent_lanes(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+// max(v, v of lane ^ 1) for non-negative v (the two halves of an FP4 block).
+__device__ __forceinline__ float pair_max_nonneg(float v) {
+    const int b = __float_as_int(v);
+    return __int_as_float(max_bits(b, dpp_i32<DPP_SWAP1>(b)));
 }
 
 // ---- conversions ------------------------------------------------------------
@@ -117,7 +229,9 @@ __device__ __forceinline__ uint32_t e4m3fn_x4(float a, float b, float c, float d
     b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
     c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
     d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // the first conversion writes the low half, the second the high half; the
+    // initial high half is never used, so a's dead register serves as it
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -145,28 +259,29 @@ __device__ __forceinline__ uint32_t fp8_x4(float a, float b, float c, float d) {
         return e4m3fn_x4(a, b, c, d);
 }
 
-// E4M3 code of one non-negative scale value (clamped to 448, RNE).
+// E4M3 code of one non-negative scale value (clamped to 448, RNE), in the
+// low byte of the result; the other bytes are unspecified.
 __device__ __forceinline__ uint32_t e4m3fn_scale_code(float v) {
     v = fminf(v, 448.0f);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, __float_as_int(v), false);
 }
 
-// Exact value of an e4m3fn code (v_cvt_f32_fp8).
+// Exact value of the e4m3fn code in the low byte of `code` (v_cvt_f32_fp8).
 __device__ __forceinline__ float e4m3fn_decode(uint32_t code) {
     return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
 }
 
 // FP4 E2M1: eight values -> eight nibbles, value 2k in the low nibble of byte
-// k.  Clamped to +-6, then v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to
-// nearest even.
+// k.  v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds to nearest even and
+// saturates to +-6 by itself (checked over the whole fp32 range, infinities
+// included, against the reference encoder), so no clamp is needed.
 __device__ __forceinline__ uint32_t e2m1_x8(const float* q) {
-    float c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(q[i], -6.0f, 6.0f);
-    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, c[0], c[1], 1.0f, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], 1.0f, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[4], c[5], 1.0f, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[6], c[7], 1.0f, 3);
+    // each conversion writes one byte and all four are written, so the
+    // initial value is irrelevant: q[0]'s dead register serves as it
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(q[0]), q[0], q[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
     return w;
 }
 

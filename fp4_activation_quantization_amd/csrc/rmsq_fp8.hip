@@ -6,51 +6,55 @@
 //
 // One pass over HBM: every input element is read once into VGPRs, the row
 // stays in registers between the reduction and the quantization, and every
-// output byte is written once.
+// output byte is written once, all with non-temporal hints.
 //
-// Work mapping: `WAVES` wavefronts cooperate on one row; a block holds
-// WPB/WAVES rows.  Lane l of a row group owns the 16-byte vectors
-// l, l + T, l + 2T, ... (T = 64 * WAVES), so each wave instruction moves
-// 1 KiB of contiguous input.  The grid is persistent: blocks stride over row
-// groups, so gamma (+ weight_offset) is unpacked into fp32 registers once per
-// block.
+// Work mapping: `waves` wavefronts (1..16, a launch parameter) cooperate on
+// one row; a block holds one row, or 4/waves rows for 1-2 waves.  Lane l of a
+// row group owns the 16-byte vectors l, l + T, l + 2T, ... (T = 64 * waves,
+// VPT vectors per lane, a compile-time constant), so each wave instruction
+// moves 1 KiB of contiguous input.  EXACT (compile time) means the lanes hold
+// the row exactly (nvec == VPT * T): no lane is idle and no access needs a
+// guard.  Blocks stride over row groups; by default the grid has one block per
+// row group (large batches stream best that way on MI355X, and
+// gamma + weight_offset comes from L2).
 //
-// Precision: s^2 is accumulated in fp32 within a 16-byte vector, then in
-// fp64 per lane and across lanes; rstd, the scale and the quantization
-// factor are formed in fp64 once per row.  Per element the kernel computes
-// t = s * g' (fp32) and q = t * k with k = rstd / stored_scale (fp32), so the
-// codes see at most a few fp32 roundings of relative error.
+// Precision: s^2 is summed in fp32 within a 16-byte vector (v_dot2c on packed
+// 16-bit pairs, whose squares are exact), then in fp64 per lane and across
+// lanes; rstd, the scale and the quantization factor are formed in fp64 once
+// per row.  Per element the kernel computes t = s * g' and q = t * k
+// (k = rstd / stored_scale) in fp32, so a code sees at most three fp32
+// roundings of relative error.
 #include "rmsq_device.h"
 #include "rmsq_internal.h"
 
 namespace rmsq {
 
-template <typename InT, bool RESID, bool FNUZ, int WAVES, int WPB, int VPT>
-__global__ void __launch_bounds__(WPB * 64) fp8_kernel(const FusedArgs a) {
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool EXACT>
+__global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
-    constexpr int T = WAVES * 64;   // lanes per row
-    constexpr int RPB = WPB / WAVES;  // rows per block
-    constexpr double FMAX = FNUZ ? 240.0 : 448.0;
+    constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
 
+    const int waves = a.waves;       // wavefronts per row
+    const int T = waves * 64;        // lanes per row
+    const int rpb = blockDim.x / T;  // rows per block
     const int tid = threadIdx.x;
     const int slot = tid / T;       // row slot within the block
     const int lt = tid - slot * T;  // lane within the row group
-    const int wv = lt >> 6;         // wave within the row group
+    const int red = slot * waves + (lt >> 6);  // this wave's reduction slot
     const int nvec = a.nvec;
     const int64_t row_bytes = (int64_t)a.hidden * V::BYTES;
+    auto live = [&](int k) { return EXACT || lt + k * T < nvec; };
 
-    __shared__ double red_sum[2][RPB][WAVES];
-    __shared__ float red_max[2][RPB][WAVES];
+    __shared__ double red_sum[2][16];
+    __shared__ int red_max[2][16];
 
-    // gamma + weight_offset for this lane's columns, fp32, once per block
+    // gamma + weight_offset for this lane's columns, fp32 (zero past the row)
     float g[VPT][EPV];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int v = lt + k * T;
-        if (v < nvec) {
-            const uint4 gv = reinterpret_cast<const uint4*>(a.gamma)[v];
-            V::unpack(gv, g[k]);
+        if (live(k)) {
+            V::unpack(reinterpret_cast<const uint4*>(a.gamma)[lt + k * T], g[k]);
 #pragma unroll
             for (int e = 0; e < EPV; ++e) g[k][e] += a.weight_offset;
         } else {
@@ -60,7 +64,7 @@ __global__ void __launch_bounds__(WPB * 64) fp8_kernel(const FusedArgs a) {
     }
 
     int parity = 0;
-    for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < a.rows; row0 += (int64_t)gridDim.x * RPB) {
+    for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
         const int64_t row = row0 + slot;
         const bool active = row < a.rows;
 
@@ -68,95 +72,82 @@ __global__ void __launch_bounds__(WPB * 64) fp8_kernel(const FusedArgs a) {
         double ssq = 0.0;
         float amax = 0.0f;
         if (active) {
-            const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) + row * row_bytes);
+            const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
+            // vectors past the end of the row are zero: they add nothing
             uint4 xv[VPT];
 #pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int v = lt + k * T;
-                xv[k] = v < nvec ? xr[v] : make_uint4(0, 0, 0, 0);
-            }
+            for (int k = 0; k < VPT; ++k) xv[k] = live(k) ? load_stream(xr, lt + k * T) : make_uint4(0, 0, 0, 0);
             if constexpr (RESID) {
-                const uint4* rr =
-                    reinterpret_cast<const uint4*>(static_cast<const char*>(a.residual) + row * row_bytes);
-                uint4* ro = reinterpret_cast<uint4*>(static_cast<char*>(a.residual_out) + row * row_bytes);
-                uint4 rv[VPT];
+                // residual_out may be x or residual itself: each vector is read
+                // and then written by the one lane that owns it
+                const char* rr = static_cast<const char*>(a.residual) + row * row_bytes;
+                char* ro = static_cast<char*>(a.residual_out) + row * row_bytes;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
-                    const int v = lt + k * T;
-                    rv[k] = v < nvec ? rr[v] : make_uint4(0, 0, 0, 0);
-                }
-#pragma unroll
-                for (int k = 0; k < VPT; ++k) {
-                    const int v = lt + k * T;
+                    const uint4 rv = live(k) ? load_stream(rr, lt + k * T) : make_uint4(0, 0, 0, 0);
                     float xf[EPV], rf[EPV];
                     V::unpack(xv[k], xf);
-                    V::unpack(rv[k], rf);
+                    V::unpack(rv, rf);
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) xf[e] += rf[e];
                     // one rounding of the fp32 sum to the element type; fp32 keeps
                     // at least 2p+2 bits of a 16-bit sum, so this equals rounding
                     // the exact sum once
                     xv[k] = V::pack(xf);
-                    if (v < nvec) ro[v] = xv[k];
+                    if (live(k)) store_stream(ro, lt + k * T, xv[k]);
                 }
             }
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
+                ssq += (double)V::sumsq(xv[k]);
                 float s[EPV];
                 V::unpack(xv[k], s);
-                float part = 0.0f;
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) part = fmaf(s[e], s[e], part);
-                ssq += (double)part;
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    t[k][e] = s[e] * g[k][e];
-                    amax = max_nonneg(amax, fabsf(t[k][e]));
-                }
+                for (int e = 0; e < EPV; ++e) t[k][e] = s[e] * g[k][e];
+                amax = abs_max<EPV>(amax, t[k]);
             }
         }
 
         ssq = wave_sum(ssq);
-        amax = wave_max(amax);
-        if constexpr (WAVES > 1) {
+        amax = wave_max_nonneg(amax);
+        if (waves > 1) {  // uniform over the block
             if ((lt & 63) == 0) {
-                red_sum[parity][slot][wv] = ssq;
-                red_max[parity][slot][wv] = amax;
+                red_sum[parity][red] = ssq;
+                red_max[parity][red] = __float_as_int(amax);
             }
             __syncthreads();
             ssq = 0.0;
-            amax = 0.0f;
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
-                ssq += red_sum[parity][slot][w];
-                amax = max_nonneg(amax, red_max[parity][slot][w]);
+            int m = 0;
+            for (int w = 0; w < waves; ++w) {
+                ssq += red_sum[parity][slot * waves + w];
+                m = max_bits(m, red_max[parity][slot * waves + w]);
             }
+            amax = __int_as_float(m);
             // the other parity's slots are rewritten only after the next
             // barrier, which every wave reaches after finishing these reads
             parity ^= 1;
         }
 
         if (active) {
-            const double rstd = 1.0 / sqrt(ssq / (double)a.hidden + (double)a.eps);
-            double sc = (double)amax * rstd / FMAX;
+            const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
+            double sc = (double)amax * rstd * INV_FMAX;
             if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
             uint32_t sbits;
             const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
-            const float kq = sc_st > 0.0f ? (float)(rstd / (double)sc_st) : 0.0f;
+            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
 
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * (int64_t)a.hidden;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
-                const int v = lt + k * T;
-                if (v < nvec) {
+                if (live(k)) {
                     if constexpr (EPV == 8) {
                         uint2 w;
                         w.x = fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq);
                         w.y = fp8_x4<FNUZ>(t[k][4] * kq, t[k][5] * kq, t[k][6] * kq, t[k][7] * kq);
-                        reinterpret_cast<uint2*>(orow)[v] = w;
+                        store_stream(orow, lt + k * T, w);
                     } else {
-                        reinterpret_cast<uint32_t*>(orow)[v] =
-                            fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq);
+                        store_stream(orow, lt + k * T,
+                                     fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq));
                     }
                 }
             }
@@ -167,44 +158,36 @@ __global__ void __launch_bounds__(WPB * 64) fp8_kernel(const FusedArgs a) {
 
 namespace {
 
-template <typename InT, bool RESID, bool FNUZ, int WAVES, int VPT>
-hipError_t launch_shape(const FusedArgs& a, Shape s, hipStream_t stream) {
-    constexpr int WPB = WAVES >= 4 ? WAVES : 4;
-    constexpr int RPB = WPB / WAVES;
-    auto kern = fp8_kernel<InT, RESID, FNUZ, WAVES, WPB, VPT>;
-    const int64_t groups = (a.rows + RPB - 1) / RPB;
-    int64_t grid = persistent_blocks(reinterpret_cast<const void*>(kern), WPB * 64);
-    if (s.grid > 0 && s.grid < grid) grid = s.grid;
+template <typename InT, bool RESID, bool FNUZ, int VPT>
+hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
+    a.waves = s.waves;
+    const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
+    // default: one block per row group
+    int64_t grid = s.grid > 0 ? s.grid : groups;
     if (grid > groups) grid = groups;
+    if (grid > INT32_MAX) grid = INT32_MAX;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WPB * 64), 0, stream, a);
+    const dim3 gd((unsigned)grid), bd(s.waves * s.rpb * 64);
+    if (a.nvec == VPT * s.waves * 64)
+        hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true>), gd, bd, 0, stream, a);
+    else
+        hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false>), gd, bd, 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename InT, bool RESID, bool FNUZ, int WAVES>
+template <typename InT, bool RESID, bool FNUZ>
 hipError_t by_vpt(const FusedArgs& a, Shape s, hipStream_t st) {
     switch (s.vpt) {
-    case 1: return launch_shape<InT, RESID, FNUZ, WAVES, 1>(a, s, st);
-    case 2: return launch_shape<InT, RESID, FNUZ, WAVES, 2>(a, s, st);
-    default: return launch_shape<InT, RESID, FNUZ, WAVES, 4>(a, s, st);
-    }
-}
-
-template <typename InT, bool RESID, bool FNUZ>
-hipError_t by_waves(const FusedArgs& a, Shape s, hipStream_t st) {
-    switch (s.waves) {
-    case 1: return by_vpt<InT, RESID, FNUZ, 1>(a, s, st);
-    case 2: return by_vpt<InT, RESID, FNUZ, 2>(a, s, st);
-    case 4: return by_vpt<InT, RESID, FNUZ, 4>(a, s, st);
-    case 8: return by_vpt<InT, RESID, FNUZ, 8>(a, s, st);
-    default: return by_vpt<InT, RESID, FNUZ, 16>(a, s, st);
+    case 1: return launch_vpt<InT, RESID, FNUZ, 1>(a, s, st);
+    case 2: return launch_vpt<InT, RESID, FNUZ, 2>(a, s, st);
+    default: return launch_vpt<InT, RESID, FNUZ, 4>(a, s, st);
     }
 }
 
 template <typename InT>
 hipError_t by_variant(const FusedArgs& a, bool resid, bool fnuz, Shape s, hipStream_t st) {
-    if (resid) return fnuz ? by_waves<InT, true, true>(a, s, st) : by_waves<InT, true, false>(a, s, st);
-    return fnuz ? by_waves<InT, false, true>(a, s, st) : by_waves<InT, false, false>(a, s, st);
+    if (resid) return fnuz ? by_vpt<InT, true, true>(a, s, st) : by_vpt<InT, true, false>(a, s, st);
+    return fnuz ? by_vpt<InT, false, true>(a, s, st) : by_vpt<InT, false, false>(a, s, st);
 }
 
 }  // namespace

@@ -18,20 +18,23 @@ struct FusedArgs {
     void* scales;              // FP8: [rows]; FP4: [rows, hidden/16]
     const float* global_scale; // FP4 only; may be null (1.0)
     int64_t rows;
+    double inv_hidden;         // 1.0 / hidden
     int32_t hidden;
     int32_t nvec;              // hidden / elements per 16-byte vector
     float eps;
     float weight_offset;
     float scale_ub;            // FP8 only
     int32_t scales_dtype;      // FP8 only (RMSQ_F32/F16/BF16)
+    int32_t waves;             // wavefronts per row (set by the launcher)
 };
 
-// Launch shape: one row is handled by `waves` wavefronts (64 lanes each), each
-// lane holding `vpt` 16-byte vectors of the row; `wpb` waves per block.
+// Launch shape: one row is handled by `waves` wavefronts (64 lanes each, any
+// count 1..16), each lane holding `vpt` 16-byte vectors of the row; a block
+// holds `rpb` rows (waves * rpb wavefronts); `grid` blocks (0 = default).
 struct Shape {
     int waves;
     int vpt;
-    int wpb;
+    int rpb;
     int grid;
 };
 

@@ -157,12 +157,14 @@ int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t str
 /*
  * rmsq_set_tuning -- process-wide launch-shape override for subsequent calls
  * (tuning and shape cross-checks).  waves_per_row in {1,2,4,8,16},
- * vectors_per_lane in {1,2,4} (each vector is 16 bytes of input), max_blocks
- * caps the persistent grid.  0 for any field keeps the automatic choice.
+ * vectors_per_lane in {1,2,4} (each vector is 16 bytes of input),
+ * grid_blocks sets the number of blocks of the row-strided grid (at most one
+ * per row group; the default is the occupancy-limited resident count).  0 for
+ * any field keeps the automatic choice.
  * Returns RMSQ_ERR_VALUE for an unsupported value.  A call whose hidden does
  * not fit the forced shape returns RMSQ_ERR_UNSUPPORTED.
  */
-int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int max_blocks);
+int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks);
 
 /* Launch shape the next call with these arguments would use (for logs). */
 int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int is_fp4,

@@ -199,7 +199,7 @@ def test_convert_errors():
 
 def test_tuning_and_query_shape():
     L = rq.lib()
-    assert L.rmsq_set_tuning(3, 0, 0) == VALUE
+    assert L.rmsq_set_tuning(17, 0, 0) == VALUE
     assert L.rmsq_set_tuning(0, 8, 0) == VALUE
     assert L.rmsq_set_tuning(0, 0, -1) == VALUE
     rq.set_tuning(0, 0, 0)
