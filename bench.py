@@ -204,8 +204,8 @@ def copy_calibration(nbytes: int, steps: int) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workloads", default="all", help="'all', 'headline' or comma-separated workload names")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline time")
     ap.add_argument("--no-cpu-baseline", action="store_true")

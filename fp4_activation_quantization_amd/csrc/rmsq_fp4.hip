@@ -17,12 +17,14 @@
 // byte and each lane stores its own 4 bytes of codes.  The grid is persistent
 // (one block per resident slot), so gamma + weight_offset is unpacked into
 // registers once per block: this path is close to the VALU limit at HBM rate.
+#include <algorithm>
+
 #include "rmsq_device.h"
 #include "rmsq_internal.h"
 
 namespace rmsq {
 
-template <typename InT, int VPT, bool EXACT>
+template <typename InT, int VPT, bool EXACT, bool ONE_ROW, int DEPTH>
 __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
     using V = Vec<InT>;
     constexpr int EPV = 8;
@@ -30,9 +32,10 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
 
     const int waves = a.waves;
     const int T = waves * 64;
-    const int rpb = blockDim.x / T;
+    // ONE_ROW: the block is one row group, so the row index is uniform
+    const int rpb = ONE_ROW ? 1 : blockDim.x / T;
     const int tid = threadIdx.x;
-    const int slot = tid / T;
+    const int slot = ONE_ROW ? 0 : tid / T;
     const int lt = tid - slot * T;
     const int red = slot * waves + (lt >> 6);
     const int nvec = a.nvec;  // even: hidden is a multiple of 16
@@ -57,40 +60,39 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
         }
     }
 
-    // Software pipeline over the rows this block owns: the next row's loads are
-    // issued before the current row is reduced and quantized, so every block
-    // keeps a row's worth of reads in flight while it computes.
+    // Software pipeline over the rows this block owns: the loads of the next
+    // DEPTH - 1 rows are in flight while the current row is reduced and
+    // quantized.  DEPTH register buffers rotate (the loop body is unrolled
+    // DEPTH times, so buffer indices are compile-time and no row is ever
+    // copied between registers).  A lane's vectors past the end of the row are
+    // the same on every row: they are zeroed once and never loaded.
     const int64_t stride = (int64_t)gridDim.x * rpb;
-    uint4 xn[VPT];  // the next row (zero past the end of the row)
-    auto fetch = [&](int64_t r) {
-        const char* xr = static_cast<const char*>(a.x) + r * row_bytes;
+    uint4 xb[DEPTH][VPT];
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) xn[k] = live(k) ? load_stream(xr, lt + k * T) : make_uint4(0, 0, 0, 0);
+    for (int b = 0; b < DEPTH; ++b)
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) xb[b][k] = make_uint4(0, 0, 0, 0);
+    auto fetch = [&](uint4 (&xn)[VPT], int64_t r) {
+        if (r < a.rows) {
+            const char* xr = static_cast<const char*>(a.x) + r * row_bytes;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k)
+                if (live(k)) xn[k] = load_stream(xr, lt + k * T);
+        }
     };
-    if ((int64_t)blockIdx.x * rpb + slot < a.rows) fetch((int64_t)blockIdx.x * rpb + slot);
 
     int parity = 0;
-    for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += stride) {
+    // One row group: reduce, then quantize.  Every wave of the block calls
+    // this for the same row0 (the barrier inside is uniform).
+    auto process = [&](const uint4 (&xv)[VPT], int64_t row0) {
         const int64_t row = row0 + slot;
         const bool active = row < a.rows;
 
-        float t[VPT][EPV];
         double ssq = 0.0;
         if (active) {
-            uint4 xv[VPT];
 #pragma unroll
-            for (int k = 0; k < VPT; ++k) xv[k] = xn[k];
-            if (row + stride < a.rows) fetch(row + stride);
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                ssq += (double)V::sumsq(xv[k]);
-                float s[EPV];
-                V::unpack(xv[k], s);
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) t[k][e] = s[e] * g[k][e];
-            }
+            for (int k = 0; k < VPT; ++k) ssq += (double)V::sumsq(xv[k]);
         }
-
         ssq = wave_sum(ssq);
         if (waves > 1) {  // uniform over the block
             if ((lt & 63) == 0) red_sum[parity][red] = ssq;
@@ -113,32 +115,58 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int v = lt + k * T;
+                float t[EPV];  // s * g'
+                V::unpack(xv[k], t);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) t[e] *= g[k][e];
                 // all lanes take part in the swap (vectors past the row are zero)
-                const float amax = pair_max_nonneg(abs_max<EPV>(0.0f, t[k]));
+                const float amax = pair_max_nonneg(abs_max<EPV>(0.0f, t));
                 const uint32_t code = e4m3fn_scale_code(amax * c_scale);
                 const float d = e4m3fn_decode(code);
                 const float kq = d > 0.0f ? c_elem * __builtin_amdgcn_rcpf(d) : 0.0f;
                 if (live(k)) {
                     float q[EPV];
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) q[e] = t[k][e] * kq;
+                    for (int e = 0; e < EPV; ++e) q[e] = t[e] * kq;
                     store_stream(orow, v, e2m1_x8(q));
                     if ((v & 1) == 0) srow[v >> 1] = (uint8_t)code;
                 }
             }
+        }
+    };
+
+    int64_t row0 = (int64_t)blockIdx.x * rpb;
+#pragma unroll
+    for (int b = 0; b + 1 < DEPTH; ++b) fetch(xb[b], row0 + b * stride + slot);
+    while (row0 < a.rows) {
+#pragma unroll
+        for (int b = 0; b < DEPTH; ++b) {
+            fetch(xb[(b + DEPTH - 1) % DEPTH], row0 + (DEPTH - 1) * stride + slot);
+            process(xb[b], row0);
+            row0 += stride;
+            if (row0 >= a.rows) break;
         }
     }
 }
 
 namespace {
 
-template <typename InT, int VPT, bool EXACT>
+// rows in flight per block: the current one and the next (three measured no
+// faster on MI355X and costs 16 more VGPRs at four vectors per lane)
+constexpr int kDepth = 2;
+
+template <typename InT, int VPT, bool EXACT, bool ONE_ROW>
 hipError_t launch_kernel(const FusedArgs& a, Shape s, hipStream_t stream) {
-    auto kern = fp4_kernel<InT, VPT, EXACT>;
+    auto kern = fp4_kernel<InT, VPT, EXACT, ONE_ROW, kDepth>;
     const int threads = s.waves * s.rpb * 64;
     const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
-    // default: persistent, one block per resident slot
-    int64_t grid = s.grid > 0 ? s.grid : (int64_t)persistent_blocks(reinterpret_cast<const void*>(kern), threads);
+    // default: at most 4 row groups per block (MI355X streams this kernel best
+    // that way), and at least one block per resident slot while rows last
+    int64_t grid = s.grid;
+    if (grid <= 0) {
+        const int64_t resident = persistent_blocks(reinterpret_cast<const void*>(kern), threads);
+        grid = std::max(std::min(groups, resident), (groups + 3) / 4);
+    }
     if (grid > groups) grid = groups;
     if (grid > INT32_MAX) grid = INT32_MAX;
     if (grid < 1) grid = 1;
@@ -149,8 +177,10 @@ hipError_t launch_kernel(const FusedArgs& a, Shape s, hipStream_t stream) {
 template <typename InT, int VPT>
 hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
     a.waves = s.waves;
-    if (a.nvec == VPT * s.waves * 64) return launch_kernel<InT, VPT, true>(a, s, stream);
-    return launch_kernel<InT, VPT, false>(a, s, stream);
+    const bool exact = a.nvec == VPT * s.waves * 64;
+    if (s.rpb == 1)
+        return exact ? launch_kernel<InT, VPT, true, true>(a, s, stream) : launch_kernel<InT, VPT, false, true>(a, s, stream);
+    return exact ? launch_kernel<InT, VPT, true, false>(a, s, stream) : launch_kernel<InT, VPT, false, false>(a, s, stream);
 }
 
 template <typename InT>

@@ -29,7 +29,7 @@
 
 namespace rmsq {
 
-template <typename InT, bool RESID, bool FNUZ, int VPT, bool EXACT>
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW>
 __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
@@ -37,9 +37,10 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
 
     const int waves = a.waves;       // wavefronts per row
     const int T = waves * 64;        // lanes per row
-    const int rpb = blockDim.x / T;  // rows per block
+    // ONE_ROW: the block is one row group, so the row index is uniform
+    const int rpb = ONE_ROW ? 1 : blockDim.x / T;  // rows per block
     const int tid = threadIdx.x;
-    const int slot = tid / T;       // row slot within the block
+    const int slot = ONE_ROW ? 0 : tid / T;        // row slot within the block
     const int lt = tid - slot * T;  // lane within the row group
     const int red = slot * waves + (lt >> 6);  // this wave's reduction slot
     const int nvec = a.nvec;
@@ -168,10 +169,18 @@ hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
     if (grid > INT32_MAX) grid = INT32_MAX;
     if (grid < 1) grid = 1;
     const dim3 gd((unsigned)grid), bd(s.waves * s.rpb * 64);
-    if (a.nvec == VPT * s.waves * 64)
-        hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true>), gd, bd, 0, stream, a);
-    else
-        hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false>), gd, bd, 0, stream, a);
+    const bool exact = a.nvec == VPT * s.waves * 64;
+    if (s.rpb == 1) {
+        if (exact)
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, true>), gd, bd, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, true>), gd, bd, 0, stream, a);
+    } else {
+        if (exact)
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, false>), gd, bd, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, false>), gd, bd, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

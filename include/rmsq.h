@@ -156,11 +156,13 @@ int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t str
 
 /*
  * rmsq_set_tuning -- process-wide launch-shape override for subsequent calls
- * (tuning and shape cross-checks).  waves_per_row in {1,2,4,8,16},
+ * (tuning and shape cross-checks).  waves_per_row in 1..16 (wavefronts that
+ * share one row; 1 and 2 put 4/waves rows in a block),
  * vectors_per_lane in {1,2,4} (each vector is 16 bytes of input),
  * grid_blocks sets the number of blocks of the row-strided grid (at most one
- * per row group; the default is the occupancy-limited resident count).  0 for
- * any field keeps the automatic choice.
+ * per row group).  By default the FP8 entry points launch one block per row
+ * group and rmsnorm_fp4 launches max(min(groups, resident blocks),
+ * ceil(groups / 4)) blocks.  0 for any field keeps the automatic choice.
  * Returns RMSQ_ERR_VALUE for an unsupported value.  A call whose hidden does
  * not fit the forced shape returns RMSQ_ERR_UNSUPPORTED.
  */

@@ -217,6 +217,34 @@ def test_tuning_and_query_shape():
         rq.set_tuning(1, 1, 0)
 
 
+@pytest.mark.parametrize("fp4", [False, True])
+def test_automatic_shape_fills_simds(fp4):
+    """Large batches get blocks of a multiple of 4 wavefronts whose lanes hold
+    the row, with the fewest idle lanes among such shapes."""
+    rq.set_tuning(0, 0, 0)
+    try:
+        for dt, epv in ((rq.torch.bfloat16, 8), (rq.torch.float16, 8), (rq.torch.float32, 4)):
+            if fp4 and dt == rq.torch.float32:
+                continue
+            for hidden in range(64 * epv if not fp4 else 128, 4096 * epv + 1, 16 * epv):
+                nvec = hidden // epv
+                s = rq.query_shape(4096, hidden, dt, fp4)
+                w, v, r = s["waves_per_row"], s["vectors_per_lane"], s["rows_per_block"]
+                assert (w * r) % 4 == 0 and w * r <= 16, (hidden, s)
+                assert r == (1 if w >= 4 else 4 // w), (hidden, s)
+                idle = w * 64 * v - nvec
+                assert idle >= 0, (hidden, s)
+                best = min(ww * 64 * vv - nvec for ww in (1, 2, 4, 8, 12, 16) for vv in (1, 2, 4)
+                           if ww * 64 * vv >= nvec)
+                assert idle == best, (hidden, s, best)
+        # the measured preferences on ties
+        assert rq.query_shape(8192, 4096, rq.torch.bfloat16)["vectors_per_lane"] == 2
+        assert rq.query_shape(16384, 7168, rq.torch.bfloat16, True) == {
+            "waves_per_row": 4, "vectors_per_lane": 4, "rows_per_block": 1}
+    finally:
+        rq.set_tuning(1, 1, 0)
+
+
 def test_binding_has_no_fallback(monkeypatch, tmp_path):
     """With the library absent the binding raises instead of computing anything."""
     monkeypatch.setattr(rq, "_lib", None)
