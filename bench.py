@@ -40,6 +40,7 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 CACHE_DEFEAT_BYTES = 1 << 30
+STREAM_MIN_BYTES = 16 << 20  # smaller workloads are latency-bound: no bandwidth reference
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["rmsq_fp8.hip", "rmsq_fp4.hip", "rmsq_device.h", "rmsq_api.cpp"]
 SC_T = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -52,17 +53,24 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w: workloads.Workload) -> int:
-    """One read of every input element, one write of every output, gamma once."""
+def algorithmic_split(w: workloads.Workload) -> tuple[int, int]:
+    """(bytes read, bytes written): one read of every input element (gamma and
+    the global scale once), one write of every output."""
     esz = {"bf16": 2, "f16": 2, "f32": 4}[w.in_dtype]
     n = w.rows * w.hidden
     if w.op == "rmsnorm_fp4":
-        return n * esz + n // 2 + n // 16 + w.hidden * esz + 4
+        return n * esz + w.hidden * esz + 4, n // 2 + n // 16
     ssz = {"f32": 4, "bf16": 2, "f16": 2}[w.scales_dtype]
-    b = n * esz + n + w.rows * ssz + w.hidden * esz
+    reads, writes = n * esz + w.hidden * esz, n + w.rows * ssz
     if w.residual:
-        b += 2 * n * esz  # residual read + residual_out write
-    return b
+        reads += n * esz   # residual
+        writes += n * esz  # residual_out
+    return reads, writes
+
+
+def algorithmic_bytes(w: workloads.Workload) -> int:
+    """One read of every input element, one write of every output, gamma once."""
+    return sum(algorithmic_split(w))
 
 
 class Case:
@@ -139,6 +147,40 @@ def time_case(case: Case, steps: int, warmup: int) -> dict:
             "gbps": b / (per_us * 1e-6) / 1e9, "rows_per_s": case.w.rows / (per_us * 1e-6)}
 
 
+def stream_ceiling(w: workloads.Workload, copies: int, steps: int, warmup: int) -> float:
+    """GB/s of the plain streaming reference kernel (rmsq_stream_probe) moving
+    this workload's read and write bytes, timed like the fused kernel and with
+    the same number of rotated buffer sets."""
+    rb, wb = algorithmic_split(w)
+    rb, wb = -(-rb // 16) * 16, -(-wb // 16) * 16
+    L = rq.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    bufs = []
+    for _ in range(copies):
+        src = torch.ones(rb // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty(wb // 4, dtype=torch.float32, device="cuda:0")
+        bufs.append((src, dst, (ctypes.c_void_p(src.data_ptr()), rb, ctypes.c_void_p(dst.data_ptr()), wb, stream)))
+
+    def step(i):
+        rc = L.rmsq_stream_probe(*bufs[i % copies][2])
+        if rc != 0:
+            raise rq.RmsqError("rmsq_stream_probe", rc, L.rmsq_last_hip_error())
+
+    for i in range(warmup):
+        step(i)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    per_s = t0.elapsed_time(t1) * 1e-3 / steps
+    del bufs
+    torch.cuda.empty_cache()
+    return (rb + wb) / per_s / 1e9
+
+
 def fp4_global_scale() -> float:
     p = os.path.join(ROOT, "tests", "golden", "fp4_global_scale.json")
     return json.load(open(p))["global_scale"]
@@ -209,6 +251,7 @@ def main() -> int:
     ap.add_argument("--workloads", default="all", help="'all', 'headline' or comma-separated workload names")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming reference kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (for counter scaling) and exit")
     args = ap.parse_args()
@@ -244,10 +287,14 @@ def main() -> int:
         res["buffer_sets"] = k
         res["launch"] = rq.query_shape(w.rows, w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.op == "rmsnorm_fp4")
         results[name] = res
-        print(f"# {name}: {res['launch_us']:.2f} us/launch, {res['gbps']:.0f} GB/s, {k} buffer set(s), "
-              f"launch {res['launch']}", file=sys.stderr, flush=True)
         del case
         torch.cuda.empty_cache()
+        # the achievable ceiling for this traffic mix (bandwidth-sized workloads only)
+        res["stream_gbps"] = (stream_ceiling(w, k, steps, args.warmup)
+                              if algorithmic_bytes(w) >= STREAM_MIN_BYTES and not args.no_stream_ceiling else None)
+        ceil = f", streaming reference {res['stream_gbps']:.0f} GB/s" if res["stream_gbps"] else ""
+        print(f"# {name}: {res['launch_us']:.2f} us/launch, {res['gbps']:.0f} GB/s{ceil}, {k} buffer set(s), "
+              f"launch {res['launch']}", file=sys.stderr, flush=True)
 
     h = results[lead]
     w = workloads.WORKLOADS[lead]
@@ -272,10 +319,14 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(h["gbps"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(h["gbps"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles(w.name),
+                     "stream_reference": round(h["stream_gbps"], 1) if h["stream_gbps"] else None,
                      "launch_us": round(h["launch_us"], 3), "bytes_per_launch": h["bytes"]},
         "workloads": {n: {"launch_us": round(r["launch_us"], 3), "gbps": round(r["gbps"], 1),
                           "frac_hbm": round(r["gbps"] / HBM_PEAK_GBS, 4), "rows_per_s": round(r["rows_per_s"], 1),
-                          "bytes": r["bytes"], "buffer_sets": r["buffer_sets"], "launch": r["launch"]}
+                          "bytes": r["bytes"], "buffer_sets": r["buffer_sets"], "launch": r["launch"],
+                          "stream_reference_gbps": round(r["stream_gbps"], 1) if r["stream_gbps"] else None,
+                          "frac_of_stream_reference": round(r["gbps"] / r["stream_gbps"], 4)
+                          if r["stream_gbps"] else None}
                       for n, r in results.items()},
         "kernel_source_hash": kernel_source_hash(),
     }

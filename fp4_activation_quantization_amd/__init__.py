@@ -60,11 +60,13 @@ def lib() -> ctypes.CDLL:
     L.residual_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4.argtypes = [I64, I64, I, P, P, F, F, P, P, P, P]
     L.rmsq_convert.argtypes = [I, P, P, I64, P]
+    L.rmsq_stream_probe.argtypes = [P, I64, P, I64, P]
     L.rmsq_set_tuning.argtypes = [I, I, I]
     L.rmsq_query_shape.argtypes = [I64, I64, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)]
     L.rmsq_status_string.argtypes = [I]
     L.rmsq_status_string.restype = ctypes.c_char_p
-    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsq_convert", "rmsq_set_tuning",
+    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsq_convert", "rmsq_stream_probe",
+               "rmsq_set_tuning",
                "rmsq_query_shape", "rmsq_abi_version", "rmsq_last_hip_error"):
         getattr(L, fn).restype = I
     _lib = L
@@ -157,6 +159,15 @@ def convert(kind: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> tor
     """Elementwise device conversion (C: rmsq_convert); n = src.numel()."""
     _check("rmsq_convert", lib().rmsq_convert(kind, _ptr(src), _ptr(dst), src.numel(), _stream(src, stream)))
     return dst
+
+
+def stream_probe(src: torch.Tensor, read_bytes: int, dst: torch.Tensor, write_bytes: int, stream=None) -> None:
+    """Measurement reference kernel (C: rmsq_stream_probe): reads read_bytes of
+    src and writes write_bytes of dst, in that proportion, computing nothing."""
+    if src.numel() * src.element_size() < read_bytes or dst.numel() * dst.element_size() < write_bytes:
+        raise ValueError("stream_probe: buffer smaller than the byte count")
+    _check("rmsq_stream_probe", lib().rmsq_stream_probe(_ptr(src), read_bytes, _ptr(dst), write_bytes,
+                                                        _stream(src, stream)))
 
 
 def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, grid_blocks: int = 0) -> None:

@@ -263,6 +263,15 @@ int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t str
     return launched(launch_convert(kind, in, out, n, stream));
 }
 
+int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, hipStream_t stream) {
+    if (read_bytes <= 0 || write_bytes <= 0 || read_bytes % 16 != 0 || write_bytes % 16 != 0)
+        return RMSQ_ERR_SHAPE;
+    if (!src || !dst) return RMSQ_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return RMSQ_ERR_ALIGN;
+    if (overlap(Span(src, read_bytes), Span(dst, write_bytes))) return RMSQ_ERR_ALIAS;
+    return launched(launch_stream(src, read_bytes, dst, write_bytes, stream));
+}
+
 int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks) {
     const bool w_ok = waves_per_row >= 0 && waves_per_row <= 16;
     const bool v_ok = vectors_per_lane == 0 || vectors_per_lane == 1 || vectors_per_lane == 2 ||

@@ -47,6 +47,7 @@ hipError_t launch_fp8(const FusedArgs& a, int in_dtype, bool residual, int out_f
                       Shape shape, hipStream_t stream);
 hipError_t launch_fp4(const FusedArgs& a, int in_dtype, Shape shape, hipStream_t stream);
 hipError_t launch_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
+hipError_t launch_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, hipStream_t stream);
 
 // Occupancy-based persistent grid size for a kernel (cached per kernel).
 int persistent_blocks(const void* kernel, int block_threads);

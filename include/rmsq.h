@@ -155,6 +155,22 @@ enum {
 int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
 
 /*
+ * rmsq_stream_probe -- measurement reference, not part of the method: a
+ * kernel that reads read_bytes from src and writes write_bytes to dst with
+ * the fused kernels' 16-byte non-temporal accesses and no arithmetic, in the
+ * same read : write proportion (within 2%) and the same order per block (a
+ * chunk of reads, then a chunk of writes).  Its rate is the achievable HBM
+ * ceiling for a fused workload with that traffic, the "plain streaming
+ * kernel that moves the same bytes" the measurement compares with.
+ *   src, dst   : DEVICE pointers, 16-byte aligned, not overlapping.
+ *   read_bytes, write_bytes : > 0, multiples of 16.
+ * The bytes written are unspecified.  Returns RMSQ_ERR_SHAPE, _NULL, _ALIGN
+ * or _ALIAS before any HIP call, RMSQ_ERR_LAUNCH on a failed launch.
+ */
+int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                      hipStream_t stream);
+
+/*
  * rmsq_set_tuning -- process-wide launch-shape override for subsequent calls
  * (tuning and shape cross-checks).  waves_per_row in 1..16 (wavefronts that
  * share one row; 1 and 2 put 4/waves rows in a block),

@@ -41,8 +41,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsq_convert", "rmsq_set_tuning",
-              "rmsq_query_shape", "rmsq_status_string", "rmsq_abi_version", "rmsq_last_hip_error"):
+    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsq_convert", "rmsq_stream_probe",
+              "rmsq_set_tuning", "rmsq_query_shape", "rmsq_status_string", "rmsq_abi_version",
+              "rmsq_last_hip_error"):
         assert f in fns, f
 
 
@@ -195,6 +196,18 @@ def test_convert_errors():
     assert L.rmsq_convert(rq.CVT_F32_TO_BF16, ctypes.c_void_p(0), P(1), 8, None) == NULL
     assert L.rmsq_convert(rq.CVT_F32_TO_BF16, ctypes.c_void_p(BASE + 4), P(1), 8, None) == ALIGN
     assert L.rmsq_convert(rq.CVT_F32_TO_BF16, P(0), ctypes.c_void_p(BASE + 16), 8, None) == ALIAS
+
+
+def test_stream_probe_argument_checks():
+    """Every rejection happens before a launch (no device needed)."""
+    L = rq.lib()
+    P = lambda off: ctypes.c_void_p(BASE + off)
+    assert L.rmsq_stream_probe(P(0), 0, P(1 << 20), 16, None) == SHAPE
+    assert L.rmsq_stream_probe(P(0), 16, P(1 << 20), 0, None) == SHAPE
+    assert L.rmsq_stream_probe(P(0), 24, P(1 << 20), 16, None) == SHAPE
+    assert L.rmsq_stream_probe(ctypes.c_void_p(0), 16, P(1 << 20), 16, None) == NULL
+    assert L.rmsq_stream_probe(P(8), 16, P(1 << 20), 16, None) == ALIGN
+    assert L.rmsq_stream_probe(P(0), 64, P(32), 64, None) == ALIAS
 
 
 def test_tuning_and_query_shape():
