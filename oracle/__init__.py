@@ -29,10 +29,12 @@ LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 # identifiers private to the oracle (the C file uses the same numbers)
 F32, F16, BF16 = 0, 1, 2
-E4M3FN, E4M3FNUZ, E2M1 = 0, 1, 2
+E4M3FN, E4M3FNUZ, E2M1, UE8M0 = 0, 1, 2, 3
+SF_E4M3, SF_UE8M0 = 0, 1  # FP4 block-scale formats
 
 DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
-FORMATS = {"e4m3fn": E4M3FN, "e4m3fnuz": E4M3FNUZ, "e2m1": E2M1}
+FORMATS = {"e4m3fn": E4M3FN, "e4m3fnuz": E4M3FNUZ, "e2m1": E2M1, "ue8m0": UE8M0}
+SCALE_FORMATS = {"e4m3": SF_E4M3, "ue8m0": SF_UE8M0}
 
 _lib = None
 
@@ -51,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.oracle_rmsnorm_fp8.restype = I
     L.oracle_rmsnorm_fp4.argtypes = [I64, I64, I, P, P, D, D, D, P, P, P, P]
     L.oracle_rmsnorm_fp4.restype = I
+    L.oracle_rmsnorm_fp4q.argtypes = [I64, I64, I, P, P, D, D, D, I, I, P, P, P, P]
+    L.oracle_rmsnorm_fp4q.restype = I
     L.oracle_rmsnorm_y.argtypes = [I64, I64, I, P, P, P, P, D, D, P, P]
     L.oracle_rmsnorm_y.restype = I
     L.oracle_rmsnorm_absmax.argtypes = [I64, I64, I, P, P, D, D]
@@ -131,35 +135,75 @@ def rmsnorm_fp8(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, sc
 
 
 def rmsnorm_fp4(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, global_scale: float,
-                threads: int | None = None, want_q: bool = True) -> dict:
-    """Reference FP4 (E2M1, one E4M3 scale per 16 elements) path.
+                threads: int | None = None, want_q: bool = True, block_size: int = 16,
+                scale_format: str = "e4m3") -> dict:
+    """Reference FP4 (E2M1) path with one scale per block of block_size (16 or
+    32) elements: E4M3 scales (gs * amax / 6 clamped to 448) or UE8M0 scales
+    (power of two >= amax / 6, no global scale).
 
     Returns packed [rows, hidden/2] (element 2k in the low nibble),
-    block_scales [rows, hidden/16] (E4M3FN codes), q [rows, hidden] float64
-    and sf [rows, hidden/16] float64 (unrounded block scale after the clamp).
+    block_scales [rows, hidden/block_size] (scale codes, row-major), q
+    [rows, hidden] float64 and sf [rows, hidden/block_size] float64 (the
+    unrounded block scale: after the clamp for E4M3, amax / 6 for UE8M0).
     """
     L = lib()
     x = _bits_array(x, in_dtype)
     g = _bits_array(gamma, in_dtype)
     rows, hidden = x.shape
-    if hidden % 16:
-        raise ValueError("hidden must be a multiple of 16")
+    if block_size not in (16, 32) or scale_format not in SCALE_FORMATS:
+        raise ValueError("block_size must be 16 or 32 and scale_format e4m3 or ue8m0")
+    if hidden % block_size:
+        raise ValueError(f"hidden must be a multiple of {block_size}")
+    nblk = hidden // block_size
     packed = np.empty((rows, hidden // 2), np.uint8)
-    bs = np.empty((rows, hidden // 16), np.uint8)
+    bs = np.empty((rows, nblk), np.uint8)
     q = np.empty((rows, hidden), np.float64) if want_q else None
-    sf = np.empty((rows, hidden // 16), np.float64)
+    sf = np.empty((rows, nblk), np.float64)
     e, o, gs = (float(np.float32(v)) for v in (eps, weight_offset, global_scale))
+    sfmt = SCALE_FORMATS[scale_format]
 
     def work(r0, r1):
         n = r1 - r0
         if n <= 0:
             return 0
-        return L.oracle_rmsnorm_fp4(n, hidden, DTYPES[in_dtype], _ptr(x[r0:r1]), _ptr(g), e, o, gs,
-                                    _ptr(packed[r0:r1]), _ptr(bs[r0:r1]),
-                                    _ptr(q[r0:r1]) if q is not None else None, _ptr(sf[r0:r1]))
+        return L.oracle_rmsnorm_fp4q(n, hidden, DTYPES[in_dtype], _ptr(x[r0:r1]), _ptr(g), e, o, gs, block_size,
+                                     sfmt, _ptr(packed[r0:r1]), _ptr(bs[r0:r1]),
+                                     _ptr(q[r0:r1]) if q is not None else None, _ptr(sf[r0:r1]))
 
     _run(work, rows, threads)
     return {"packed": packed, "block_scales": bs, "q": q, "sf": sf}
+
+
+# ---- swizzled scale layout ---------------------------------------------------
+# FlashInfer "rmsnorm_fp4quant.py", the kernel's scale store and the API
+# docstring: 128 x 4 tiles, flat offset
+#   m_tile * (k_tiles * 512) + k_tile * 512 + outer_m * 16 + inner_m * 4 + inner_k
+# with m_tile = row // 128, inner_m = (row % 128) // 32, outer_m = row % 32,
+# k_tile = sf // 4, inner_k = sf % 4, k_tiles = ceil(sf_per_row / 4); the
+# buffer holds ceil(rows / 128) * k_tiles * 512 bytes.  Positions of rows or
+# scale columns past the ends (the tiles' padding) are not written.
+
+def swizzled_size(rows: int, sf_per_row: int) -> int:
+    return -(-rows // 128) * -(-sf_per_row // 4) * 512
+
+
+def swizzled_offset(row, sf, sf_per_row: int):
+    row = np.asarray(row, dtype=np.int64)
+    sf = np.asarray(sf, dtype=np.int64)
+    k_tiles = -(-sf_per_row // 4)
+    return ((row // 128) * (k_tiles * 512) + (sf // 4) * 512 + (row % 32) * 16 + ((row % 128) // 32) * 4
+            + sf % 4)
+
+
+def swizzle_scales(block_scales: np.ndarray, out: np.ndarray | None = None, fill: int = 0) -> np.ndarray:
+    """Place a row-major [rows, sf_per_row] scale matrix at its swizzled
+    offsets; padding positions keep `out`'s bytes (or `fill`)."""
+    rows, nsf = block_scales.shape
+    if out is None:
+        out = np.full(swizzled_size(rows, nsf), fill, np.uint8)
+    r, c = np.meshgrid(np.arange(rows), np.arange(nsf), indexing="ij")
+    out[swizzled_offset(r, c, nsf)] = block_scales
+    return out
 
 
 def rmsnorm_y(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, residual=None,

@@ -21,7 +21,11 @@
  *        kernel "Phase 2" (mean of squares over the full row, reciprocal
  *        square root of mean + eps) and "Phase 3" (block scale =
  *        global_scale * block_amax / 6 clamped to 448, then RNE to E4M3;
- *        quantize with global_scale / decoded_scale).
+ *        quantize with global_scale / decoded_scale); section "UE8M0
+ *        Intrinsics (for MXFP4)" (scale code = ceil(log2(v)) + 127 clamped
+ *        to [0, 255], zero for v <= 0; element factor 2^(127 - code), zero
+ *        for code 0; no global scale) and the kernel's constructor and API
+ *        docstring (block_size 16 or 32, scale_format e4m3 or ue8m0).
  *
  * Readings where the pages are silent or disagree (each listed in the
  * project's design notes):
@@ -42,6 +46,8 @@
  *             code 0x80 is NaN, so a zero result is always 0x00.
  *   E2M1    : 2 exp bits, 1 mantissa, bias 1, largest code 7 = 6.0, sign in
  *             bit 3.
+ *   UE8M0   : 8 exponent bits, no sign, no mantissa: code c stands for
+ *             2^(c - 127); used only as a block scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -50,7 +56,8 @@
 
 /* ---- dtype and format identifiers private to the oracle ---------------- */
 enum { ORQ_F32 = 0, ORQ_F16 = 1, ORQ_BF16 = 2 };
-enum { ORQ_E4M3FN = 0, ORQ_E4M3FNUZ = 1, ORQ_E2M1 = 2 };
+enum { ORQ_E4M3FN = 0, ORQ_E4M3FNUZ = 1, ORQ_E2M1 = 2, ORQ_UE8M0 = 3 };
+enum { ORQ_SF_E4M3 = 0, ORQ_SF_UE8M0 = 1 }; /* FP4 block-scale formats */
 
 typedef struct {
     int ebits, mbits, bias;
@@ -78,7 +85,26 @@ static double mag_value(const minifloat* f, int m) {
     return ldexp((double)((1 << f->mbits) + man), e - f->bias - f->mbits);
 }
 
+/* UE8M0 block scale of a value v ([P3] "UE8M0 Intrinsics"): the exponent of
+ * the smallest power of two >= v, biased by 127 and clamped to [0, 255];
+ * v <= 0 (or NaN) gives 0.  frexp splits v = m * 2^e with m in [0.5, 1), so
+ * ceil(log2(v)) is e, or e - 1 when m is exactly 0.5 (v = 2^(e-1)). */
+static int ue8m0_encode(double v) {
+    if (!(v > 0.0)) return 0;
+    if (isinf(v)) return 255;
+    int e;
+    double m = frexp(v, &e);
+    int c = (m == 0.5 ? e - 1 : e) + 127;
+    return c < 0 ? 0 : (c > 255 ? 255 : c);
+}
+
+/* The factor elements of a UE8M0-scaled block are multiplied by:
+ * 1 / 2^(code - 127) = 2^(127 - code), and 0 for code 0 ([P3] "UE8M0
+ * Intrinsics", its zero check). */
+static double ue8m0_inverse(int code) { return code == 0 ? 0.0 : ldexp(1.0, 127 - code); }
+
 double oracle_decode(int fmt, int code) {
+    if (fmt == ORQ_UE8M0) return ldexp(1.0, code - 127);
     minifloat f = fmt_of(fmt);
     int sign = (code >> f.sign_bit) & 1;
     int m = code & ((1 << f.sign_bit) - 1);
@@ -92,6 +118,7 @@ double oracle_decode(int fmt, int code) {
  * saturating to the largest finite value.  Sign is the sign bit of v.
  * Found by walking the ordered magnitude codes: slow and plain. */
 int oracle_encode(int fmt, double v) {
+    if (fmt == ORQ_UE8M0) return ue8m0_encode(v);
     minifloat f = fmt_of(fmt);
     int neg = signbit(v) ? 1 : 0;
     double a = fabs(v);
@@ -284,23 +311,28 @@ int oracle_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dt,
     return 0;
 }
 
-/* FP4 block-scaled quantization ([P3] "Phase 3", 16-element blocks).
+/* FP4 block-scaled quantization ([P3] "Phase 3"), blocks of `block` (16 or
+ * 32) consecutive elements of a row, one scale per block:
+ *   sfmt ORQ_SF_E4M3 : scale = min(gs * amax / 6, 448) rounded to E4M3FN,
+ *                      element factor gs / decoded scale (0 if it is 0);
+ *   sfmt ORQ_SF_UE8M0: scale code = UE8M0(amax / 6), element factor
+ *                      2^(127 - code) (0 for code 0); gs is not used.
+ * Elements are then E2M1 codes of y * factor (saturating RNE).
  *   out: [rows, hidden/2] bytes, element 2k in the low nibble of byte k.
- *   block_scales: [rows, hidden/16] E4M3FN codes, row-major.
+ *   block_scales: [rows, hidden/block] scale codes, row-major.
  *   global_scale: the fp32 value, widened.
  *   q_out (optional): [rows, hidden] unrounded float64 quantizer input.
- *   sf_out (optional): [rows, hidden/16] unrounded float64 block scale
- *   (after the clamp to 448).
- * hidden must be a multiple of 16.  Returns 0, -1 on allocation failure,
- * -2 on a bad hidden. */
-int oracle_rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dt,
-                       const void* x, const void* gamma, double eps, double offset,
-                       double global_scale, uint8_t* out, uint8_t* block_scales,
-                       double* q_out, double* sf_out) {
-    const int block = 16;
+ *   sf_out (optional): [rows, hidden/block] unrounded float64 block scale
+ *   (after the clamp to 448 for E4M3; amax / 6 for UE8M0).
+ * Returns 0, -1 on allocation failure, -2 on a bad hidden / block / format. */
+int oracle_rmsnorm_fp4q(int64_t rows, int64_t hidden, int in_dt,
+                        const void* x, const void* gamma, double eps, double offset,
+                        double global_scale, int block, int sfmt, uint8_t* out, uint8_t* block_scales,
+                        double* q_out, double* sf_out) {
     minifloat e4m3 = fmt_of(ORQ_E4M3FN), e2m1 = fmt_of(ORQ_E2M1);
     const double e4m3_max = mag_value(&e4m3, e4m3.max_mag); /* 448 */
     const double e2m1_max = mag_value(&e2m1, e2m1.max_mag); /* 6 */
+    if ((block != 16 && block != 32) || (sfmt != ORQ_SF_E4M3 && sfmt != ORQ_SF_UE8M0)) return -2;
     if (hidden % block) return -2;
     size_t esz = in_dt == ORQ_F32 ? 4 : 2;
     int64_t nblk = hidden / block;
@@ -315,15 +347,24 @@ int oracle_rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dt,
             double amax = 0.0;
             for (int k = 0; k < block; k++)
                 if (fabs(y[b * block + k]) > amax) amax = fabs(y[b * block + k]);
-            double sf = global_scale * amax / e2m1_max;
-            if (sf > e4m3_max) sf = e4m3_max;
+            double sf, d = 0.0, inv = 0.0;
+            int S;
+            if (sfmt == ORQ_SF_E4M3) {
+                sf = global_scale * amax / e2m1_max;
+                if (sf > e4m3_max) sf = e4m3_max;
+                S = oracle_encode(ORQ_E4M3FN, (double)(float)sf);
+                d = oracle_decode(ORQ_E4M3FN, S);
+            } else {
+                sf = amax / e2m1_max;
+                S = ue8m0_encode((double)(float)sf);
+                inv = ue8m0_inverse(S); /* a power of two: y * inv is exact */
+            }
             if (sf_out) sf_out[r * nblk + b] = sf;
-            int S = oracle_encode(ORQ_E4M3FN, (double)(float)sf);
             block_scales[r * nblk + b] = (uint8_t)S;
-            double d = oracle_decode(ORQ_E4M3FN, S);
             for (int k = 0; k < block; k++) {
                 int64_t j = b * block + k;
-                double q = d > 0.0 ? y[j] * global_scale / d : y[j] * 0.0;
+                /* a zero factor keeps the sign of y */
+                double q = sfmt == ORQ_SF_UE8M0 ? y[j] * inv : (d > 0.0 ? y[j] * global_scale / d : y[j] * 0.0);
                 if (q_out) q_out[r * hidden + j] = q;
                 c[j] = oracle_encode(ORQ_E2M1, (double)(float)q);
             }
@@ -335,6 +376,15 @@ int oracle_rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dt,
     free(y);
     free(c);
     return 0;
+}
+
+/* The page's default configuration: 16-element blocks, E4M3 scales. */
+int oracle_rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dt,
+                       const void* x, const void* gamma, double eps, double offset,
+                       double global_scale, uint8_t* out, uint8_t* block_scales,
+                       double* q_out, double* sf_out) {
+    return oracle_rmsnorm_fp4q(rows, hidden, in_dt, x, gamma, eps, offset, global_scale, 16, ORQ_SF_E4M3,
+                               out, block_scales, q_out, sf_out);
 }
 
 /* The normalized values y = s * rstd * (gamma + offset) as float64
