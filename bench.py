@@ -59,7 +59,9 @@ def algorithmic_split(w: workloads.Workload) -> tuple[int, int]:
     esz = {"bf16": 2, "f16": 2, "f32": 4}[w.in_dtype]
     n = w.rows * w.hidden
     if w.op == "rmsnorm_fp4":
-        return n * esz + w.hidden * esz + 4, n // 2 + n // 16
+        # the global scale is read only with E4M3 scales; padding of the
+        # swizzled scale tiles is not written
+        return n * esz + w.hidden * esz + (4 if w.fp4_scale == "e4m3" else 0), n // 2 + n // w.fp4_block
     ssz = {"f32": 4, "bf16": 2, "f16": 2}[w.scales_dtype]
     reads, writes = n * esz + w.hidden * esz, n + w.rows * ssz
     if w.residual:
@@ -93,11 +95,15 @@ class Case:
             x = x0 if i == 0 else x0.clone()
             if w.op == "rmsnorm_fp4":
                 out = torch.empty((w.rows, w.hidden // 2), dtype=torch.uint8, device=dev)
-                bs = torch.empty((w.rows, w.hidden // 16), dtype=torch.uint8, device=dev)
+                bs = torch.empty((rq.fp4_scale_bytes(w.rows, w.hidden, w.fp4_block, w.fp4_swizzled),),
+                                 dtype=torch.uint8, device=dev)
                 gst = torch.tensor([gs], dtype=torch.float32, device=dev)
                 self.keep += [x, out, bs, gst]
-                args = (w.rows, w.hidden, dt, P(x), P(g), w.eps, w.weight_offset, P(gst), P(out), P(bs), stream)
-                self.calls.append((L.rmsnorm_fp4, args))
+                sfmt = rq.SF_UE8M0 if w.fp4_scale == "ue8m0" else rq.SF_E4M3
+                layout = rq.SF_SWIZZLED if w.fp4_swizzled else rq.SF_ROW_MAJOR
+                args = (w.rows, w.hidden, dt, P(x), P(g), w.eps, w.weight_offset, P(gst), w.fp4_block, sfmt, layout,
+                        P(out), P(bs), stream)
+                self.calls.append((L.rmsnorm_fp4quant, args))
                 continue
             out = torch.empty((w.rows, w.hidden), dtype=torch.uint8, device=dev)
             sc = torch.empty((w.rows,), dtype=SC_T[w.scales_dtype], device=dev)

@@ -26,6 +26,8 @@ LIB_PATH = os.path.join(HERE, "librmsq.so")
 # enums of include/rmsq.h
 F32, F16, BF16 = 0, 1, 2
 E4M3FN, E4M3FNUZ = 0, 1
+SF_E4M3, SF_UE8M0 = 0, 1            # FP4 block-scale formats
+SF_ROW_MAJOR, SF_SWIZZLED = 0, 1    # FP4 block-scale layouts
 CVT_F32_TO_E4M3FN, CVT_F32_TO_E4M3FNUZ, CVT_F32_TO_E2M1, CVT_F32_TO_BF16, CVT_F32_TO_F16, CVT_E4M3FN_TO_F32 = range(6)
 STATUS = {0: "RMSQ_OK", -1: "RMSQ_ERR_NULL", -2: "RMSQ_ERR_DTYPE", -3: "RMSQ_ERR_SHAPE", -4: "RMSQ_ERR_ALIGN",
           -5: "RMSQ_ERR_VALUE", -6: "RMSQ_ERR_ALIAS", -7: "RMSQ_ERR_UNSUPPORTED", -8: "RMSQ_ERR_LAUNCH"}
@@ -59,13 +61,17 @@ def lib() -> ctypes.CDLL:
     L.rmsnorm_fp8.argtypes = [I64, I64, I, P, P, F, F, F, I, P, I, P, P]
     L.residual_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4.argtypes = [I64, I64, I, P, P, F, F, P, P, P, P]
+    L.rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, F, F, P, I, I, I, P, P, P]
+    L.rmsq_fp4_scale_bytes.argtypes = [I64, I64, I, I]
+    L.rmsq_fp4_scale_bytes.restype = I64
     L.rmsq_convert.argtypes = [I, P, P, I64, P]
     L.rmsq_stream_probe.argtypes = [P, I64, P, I64, P]
     L.rmsq_set_tuning.argtypes = [I, I, I]
     L.rmsq_query_shape.argtypes = [I64, I64, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)]
     L.rmsq_status_string.argtypes = [I]
     L.rmsq_status_string.restype = ctypes.c_char_p
-    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsq_convert", "rmsq_stream_probe",
+    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "rmsq_convert",
+               "rmsq_stream_probe",
                "rmsq_set_tuning",
                "rmsq_query_shape", "rmsq_abi_version", "rmsq_last_hip_error"):
         getattr(L, fn).restype = I
@@ -152,6 +158,48 @@ def rmsnorm_fp4(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, out=No
     _check("rmsnorm_fp4", lib().rmsnorm_fp4(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset,
                                             _ptr(global_scale), _ptr(_u8(out)), _ptr(_u8(block_scales)),
                                             _stream(x, stream)))
+    return out, block_scales
+
+
+def fp4_scale_bytes(rows: int, hidden: int, block_size: int = 16, swizzled: bool = False) -> int:
+    """Bytes of the block-scale buffer (C: rmsq_fp4_scale_bytes)."""
+    n = lib().rmsq_fp4_scale_bytes(rows, hidden, block_size, SF_SWIZZLED if swizzled else SF_ROW_MAJOR)
+    if n < 0:
+        _check("rmsq_fp4_scale_bytes", int(n))
+    return int(n)
+
+
+def rmsnorm_fp4quant(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, block_size=16,
+                     scale_format=None, swizzled=False, out=None, block_scales=None, stream=None):
+    """RMSNorm + FP4 E2M1 with one scale per block_size (16 or 32) elements
+    (C: rmsnorm_fp4quant).
+
+    scale_format: "e4m3" or "ue8m0"; None picks "e4m3" for 16-element and
+    "ue8m0" for 32-element blocks.  global_scale (a one-element float32
+    device tensor, or None for 1.0) is used by E4M3 scales only.
+    swizzled: 128 x 4-tile scale layout (a flat uint8 buffer of
+    fp4_scale_bytes() bytes) instead of [..., H/block_size] row-major.
+    Returns (packed uint8 [..., H/2], block_scales uint8).
+    """
+    rows, hidden = _rows_hidden(x)
+    if scale_format is None:
+        scale_format = "ue8m0" if block_size == 32 else "e4m3"
+    sfmt = {"e4m3": SF_E4M3, "ue8m0": SF_UE8M0}[scale_format]
+    if out is None:
+        out = torch.empty((*x.shape[:-1], hidden // 2), dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        if swizzled:
+            block_scales = torch.empty((fp4_scale_bytes(rows, hidden, block_size, True),), dtype=torch.uint8,
+                                       device=x.device)
+        else:
+            block_scales = torch.empty((*x.shape[:-1], hidden // block_size), dtype=torch.uint8, device=x.device)
+    elif block_scales.numel() * block_scales.element_size() < fp4_scale_bytes(rows, hidden, block_size, swizzled):
+        raise ValueError("block_scales is smaller than fp4_scale_bytes()")
+    if global_scale is not None and (global_scale.dtype != torch.float32 or global_scale.numel() != 1):
+        raise ValueError("global_scale must be a one-element float32 tensor")
+    _check("rmsnorm_fp4quant", lib().rmsnorm_fp4quant(
+        rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset, _ptr(global_scale), block_size, sfmt,
+        SF_SWIZZLED if swizzled else SF_ROW_MAJOR, _ptr(_u8(out)), _ptr(_u8(block_scales)), _stream(x, stream)))
     return out, block_scales
 
 

@@ -209,11 +209,23 @@ int residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, const void*
                       scale_ub, out_fp8, out, scales_dtype, scales, stream);
 }
 
-int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
-                float weight_offset, const float* global_scale, void* out, void* block_scales,
-                hipStream_t stream) {
+int64_t rmsq_fp4_scale_bytes(int64_t rows, int64_t hidden, int block_size, int scale_layout) {
+    if (block_size != 16 && block_size != 32) return RMSQ_ERR_VALUE;
+    if (scale_layout != RMSQ_SF_ROW_MAJOR && scale_layout != RMSQ_SF_SWIZZLED) return RMSQ_ERR_DTYPE;
+    if (rows < 0 || hidden <= 0 || hidden % block_size != 0 || !size_ok(rows, hidden, 2)) return RMSQ_ERR_SHAPE;
+    const int64_t nsf = hidden / block_size;
+    if (scale_layout == RMSQ_SF_ROW_MAJOR) return rows * nsf;
+    return ceil_div(rows, 128) * ceil_div(nsf, 4) * 512;
+}
+
+int rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
+                     float weight_offset, const float* global_scale, int block_size, int scale_format,
+                     int scale_layout, void* out, void* block_scales, hipStream_t stream) {
     if (in_dtype != RMSQ_F16 && in_dtype != RMSQ_BF16) return RMSQ_ERR_DTYPE;
-    if (rows < 0 || hidden <= 0 || hidden % 16 != 0) return RMSQ_ERR_SHAPE;
+    if (scale_format != RMSQ_SF_E4M3 && scale_format != RMSQ_SF_UE8M0) return RMSQ_ERR_DTYPE;
+    if (scale_layout != RMSQ_SF_ROW_MAJOR && scale_layout != RMSQ_SF_SWIZZLED) return RMSQ_ERR_DTYPE;
+    if (block_size != 16 && block_size != 32) return RMSQ_ERR_VALUE;
+    if (rows < 0 || hidden <= 0 || hidden % block_size != 0) return RMSQ_ERR_SHAPE;
     if (!size_ok(rows, hidden, 2)) return RMSQ_ERR_SHAPE;
     if (int rc = check_scalars(eps, weight_offset, 1.0f, false)) return rc;
     const int nvec = (int)(hidden / 8);
@@ -221,13 +233,15 @@ int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const
     if (rows == 0) return RMSQ_OK;
     if (!x || !gamma || !out || !block_scales) return RMSQ_ERR_NULL;
     if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(out, 16)) return RMSQ_ERR_ALIGN;
-    if (global_scale && !aligned(global_scale, 4)) return RMSQ_ERR_ALIGN;
-    const Span sx(x, rows * hidden * 2), sg(gamma, hidden * 2), so(out, rows * hidden / 2),
-        ss(block_scales, rows * hidden / 16);
+    // the global scale is read only for E4M3 scales
+    const float* gsp = scale_format == RMSQ_SF_E4M3 ? global_scale : nullptr;
+    if (gsp && !aligned(gsp, 4)) return RMSQ_ERR_ALIGN;
+    const int64_t sbytes = rmsq_fp4_scale_bytes(rows, hidden, block_size, scale_layout);
+    const Span sx(x, rows * hidden * 2), sg(gamma, hidden * 2), so(out, rows * hidden / 2), ss(block_scales, sbytes);
     if (overlap(so, ss) || overlap(so, sx) || overlap(so, sg) || overlap(ss, sx) || overlap(ss, sg))
         return RMSQ_ERR_ALIAS;
-    if (global_scale) {
-        const Span sgs(global_scale, 4);
+    if (gsp) {
+        const Span sgs(gsp, 4);
         if (overlap(sgs, so) || overlap(sgs, ss)) return RMSQ_ERR_ALIAS;
     }
     Shape shape;
@@ -237,14 +251,24 @@ int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const
     a.gamma = gamma;
     a.out = out;
     a.scales = block_scales;
-    a.global_scale = global_scale;
+    a.global_scale = gsp;
     a.rows = rows;
     a.hidden = (int32_t)hidden;
     a.inv_hidden = 1.0 / (double)hidden;
     a.nvec = nvec;
     a.eps = eps;
     a.weight_offset = weight_offset;
-    return launched(launch_fp4(a, in_dtype, shape, stream));
+    a.sf_swizzled = scale_layout == RMSQ_SF_SWIZZLED ? 1 : 0;
+    a.sf_k_tiles = (int32_t)ceil_div(hidden / block_size, 4);
+    const Fp4Format fmt{block_size, scale_format == RMSQ_SF_UE8M0};
+    return launched(launch_fp4(a, in_dtype, fmt, shape, stream));
+}
+
+int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
+                float weight_offset, const float* global_scale, void* out, void* block_scales,
+                hipStream_t stream) {
+    return rmsnorm_fp4quant(rows, hidden, in_dtype, x, gamma, eps, weight_offset, global_scale, 16, RMSQ_SF_E4M3,
+                            RMSQ_SF_ROW_MAJOR, out, block_scales, stream);
 }
 
 int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream) {

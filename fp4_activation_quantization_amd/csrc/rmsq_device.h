@@ -213,10 +213,20 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
     return __int_as_float(r);
 }
 
-// max(v, v of lane ^ 1) for non-negative v (the two halves of an FP4 block).
+// max(v, v of lane ^ 1) for non-negative v (the two halves of a 16-element
+// FP4 block).
 __device__ __forceinline__ float pair_max_nonneg(float v) {
     const int b = __float_as_int(v);
     return __int_as_float(max_bits(b, dpp_i32<DPP_SWAP1>(b)));
+}
+
+// max over the lanes 4j .. 4j+3 for non-negative v (the four quarters of a
+// 32-element FP4 block).
+__device__ __forceinline__ float quad_max_nonneg(float v) {
+    int b = __float_as_int(v);
+    b = max_bits(b, dpp_i32<DPP_SWAP1>(b));
+    b = max_bits(b, dpp_i32<DPP_SWAP2>(b));
+    return __int_as_float(b);
 }
 
 // ---- conversions ------------------------------------------------------------
@@ -264,6 +274,23 @@ __device__ __forceinline__ uint32_t fp8_x4(float a, float b, float c, float d) {
 __device__ __forceinline__ uint32_t e4m3fn_scale_code(float v) {
     v = fminf(v, 448.0f);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, __float_as_int(v), false);
+}
+
+// UE8M0 block-scale code of a non-negative fp32 value v: the exponent of the
+// smallest power of two >= v, plus 127, clamped to [0, 255] (0 for v = 0).
+// For a normal v that is the exponent field, plus one when any mantissa bit
+// is set: adding 0x7FFFFF to the bits carries into the exponent exactly then
+// (and the largest finite value gives 255).  A subnormal v (< 2^-126) has
+// code 1 above 2^-127 and 0 at or below it.
+__device__ __forceinline__ uint32_t ue8m0_code(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return b >= 0x00800000u ? (b + 0x007FFFFFu) >> 23 : (b > 0x00400000u ? 1u : 0u);
+}
+
+// c * 2^(127 - code), and 0 for code 0: the element factor of a UE8M0 block
+// (v_ldexp_f32 scales exactly unless the result leaves the fp32 range).
+__device__ __forceinline__ float ue8m0_factor(float c, uint32_t code) {
+    return code == 0 ? 0.0f : __builtin_amdgcn_ldexpf(c, 127 - (int)code);
 }
 
 // Exact value of the e4m3fn code in the low byte of `code` (v_cvt_f32_fp8).

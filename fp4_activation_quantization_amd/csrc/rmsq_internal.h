@@ -15,8 +15,8 @@ struct FusedArgs {
     void* residual_out;        // FP8 residual variant only
     const void* gamma;
     void* out;                 // FP8: [rows, hidden]; FP4: [rows, hidden/2]
-    void* scales;              // FP8: [rows]; FP4: [rows, hidden/16]
-    const float* global_scale; // FP4 only; may be null (1.0)
+    void* scales;              // FP8: [rows]; FP4: [rows, hidden/block] or swizzled
+    const float* global_scale; // FP4 E4M3 scales only; may be null (1.0)
     int64_t rows;
     double inv_hidden;         // 1.0 / hidden
     int32_t hidden;
@@ -26,6 +26,14 @@ struct FusedArgs {
     float scale_ub;            // FP8 only
     int32_t scales_dtype;      // FP8 only (RMSQ_F32/F16/BF16)
     int32_t waves;             // wavefronts per row (set by the launcher)
+    int32_t sf_swizzled;       // FP4: 1 for the 128x4-tile scale layout
+    int32_t sf_k_tiles;        // FP4 swizzled: ceil((hidden / block) / 4)
+};
+
+// FP4 variant: elements per block scale and the scale format.
+struct Fp4Format {
+    int block;   // 16 or 32
+    bool ue8m0;  // UE8M0 power-of-two scales (else E4M3)
 };
 
 // Launch shape: one row is handled by `waves` wavefronts (64 lanes each, any
@@ -45,7 +53,7 @@ bool choose_shape(int64_t rows, int nvec, bool fp4, Shape* s);
 // Kernel launchers (no argument checks).  Return the hipError_t of the launch.
 hipError_t launch_fp8(const FusedArgs& a, int in_dtype, bool residual, int out_fp8,
                       Shape shape, hipStream_t stream);
-hipError_t launch_fp4(const FusedArgs& a, int in_dtype, Shape shape, hipStream_t stream);
+hipError_t launch_fp4(const FusedArgs& a, int in_dtype, Fp4Format fmt, Shape shape, hipStream_t stream);
 hipError_t launch_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
 hipError_t launch_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, hipStream_t stream);
 

@@ -131,6 +131,48 @@ int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype,
                 float eps, float weight_offset, const float* global_scale,
                 void* out, void* block_scales, hipStream_t stream);
 
+/* FP4 block-scale formats and layouts (rmsnorm_fp4quant). */
+enum { RMSQ_SF_E4M3 = 0, RMSQ_SF_UE8M0 = 1 };
+enum { RMSQ_SF_ROW_MAJOR = 0, RMSQ_SF_SWIZZLED = 1 };
+
+/*
+ * rmsnorm_fp4quant -- the general form of rmsnorm_fp4, with the options of
+ * FlashInfer "rmsnorm_fp4quant.py" (its API docstring: block_size,
+ * scale_format, is_sf_swizzled_layout; section "UE8M0 Intrinsics (for
+ * MXFP4)"; the kernel's swizzled scale store).
+ *   block_size   : 16 or 32 elements per block scale (RMSQ_ERR_VALUE else);
+ *                  hidden must be a multiple of it.
+ *   scale_format : RMSQ_SF_E4M3 -- scale = min(gs * max|y_block| / 6, 448)
+ *                  rounded to E4M3FN, elements quantized as y * gs / decoded
+ *                  scale (the NVFP4 pairing is block 16);
+ *                  RMSQ_SF_UE8M0 -- code = exponent of the smallest power of
+ *                  two >= max|y_block| / 6, plus 127, clamped to [0, 255];
+ *                  elements quantized as y * 2^(127 - code), and as zero for
+ *                  code 0.  global_scale is not read (the MXFP4 pairing is
+ *                  block 32).
+ *   scale_layout : RMSQ_SF_ROW_MAJOR -- block_scales is [rows, hidden/block];
+ *                  RMSQ_SF_SWIZZLED -- 128 x 4 tiles for FP4 GEMM operands:
+ *                  the scale of (row, j) is at byte
+ *                    (row/128) * K * 512 + (j/4) * 512 + (row%32) * 16
+ *                    + ((row%128)/32) * 4 + j%4,   K = ceil((hidden/block)/4),
+ *                  in a buffer of rmsq_fp4_scale_bytes() bytes; bytes of the
+ *                  tiles' padding rows and columns are not written.
+ *   Other arguments, the code layout and the errors are as rmsnorm_fp4;
+ *   RMSQ_ERR_DTYPE for an unknown scale_format or scale_layout.
+ * rmsnorm_fp4(...) == rmsnorm_fp4quant(..., 16, RMSQ_SF_E4M3,
+ * RMSQ_SF_ROW_MAJOR, ...).
+ */
+int rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype,
+                     const void* x, const void* gamma,
+                     float eps, float weight_offset, const float* global_scale,
+                     int block_size, int scale_format, int scale_layout,
+                     void* out, void* block_scales, hipStream_t stream);
+
+/* Bytes of the block_scales buffer rmsnorm_fp4quant writes into for this
+ * shape and layout (rows * hidden / block row-major; whole 128 x 4 tiles
+ * swizzled), or a negative RMSQ_ERR_* for invalid arguments.  No HIP call. */
+int64_t rmsq_fp4_scale_bytes(int64_t rows, int64_t hidden, int block_size, int scale_layout);
+
 /*
  * rmsq_convert -- the device conversions the fused kernels use, applied
  * elementwise (standalone quantizers; also used to check the hardware

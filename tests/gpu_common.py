@@ -10,7 +10,7 @@ import torch
 import fp4_activation_quantization_amd as rq
 import oracle
 import workloads
-from parity import compare_fp4, compare_fp8
+from parity import compare_fp4, compare_fp8, unswizzle_scales
 
 DEV = "cuda:0"
 
@@ -81,14 +81,35 @@ def check_fp8(w, inp, *, rows_idx=None, label="", **kw):
     return rep
 
 
+CANARY = 0xA5  # fill of swizzled scale buffers: padding bytes must keep it
+
+
 def run_fp4(w, inp, gs, *, rows_idx=None, weight_offset=None, stream=None):
+    """Run the workload's FP4 variant; returns (packed, row-major block scales)
+    for the selected rows.  A swizzled buffer is checked to leave its padding
+    untouched and is returned un-swizzled."""
     x, g = to_dev(inp["x"]), to_dev(inp["gamma"])
     gst = torch.tensor([gs], dtype=torch.float32, device=DEV) if gs is not None else None
-    packed, bs = rq.rmsnorm_fp4(x, g, eps=w.eps, weight_offset=w.weight_offset if weight_offset is None else weight_offset,
-                                global_scale=gst, stream=stream)
+    off = w.weight_offset if weight_offset is None else weight_offset
+    rows, hidden = x.shape
+    if w.fp4_block == 16 and w.fp4_scale == "e4m3" and not w.fp4_swizzled:
+        packed, bs = rq.rmsnorm_fp4(x, g, eps=w.eps, weight_offset=off, global_scale=gst, stream=stream)
+    else:
+        bs = None
+        if w.fp4_swizzled:
+            bs = torch.full((rq.fp4_scale_bytes(rows, hidden, w.fp4_block, True),), CANARY, dtype=torch.uint8,
+                            device=DEV)
+        packed, bs = rq.rmsnorm_fp4quant(x, g, eps=w.eps, weight_offset=off, global_scale=gst,
+                                         block_size=w.fp4_block, scale_format=w.fp4_scale, swizzled=w.fp4_swizzled,
+                                         block_scales=bs, stream=stream)
     torch.cuda.synchronize()
-    sel = slice(None) if rows_idx is None else torch.as_tensor(rows_idx, device=DEV)
-    return packed[sel].cpu().numpy(), bs[sel].cpu().numpy()
+    bs = bs.cpu().numpy()
+    if w.fp4_swizzled:
+        raw = bs
+        bs, pad = unswizzle_scales(raw, rows, hidden // w.fp4_block)
+        assert np.all(raw[pad] == CANARY), "swizzled padding bytes were written"
+    sel = slice(None) if rows_idx is None else np.asarray(rows_idx)
+    return packed.cpu().numpy()[sel], bs[sel]
 
 
 def check_fp4(w, inp, gs, *, rows_idx=None, label="", weight_offset=None):
@@ -100,9 +121,9 @@ def check_fp4(w, inp, gs, *, rows_idx=None, label="", weight_offset=None):
     off = w.weight_offset if weight_offset is None else weight_offset
     kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=off)
     gsv = 1.0 if gs is None else gs
-    ref = oracle.rmsnorm_fp4(x, g, global_scale=gsv, **kw)
+    ref = oracle.rmsnorm_fp4(x, g, global_scale=gsv, block_size=w.fp4_block, scale_format=w.fp4_scale, **kw)
     y = oracle.rmsnorm_y(x, g, **kw)["y"]
-    rep = compare_fp4(p, bs, ref, y, global_scale=gsv)
+    rep = compare_fp4(p, bs, ref, y, global_scale=gsv, block_size=w.fp4_block, scale_format=w.fp4_scale)
     say(f"  parity {label or w.name}: {rep}")
     return rep
 

@@ -157,8 +157,24 @@ def unpack_e2m1(packed):
     return np.stack([p & 0xF, p >> 4], axis=-1).reshape(*p.shape[:-1], p.shape[-1] * 2)
 
 
-def compare_fp4(gpu_packed, gpu_block_scales, ref, y, *, global_scale):
-    """ref: oracle.rmsnorm_fp4 result (with q and sf); y: oracle float64 normalized values."""
+def near_power_of_two(v, rel=REL):
+    """v (> 0) within rel (relative) of a power of two: the decision points of
+    a UE8M0 scale (the smallest power of two >= v)."""
+    v = np.asarray(v, np.float64)
+    with np.errstate(divide="ignore"):
+        p = np.exp2(np.round(np.log2(np.where(v > 0, v, 1.0))))
+    return (v > 0) & (np.abs(v - p) <= rel * p)
+
+
+def compare_fp4(gpu_packed, gpu_block_scales, ref, y, *, global_scale, block_size=16, scale_format="e4m3"):
+    """ref: oracle.rmsnorm_fp4 result (with q and sf) for the same block size and
+    scale format; y: oracle float64 normalized values; gpu_block_scales
+    row-major [rows, hidden/block_size].
+
+    A block-scale code may differ by one where the oracle's unrounded scale
+    is within 1e-6 of the format's decision point: an E4M3 rounding midpoint,
+    or a power of two for UE8M0 (the scale is the smallest power of two >=
+    amax/6).  That block's codes are then re-derived from the GPU's scale."""
     rep = Report()
     gb = np.asarray(gpu_block_scales, np.uint8)
     ob = ref["block_scales"]
@@ -169,17 +185,33 @@ def compare_fp4(gpu_packed, gpu_block_scales, ref, y, *, global_scale):
     if d.any():
         r, b = np.nonzero(d)
         step1 = np.abs(gb[r, b].astype(np.int64) - ob[r, b].astype(np.int64)) == 1
-        near = near_midpoint("e4m3fn", ref["sf"][r, b].astype(np.float32).astype(np.float64))
+        sf32 = ref["sf"][r, b].astype(np.float32).astype(np.float64)
+        near = near_power_of_two(sf32) if scale_format == "ue8m0" else near_midpoint("e4m3fn", sf32)
         if not np.all(step1 & near):
             k = np.nonzero(~(step1 & near))[0][:4]
             raise AssertionError(f"block scales differ away from a boundary at {list(zip(r[k], b[k]))}: "
                                  f"gpu {gb[r[k], b[k]]} oracle {ob[r[k], b[k]]} sf {ref['sf'][r[k], b[k]]}")
         gs = float(np.float32(global_scale))
         for rr, bb in zip(r, b):
-            dg = oracle.decode("e4m3fn", [gb[rr, bb]])[0]
-            sl = slice(16 * bb, 16 * bb + 16)
-            q[rr, sl] = y[rr, sl] * gs / dg if dg > 0 else y[rr, sl] * 0.0
+            sl = slice(block_size * bb, block_size * (bb + 1))
+            if scale_format == "ue8m0":
+                sg = int(gb[rr, bb])
+                q[rr, sl] = y[rr, sl] * (np.ldexp(1.0, 127 - sg) if sg else 0.0)
+            else:
+                dg = oracle.decode("e4m3fn", [gb[rr, bb]])[0]
+                q[rr, sl] = y[rr, sl] * gs / dg if dg > 0 else y[rr, sl] * 0.0
             expect[rr, sl] = oracle.encode("e2m1", q[rr, sl].astype(np.float32).astype(np.float64))
     _check_codes("e2m1", unpack_e2m1(gpu_packed), expect, q, rep, "codes")
     rep["ok"] = True
     return rep
+
+
+def unswizzle_scales(buf, rows, sf_per_row):
+    """Row-major [rows, sf_per_row] view of a swizzled scale buffer (the
+    oracle's offsets), and a mask of the buffer bytes that hold no scale."""
+    buf = np.asarray(buf, np.uint8)
+    r, c = np.meshgrid(np.arange(rows), np.arange(sf_per_row), indexing="ij")
+    off = oracle.swizzled_offset(r, c, sf_per_row)
+    pad = np.ones(buf.size, bool)
+    pad[off.ravel()] = False
+    return buf[off], pad

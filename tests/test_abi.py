@@ -35,13 +35,14 @@ def no_launch_possible():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(", text,
-                                 flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int64_t|int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsq_convert", "rmsq_stream_probe",
+    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "rmsq_fp4_scale_bytes",
+              "rmsq_convert", "rmsq_stream_probe",
               "rmsq_set_tuning", "rmsq_query_shape", "rmsq_status_string", "rmsq_abi_version",
               "rmsq_last_hip_error"):
         assert f in fns, f
@@ -186,6 +187,48 @@ def test_fp4_errors():
     assert fp4(gs=ctypes.c_void_p(BASE + 9 * MB + 2)) == ALIGN
     assert fp4(bs=ctypes.c_void_p(BASE + 2 * MB + 16)) == ALIAS
     assert fp4(gs=ctypes.c_void_p(BASE + 3 * MB)) == ALIAS
+
+
+def fp4q(rows=4, hidden=4096, block=16, sfmt=None, layout=None, gs=None, out=None, bs=None):
+    sfmt = rq.SF_E4M3 if sfmt is None else sfmt
+    layout = rq.SF_ROW_MAJOR if layout is None else layout
+    out = P(2) if out is None else out
+    bs = P(3) if bs is None else bs
+    return rq.lib().rmsnorm_fp4quant(rows, hidden, rq.BF16, P(0), P(1), 1e-6, 0.0, gs, block, sfmt, layout, out, bs,
+                                     None)
+
+
+def test_fp4quant_errors():
+    assert fp4q(block=8) == VALUE
+    assert fp4q(block=64) == VALUE
+    assert fp4q(sfmt=2) == DTYPE
+    assert fp4q(layout=2) == DTYPE
+    assert fp4q(hidden=48, block=32) == SHAPE
+    for block in (16, 32):
+        for sfmt in (rq.SF_E4M3, rq.SF_UE8M0):
+            for layout in (rq.SF_ROW_MAJOR, rq.SF_SWIZZLED):
+                assert fp4q(block=block, sfmt=sfmt, layout=layout) == UNSUP
+    # UE8M0 scales never read the global scale: a misaligned one is not an error
+    bad_gs = ctypes.c_void_p(BASE + 9 * MB + 2)
+    assert fp4q(sfmt=rq.SF_E4M3, gs=bad_gs) == ALIGN
+    assert fp4q(sfmt=rq.SF_UE8M0, gs=bad_gs) == UNSUP
+    # the swizzled buffer covers whole 128 x 4 tiles: 32768 bytes here, against
+    # 1024 row-major, so a buffer just below the codes overlaps only when swizzled
+    below = ctypes.c_void_p(BASE + 2 * MB - 2048)
+    assert fp4q(bs=below) == UNSUP
+    assert fp4q(bs=below, layout=rq.SF_SWIZZLED) == ALIAS
+
+
+def test_fp4_scale_bytes():
+    L = rq.lib()
+    assert L.rmsq_fp4_scale_bytes(130, 80, 16, rq.SF_ROW_MAJOR) == 650
+    assert L.rmsq_fp4_scale_bytes(130, 80, 16, rq.SF_SWIZZLED) == 2048   # 2 m-tiles x 2 k-tiles x 512
+    assert L.rmsq_fp4_scale_bytes(16384, 7168, 32, rq.SF_SWIZZLED) == 128 * 56 * 512
+    assert L.rmsq_fp4_scale_bytes(0, 7168, 16, rq.SF_SWIZZLED) == 0
+    assert L.rmsq_fp4_scale_bytes(4, 64, 8, rq.SF_ROW_MAJOR) == VALUE
+    assert L.rmsq_fp4_scale_bytes(4, 64, 16, 3) == DTYPE
+    assert L.rmsq_fp4_scale_bytes(4, 24, 16, rq.SF_ROW_MAJOR) == SHAPE
+    assert rq.fp4_scale_bytes(256, 4096, 32, swizzled=True) == 2 * 32 * 512
 
 
 def test_convert_errors():

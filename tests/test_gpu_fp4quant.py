@@ -1,0 +1,125 @@
+"""GPU parity of rmsnorm_fp4quant (through the C ABI) against the oracle for
+every block size (16, 32), scale format (E4M3, UE8M0) and scale layout
+(row-major, swizzled 128 x 4 tiles), on bf16 and fp16 inputs:
+
+* row counts that leave a ragged last 128-row tile and hidden sizes whose
+  scale columns leave a ragged last 4-column tile (swizzled padding must keep
+  its bytes);
+* the hand-worked rows of tests/golden/hand_rows.json (fp4_block_rows),
+  byte for byte;
+* forced launch shapes (1-16 waves per row, 1-4 vectors per lane), so the
+  4-lane block reduction of 32-element blocks runs in every mapping;
+* the 16-element E4M3 row-major case equals rmsnorm_fp4 bit for bit.
+The comparison rule is in tests/parity.py.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_activation_quantization_amd as rq
+import oracle
+import workloads
+from gpu_common import DEV, check_fp4, say
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = json.load(open(os.path.join(HERE, "golden", "hand_rows.json")))
+TD = workloads.TORCH_DTYPES
+
+
+@pytest.fixture(autouse=True)
+def default_shape():
+    rq.set_tuning(0, 0, 0)
+    yield
+    rq.set_tuning(0, 0, 0)
+
+
+def _inputs(rows, hidden, dt, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, hidden))
+    heavy = rng.choice(hidden, size=max(1, hidden // 100), replace=False)
+    x[:, heavy] = rng.standard_t(3.0, size=(rows, heavy.size))
+    x *= np.exp2(rng.integers(-8, 8, (rows, 1)))  # rows of different magnitude
+    return {"x": torch.from_numpy(x).to(TD[dt]), "residual": None,
+            "gamma": torch.from_numpy(rng.uniform(0.8, 1.2, hidden)).to(TD[dt])}
+
+
+def _wl(rows, hidden, dt, block, fmt, swz, offset=0.0):
+    return workloads.Workload("fp4quant", "rmsnorm_fp4", rows, hidden, dt, 98, eps=1e-6, weight_offset=offset,
+                              fp4_block=block, fp4_scale=fmt, fp4_swizzled=swz)
+
+
+def _gs(inp, w):
+    amax = oracle.absmax(workloads.bits(inp["x"]), workloads.bits(inp["gamma"]), in_dtype=w.in_dtype, eps=w.eps,
+                         weight_offset=w.weight_offset)
+    return float(np.float32(448 * 6 / amax))
+
+
+@pytest.mark.parametrize("swz", [False, True], ids=["rowmajor", "swizzled"])
+@pytest.mark.parametrize("fmt", ["e4m3", "ue8m0"])
+@pytest.mark.parametrize("block", [16, 32])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_every_variant(dt, block, fmt, swz):
+    for rows, hidden in ((300, 160), (131, 7168), (257, 2080)):
+        w = _wl(rows, hidden, dt, block, fmt, swz)
+        inp = _inputs(rows, hidden, dt, seed=rows + hidden + block)
+        say(f"[fp4quant] {dt} block={block} {fmt} swizzled={swz} rows={rows} hidden={hidden}")
+        check_fp4(w, inp, _gs(inp, w), label=f"{dt} {block} {fmt} swz={swz} {rows}x{hidden}")
+
+
+@pytest.mark.parametrize("row", GOLDEN["fp4_block_rows"], ids=lambda r: r["id"])
+def test_hand_rows_byte_exact(row):
+    dt = row["in_dtype"]
+    if dt == "f32":
+        dt = "bf16"  # every value of these rows is exact in bf16 (powers of two times 1, 3)
+    n = len(row["x"])
+    x = torch.tensor([row["x"]], dtype=torch.float64).to(TD[dt]).to(DEV)
+    g = torch.ones(n, dtype=TD[dt], device=DEV)
+    gst = torch.tensor([row["global_scale"]], dtype=torch.float32, device=DEV)
+    say(f"[fp4quant hand row] {row['id']}")
+    for swz in (False, True):
+        packed, bs = rq.rmsnorm_fp4quant(x, g, eps=row["eps"], weight_offset=row["weight_offset"], global_scale=gst,
+                                         block_size=row["block_size"], scale_format=row["scale_format"],
+                                         swizzled=swz)
+        torch.cuda.synchronize()
+        got_p = [f"0x{v:02X}" for v in packed.cpu().numpy()[0]]
+        b = bs.cpu().numpy()
+        if swz:
+            b = b[oracle.swizzled_offset(0, np.arange(n // row["block_size"]), n // row["block_size"])]
+        got_s = [f"0x{v:02X}" for v in np.ravel(b)[: n // row["block_size"]]]
+        assert got_s == row["expect_block_scales"]
+        assert got_p == row["expect_packed"]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "ue8m0"])
+def test_forced_launch_shapes_block32(fmt):
+    hidden = 4096  # 512 vectors
+    inp = _inputs(70, hidden, "bf16", seed=3)
+    w = _wl(70, hidden, "bf16", 32, fmt, False)
+    gs = _gs(inp, w)
+    for waves, vpt in ((1, 4), (2, 4), (2, 2), (4, 2), (8, 1), (3, 4), (16, 1), (12, 1), (5, 2)):
+        if waves * 64 * vpt * 8 < hidden:
+            continue
+        rq.set_tuning(waves, vpt, 7)
+        say(f"[fp4quant shape] {fmt} waves={waves} vpt={vpt}")
+        check_fp4(w, inp, gs, label=f"block32 {fmt} {waves}x{vpt}")
+    rq.set_tuning(0, 0, 0)
+
+
+def test_weight_offset_and_f16_block32():
+    inp = _inputs(90, 7168, "f16", seed=11)
+    w = _wl(90, 7168, "f16", 32, "ue8m0", True, offset=0.25)
+    check_fp4(w, inp, 1.0, label="f16 block32 ue8m0 swizzled offset 0.25")
+
+
+def test_default_variant_equals_rmsnorm_fp4():
+    inp = _inputs(200, 7168, "bf16", seed=12)
+    x, g = inp["x"].to(DEV), inp["gamma"].to(DEV)
+    gst = torch.tensor([37.5], dtype=torch.float32, device=DEV)
+    p1, s1 = rq.rmsnorm_fp4(x, g, global_scale=gst)
+    p2, s2 = rq.rmsnorm_fp4quant(x, g, global_scale=gst, block_size=16, scale_format="e4m3")
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(s1, s2)

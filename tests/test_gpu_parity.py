@@ -30,7 +30,8 @@ FP8_NAMES = [n for n, w in W.items() if w.op != "rmsnorm_fp4"]
 SMALL_ROWS = {"rmsnorm_fp8_bf16_16x512": 16, "residual_rmsnorm_fp8_bf16_8192x4096": 301,
               "rmsnorm_fp8_f16_decode_1x8192": 1, "rmsnorm_fp8_f16_decode_8x8192": 8,
               "rmsnorm_fp8_f16_decode_64x8192": 64, "residual_rmsnorm_fp8_bf16_32768x8192": 203,
-              "residual_rmsnorm_fp8_f32_32768x8192": 203, "rmsnorm_fp4_bf16_16384x7168": 157}
+              "residual_rmsnorm_fp8_f32_32768x8192": 203, "rmsnorm_fp4_bf16_16384x7168": 157,
+              "rmsnorm_mxfp4_bf16_16384x7168": 157, "rmsnorm_fp4_swizzled_bf16_16384x7168": 300}
 
 
 def golden_gs():

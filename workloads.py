@@ -12,7 +12,8 @@ these kernels see in LLM inference: a small smoke shape, a Llama-3-8B hidden
 size with a few hot outlier channels, single-token decode batches with a
 Gemma-style (1 + gamma) weight, a 70B-class prefill batch with heavy-tailed
 (Laplace) activations and a few hot rows, and a 7168-wide FP4 tensor whose
-1% heavy channels follow Student-t(3).
+1% heavy channels follow Student-t(3) (quantized three ways: 16-element E4M3
+scales row-major or swizzled, and 32-element UE8M0 scales).
 """
 from __future__ import annotations
 
@@ -49,6 +50,9 @@ class Workload:
     outlier_row_frac: float = 0.0  # fraction of rows scaled by outlier_scale
     heavy_channel_frac: float = 0.0  # fraction of columns drawn from Student-t(3)
     widen_from: str | None = None    # f32 workload holding another workload's bf16 values
+    fp4_block: int = 16              # FP4 only: elements per block scale (16 or 32)
+    fp4_scale: str = "e4m3"          # FP4 only: "e4m3" or "ue8m0" block scales
+    fp4_swizzled: bool = False       # FP4 only: 128 x 4-tile scale layout
 
     @property
     def residual(self) -> bool:
@@ -80,6 +84,12 @@ WORKLOADS = {w.name: w for w in [
              outlier_scale=100.0, widen_from="bf16"),
     Workload("rmsnorm_fp4_bf16_16384x7168", "rmsnorm_fp4", 16384, 7168, "bf16", 4, eps=1e-6,
              gamma_lo=0.8, gamma_hi=1.2, heavy_channel_frac=0.01),
+    # the same tensor (same workload id, so the same draws) quantized as MXFP4
+    # (32-element blocks, UE8M0 scales), and as NVFP4 with swizzled scales
+    Workload("rmsnorm_mxfp4_bf16_16384x7168", "rmsnorm_fp4", 16384, 7168, "bf16", 4, eps=1e-6,
+             gamma_lo=0.8, gamma_hi=1.2, heavy_channel_frac=0.01, fp4_block=32, fp4_scale="ue8m0"),
+    Workload("rmsnorm_fp4_swizzled_bf16_16384x7168", "rmsnorm_fp4", 16384, 7168, "bf16", 4, eps=1e-6,
+             gamma_lo=0.8, gamma_hi=1.2, heavy_channel_frac=0.01, fp4_swizzled=True),
 ]}
 
 # The workload the headline throughput is quoted on.
