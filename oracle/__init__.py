@@ -53,7 +53,7 @@ def lib() -> ctypes.CDLL:
     L.oracle_rmsnorm_fp8.restype = I
     L.oracle_rmsnorm_fp4.argtypes = [I64, I64, I, P, P, D, D, D, P, P, P, P]
     L.oracle_rmsnorm_fp4.restype = I
-    L.oracle_rmsnorm_fp4q.argtypes = [I64, I64, I, P, P, D, D, D, I, I, P, P, P, P]
+    L.oracle_rmsnorm_fp4q.argtypes = [I64, I64, I, P, P, P, P, D, D, D, I, I, P, P, P, P]
     L.oracle_rmsnorm_fp4q.restype = I
     L.oracle_rmsnorm_y.argtypes = [I64, I64, I, P, P, P, P, D, D, P, P]
     L.oracle_rmsnorm_y.restype = I
@@ -136,7 +136,7 @@ def rmsnorm_fp8(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, sc
 
 def rmsnorm_fp4(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, global_scale: float,
                 threads: int | None = None, want_q: bool = True, block_size: int = 16,
-                scale_format: str = "e4m3") -> dict:
+                scale_format: str = "e4m3", residual=None) -> dict:
     """Reference FP4 (E2M1) path with one scale per block of block_size (16 or
     32) elements: E4M3 scales (gs * amax / 6 clamped to 448) or UE8M0 scales
     (power of two >= amax / 6, no global scale).
@@ -145,6 +145,8 @@ def rmsnorm_fp4(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, gl
     block_scales [rows, hidden/block_size] (scale codes, row-major), q
     [rows, hidden] float64 and sf [rows, hidden/block_size] float64 (the
     unrounded block scale: after the clamp for E4M3, amax / 6 for UE8M0).
+    With a residual, the row is s = round(x + residual) (also returned as
+    residual_out bits) and the quantizer runs on it.
     """
     L = lib()
     x = _bits_array(x, in_dtype)
@@ -161,17 +163,21 @@ def rmsnorm_fp4(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, gl
     sf = np.empty((rows, nblk), np.float64)
     e, o, gs = (float(np.float32(v)) for v in (eps, weight_offset, global_scale))
     sfmt = SCALE_FORMATS[scale_format]
+    res = _bits_array(residual, in_dtype) if residual is not None else None
+    rout = np.empty_like(x) if res is not None else None
 
     def work(r0, r1):
         n = r1 - r0
         if n <= 0:
             return 0
-        return L.oracle_rmsnorm_fp4q(n, hidden, DTYPES[in_dtype], _ptr(x[r0:r1]), _ptr(g), e, o, gs, block_size,
-                                     sfmt, _ptr(packed[r0:r1]), _ptr(bs[r0:r1]),
+        return L.oracle_rmsnorm_fp4q(n, hidden, DTYPES[in_dtype], _ptr(x[r0:r1]),
+                                     _ptr(res[r0:r1]) if res is not None else None,
+                                     _ptr(rout[r0:r1]) if rout is not None else None, _ptr(g), e, o, gs,
+                                     block_size, sfmt, _ptr(packed[r0:r1]), _ptr(bs[r0:r1]),
                                      _ptr(q[r0:r1]) if q is not None else None, _ptr(sf[r0:r1]))
 
     _run(work, rows, threads)
-    return {"packed": packed, "block_scales": bs, "q": q, "sf": sf}
+    return {"packed": packed, "block_scales": bs, "q": q, "sf": sf, "residual_out": rout}
 
 
 # ---- swizzled scale layout ---------------------------------------------------

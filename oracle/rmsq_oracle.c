@@ -318,6 +318,10 @@ int oracle_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dt,
  *   sfmt ORQ_SF_UE8M0: scale code = UE8M0(amax / 6), element factor
  *                      2^(127 - code) (0 for code 0); gs is not used.
  * Elements are then E2M1 codes of y * factor (saturating RNE).
+ *   x, residual, residual_out: [rows, hidden] in in_dt; with a residual the
+ *   row is s = round_to_in_dt(x + r), written to residual_out, as in the FP8
+ *   path ([P2] residual_output; the FP4 page has no residual, so this pairs
+ *   its quantizer with [P2]'s pre-norm sum).  residual may be NULL.
  *   out: [rows, hidden/2] bytes, element 2k in the low nibble of byte k.
  *   block_scales: [rows, hidden/block] scale codes, row-major.
  *   global_scale: the fp32 value, widened.
@@ -326,7 +330,8 @@ int oracle_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dt,
  *   (after the clamp to 448 for E4M3; amax / 6 for UE8M0).
  * Returns 0, -1 on allocation failure, -2 on a bad hidden / block / format. */
 int oracle_rmsnorm_fp4q(int64_t rows, int64_t hidden, int in_dt,
-                        const void* x, const void* gamma, double eps, double offset,
+                        const void* x, const void* residual, void* residual_out,
+                        const void* gamma, double eps, double offset,
                         double global_scale, int block, int sfmt, uint8_t* out, uint8_t* block_scales,
                         double* q_out, double* sf_out) {
     minifloat e4m3 = fmt_of(ORQ_E4M3FN), e2m1 = fmt_of(ORQ_E2M1);
@@ -342,7 +347,9 @@ int oracle_rmsnorm_fp4q(int64_t rows, int64_t hidden, int in_dt,
     if (!s || !y || !c) { free(s); free(y); free(c); return -1; }
     for (int64_t r = 0; r < rows; r++) {
         const char* xr = (const char*)x + (size_t)r * hidden * esz;
-        norm_row(hidden, in_dt, xr, NULL, NULL, gamma, eps, offset, s, y);
+        const char* rr = residual ? (const char*)residual + (size_t)r * hidden * esz : NULL;
+        char* ro = residual ? (char*)residual_out + (size_t)r * hidden * esz : NULL;
+        norm_row(hidden, in_dt, xr, rr, ro, gamma, eps, offset, s, y);
         for (int64_t b = 0; b < nblk; b++) {
             double amax = 0.0;
             for (int k = 0; k < block; k++)
@@ -383,8 +390,8 @@ int oracle_rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dt,
                        const void* x, const void* gamma, double eps, double offset,
                        double global_scale, uint8_t* out, uint8_t* block_scales,
                        double* q_out, double* sf_out) {
-    return oracle_rmsnorm_fp4q(rows, hidden, in_dt, x, gamma, eps, offset, global_scale, 16, ORQ_SF_E4M3,
-                               out, block_scales, q_out, sf_out);
+    return oracle_rmsnorm_fp4q(rows, hidden, in_dt, x, NULL, NULL, gamma, eps, offset, global_scale, 16,
+                               ORQ_SF_E4M3, out, block_scales, q_out, sf_out);
 }
 
 /* The normalized values y = s * rstd * (gamma + offset) as float64

@@ -181,3 +181,55 @@ def test_swizzle_is_the_tile_view_and_a_bijection(rows, nsf):
     r, c = np.meshgrid(np.arange(rows), np.arange(nsf), indexing="ij")
     offs = oracle.swizzled_offset(r, c, nsf).reshape(-1)
     assert len(np.unique(offs)) == offs.size and offs.min() >= 0 and offs.max() < got.size
+
+
+# ---- residual input and fp32 input (the FP4 quantizer on the residual page's
+# pre-norm sum; the quantizer itself is unchanged) --------------------------------
+
+def test_fp4_residual_hand_row():
+    """x + r reproduces the mx32 hand row exactly: r = 0.5 everywhere and
+    x = row - 0.5 (all exact in bf16), so residual_out holds the row's bf16
+    bits and the codes equal the hand row's."""
+    base = next(r for r in GOLDEN["fp4_block_rows"] if r["id"] == "mx32_ue8m0")
+    n = len(base["x"])
+    x = [v - 0.5 for v in base["x"]]
+    r = oracle.rmsnorm_fp4(as_bits([x], "bf16"), as_bits([1.0] * n, "bf16"), in_dtype="bf16", eps=0.0,
+                           weight_offset=0.0, global_scale=1.0, block_size=32, scale_format="ue8m0",
+                           residual=as_bits([[0.5] * n], "bf16"))
+    # bf16 bits: 4 = 0x4080, 2 = 0x4000, -2 = 0xC000, 3 = 0x4040, -3 = 0xC040, 1 = 0x3F80, 0 = 0
+    want = [0x4080, 0x4000, 0xC000, 0x4000, 0xC000] + [0] * 27 + [0x4040, 0x4040, 0xC040] + [0x3F80] * 5 + [0] * 24
+    assert [int(v) for v in r["residual_out"][0]] == want
+    assert hexes(r["block_scales"][0]) == base["expect_block_scales"]
+    assert hexes(r["packed"][0]) == base["expect_packed"]
+
+
+@pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0"), (32, "e4m3"), (16, "ue8m0")])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_fp4_residual_is_fp4_of_the_stored_sum(dt, block, fmt):
+    rng = np.random.default_rng(30 + block)
+    rows, h = 12, 512
+    x = as_bits(rng.standard_normal((rows, h)).tolist(), dt)
+    res = as_bits(rng.standard_normal((rows, h)).tolist(), dt)
+    g = as_bits(rng.uniform(0.5, 1.5, h).tolist(), dt)
+    kw = dict(in_dtype=dt, eps=1e-6, weight_offset=0.0, global_scale=250.0, block_size=block, scale_format=fmt)
+    a = oracle.rmsnorm_fp4(x, g, residual=res, **kw)
+    # the stored sum is torch's correctly rounded (fp32 holds the exact sum of two 16-bit values)
+    tx = workloads.from_bits(x, dt).to(torch.float64)
+    tr = workloads.from_bits(res, dt).to(torch.float64)
+    assert np.array_equal(a["residual_out"], workloads.bits((tx + tr).to(TD[dt])))
+    b = oracle.rmsnorm_fp4(a["residual_out"], g, **kw)
+    for k in ("packed", "block_scales"):
+        assert np.array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0")])
+def test_fp4_fp32_input_of_bf16_values_matches_bf16(block, fmt):
+    """Widening bf16 values to fp32 changes no value, so no code."""
+    rng = np.random.default_rng(40 + block)
+    xb = torch.from_numpy(rng.standard_normal((9, 768))).to(torch.bfloat16)
+    gb = torch.from_numpy(rng.uniform(0.5, 1.5, 768)).to(torch.bfloat16)
+    kw = dict(eps=1e-6, weight_offset=0.0, global_scale=77.0, block_size=block, scale_format=fmt)
+    a = oracle.rmsnorm_fp4(workloads.bits(xb), workloads.bits(gb), in_dtype="bf16", **kw)
+    b = oracle.rmsnorm_fp4(workloads.bits(xb.float()), workloads.bits(gb.float()), in_dtype="f32", **kw)
+    for k in ("packed", "block_scales"):
+        assert np.array_equal(a[k], b[k])
