@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 CACHE_DEFEAT_BYTES = 1 << 30
 STREAM_MIN_BYTES = 16 << 20  # smaller workloads are latency-bound: no bandwidth reference
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["rmsq_fp8.hip", "rmsq_fp4.hip", "rmsq_device.h", "rmsq_api.cpp"]
+KERNEL_SOURCES = ["rmsq_fp8.hip", "rmsq_fp4.hip", "rmsq_fp4_kernel.h", "rmsq_device.h", "rmsq_api.cpp"]
 SC_T = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
@@ -58,10 +58,15 @@ def algorithmic_split(w: workloads.Workload) -> tuple[int, int]:
     the global scale once), one write of every output."""
     esz = {"bf16": 2, "f16": 2, "f32": 4}[w.in_dtype]
     n = w.rows * w.hidden
-    if w.op == "rmsnorm_fp4":
+    if w.fp4:
         # the global scale is read only with E4M3 scales; padding of the
         # swizzled scale tiles is not written
-        return n * esz + w.hidden * esz + (4 if w.fp4_scale == "e4m3" else 0), n // 2 + n // w.fp4_block
+        reads = n * esz + w.hidden * esz + (4 if w.fp4_scale == "e4m3" else 0)
+        writes = n // 2 + n // w.fp4_block
+        if w.residual:
+            reads += n * esz   # residual
+            writes += n * esz  # residual_out
+        return reads, writes
     ssz = {"f32": 4, "bf16": 2, "f16": 2}[w.scales_dtype]
     reads, writes = n * esz + w.hidden * esz, n + w.rows * ssz
     if w.residual:
@@ -93,7 +98,7 @@ class Case:
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         for i in range(copies):
             x = x0 if i == 0 else x0.clone()
-            if w.op == "rmsnorm_fp4":
+            if w.fp4:
                 out = torch.empty((w.rows, w.hidden // 2), dtype=torch.uint8, device=dev)
                 bs = torch.empty((rq.fp4_scale_bytes(w.rows, w.hidden, w.fp4_block, w.fp4_swizzled),),
                                  dtype=torch.uint8, device=dev)
@@ -101,9 +106,17 @@ class Case:
                 self.keep += [x, out, bs, gst]
                 sfmt = rq.SF_UE8M0 if w.fp4_scale == "ue8m0" else rq.SF_E4M3
                 layout = rq.SF_SWIZZLED if w.fp4_swizzled else rq.SF_ROW_MAJOR
-                args = (w.rows, w.hidden, dt, P(x), P(g), w.eps, w.weight_offset, P(gst), w.fp4_block, sfmt, layout,
-                        P(out), P(bs), stream)
-                self.calls.append((L.rmsnorm_fp4quant, args))
+                if w.residual:
+                    r = r0 if i == 0 else r0.clone()
+                    ro = torch.empty_like(x)
+                    self.keep += [r, ro]
+                    args = (w.rows, w.hidden, dt, P(x), P(r), P(ro), P(g), w.eps, w.weight_offset, P(gst), w.fp4_block,
+                            sfmt, layout, P(out), P(bs), stream)
+                    self.calls.append((L.residual_rmsnorm_fp4quant, args))
+                else:
+                    args = (w.rows, w.hidden, dt, P(x), P(g), w.eps, w.weight_offset, P(gst), w.fp4_block, sfmt,
+                            layout, P(out), P(bs), stream)
+                    self.calls.append((L.rmsnorm_fp4quant, args))
                 continue
             out = torch.empty((w.rows, w.hidden), dtype=torch.uint8, device=dev)
             sc = torch.empty((w.rows,), dtype=SC_T[w.scales_dtype], device=dev)
@@ -187,9 +200,11 @@ def stream_ceiling(w: workloads.Workload, copies: int, steps: int, warmup: int) 
     return (rb + wb) / per_s / 1e9
 
 
-def fp4_global_scale() -> float:
+def fp4_global_scale(name: str) -> float:
+    """The stored calibration of an FP4 workload (1.0 where its scales do not use one)."""
     p = os.path.join(ROOT, "tests", "golden", "fp4_global_scale.json")
-    return json.load(open(p))["global_scale"]
+    entry = json.load(open(p))["workloads"].get(name)
+    return entry["global_scale"] if entry else 1.0
 
 
 def copies_for(w: workloads.Workload) -> int:
@@ -287,11 +302,11 @@ def main() -> int:
     for name in names:
         w = workloads.WORKLOADS[name]
         k = copies_for(w)
-        case = Case(w, k, fp4_global_scale() if w.op == "rmsnorm_fp4" else None)
+        case = Case(w, k, fp4_global_scale(name) if w.fp4 else None)
         steps = args.steps if name == workloads.HEADLINE else max(10, args.steps // 2)
         res = time_case(case, steps, args.warmup)
         res["buffer_sets"] = k
-        res["launch"] = rq.query_shape(w.rows, w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.op == "rmsnorm_fp4")
+        res["launch"] = rq.query_shape(w.rows, w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.fp4, w.residual)
         results[name] = res
         del case
         torch.cuda.empty_cache()

@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
     L.residual_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4.argtypes = [I64, I64, I, P, P, F, F, P, P, P, P]
     L.rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, F, F, P, I, I, I, P, P, P]
+    L.residual_rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, P, P, F, F, P, I, I, I, P, P, P]
     L.rmsq_fp4_scale_bytes.argtypes = [I64, I64, I, I]
     L.rmsq_fp4_scale_bytes.restype = I64
     L.rmsq_convert.argtypes = [I, P, P, I64, P]
@@ -70,7 +71,8 @@ def lib() -> ctypes.CDLL:
     L.rmsq_query_shape.argtypes = [I64, I64, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)]
     L.rmsq_status_string.argtypes = [I]
     L.rmsq_status_string.restype = ctypes.c_char_p
-    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "rmsq_convert",
+    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant",
+               "residual_rmsnorm_fp4quant", "rmsq_convert",
                "rmsq_stream_probe",
                "rmsq_set_tuning",
                "rmsq_query_shape", "rmsq_abi_version", "rmsq_last_hip_error"):
@@ -203,6 +205,40 @@ def rmsnorm_fp4quant(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, b
     return out, block_scales
 
 
+def residual_rmsnorm_fp4quant(x, residual, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, block_size=16,
+                              scale_format=None, swizzled=False, out=None, block_scales=None, residual_out=None,
+                              stream=None):
+    """residual_out = x + residual (rounded once to x's dtype), then
+    rmsnorm_fp4quant of residual_out (C: residual_rmsnorm_fp4quant).
+    residual_out may be x or residual itself (in-place update).
+    Returns (packed, block_scales, residual_out)."""
+    rows, hidden = _rows_hidden(x)
+    if residual.shape != x.shape or residual.dtype != x.dtype or not residual.is_contiguous():
+        raise ValueError("residual must be contiguous with x's shape and dtype")
+    if scale_format is None:
+        scale_format = "ue8m0" if block_size == 32 else "e4m3"
+    sfmt = {"e4m3": SF_E4M3, "ue8m0": SF_UE8M0}[scale_format]
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    if out is None:
+        out = torch.empty((*x.shape[:-1], hidden // 2), dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        if swizzled:
+            block_scales = torch.empty((fp4_scale_bytes(rows, hidden, block_size, True),), dtype=torch.uint8,
+                                       device=x.device)
+        else:
+            block_scales = torch.empty((*x.shape[:-1], hidden // block_size), dtype=torch.uint8, device=x.device)
+    elif block_scales.numel() * block_scales.element_size() < fp4_scale_bytes(rows, hidden, block_size, swizzled):
+        raise ValueError("block_scales is smaller than fp4_scale_bytes()")
+    if global_scale is not None and (global_scale.dtype != torch.float32 or global_scale.numel() != 1):
+        raise ValueError("global_scale must be a one-element float32 tensor")
+    _check("residual_rmsnorm_fp4quant", lib().residual_rmsnorm_fp4quant(
+        rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), eps, weight_offset,
+        _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR, _ptr(_u8(out)),
+        _ptr(_u8(block_scales)), _stream(x, stream)))
+    return out, block_scales, residual_out
+
+
 def convert(kind: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
     """Elementwise device conversion (C: rmsq_convert); n = src.numel()."""
     _check("rmsq_convert", lib().rmsq_convert(kind, _ptr(src), _ptr(dst), src.numel(), _stream(src, stream)))
@@ -223,8 +259,11 @@ def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, grid_blocks: i
     _check("rmsq_set_tuning", lib().rmsq_set_tuning(waves_per_row, vectors_per_lane, grid_blocks))
 
 
-def query_shape(rows: int, hidden: int, dtype: torch.dtype, fp4: bool = False) -> dict:
+def query_shape(rows: int, hidden: int, dtype: torch.dtype, fp4: bool = False, residual: bool = False) -> dict:
+    """Launch shape of the FP8 (fp4=False) or FP4 path; residual selects
+    residual_rmsnorm_fp4quant's shape (FP8 shapes do not depend on it)."""
     w, v, r = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check("rmsq_query_shape", lib().rmsq_query_shape(rows, hidden, _DT[dtype], int(fp4), ctypes.byref(w),
+    path = (2 if residual else 1) if fp4 else 0
+    _check("rmsq_query_shape", lib().rmsq_query_shape(rows, hidden, _DT[dtype], path, ctypes.byref(w),
                                                       ctypes.byref(v), ctypes.byref(r)))
     return {"waves_per_row": w.value, "vectors_per_lane": v.value, "rows_per_block": r.value}

@@ -93,7 +93,7 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
     }
 
     Shape shape;
-    if (!choose_shape(rows, nvec, false, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    if (!choose_shape(rows, nvec, kPathFp8, &shape)) return RMSQ_ERR_UNSUPPORTED;
     FusedArgs a{};
     a.x = x;
     a.residual = residual;
@@ -126,10 +126,71 @@ int vpt_for(int nvec, int waves) {
     return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
 }
 
+int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
+               void* residual_out, bool resid, const void* gamma, float eps, float weight_offset,
+               const float* global_scale, int block_size, int scale_format, int scale_layout, void* out,
+               void* block_scales, hipStream_t stream) {
+    if (!valid_dtype(in_dtype)) return RMSQ_ERR_DTYPE;
+    if (scale_format != RMSQ_SF_E4M3 && scale_format != RMSQ_SF_UE8M0) return RMSQ_ERR_DTYPE;
+    if (scale_layout != RMSQ_SF_ROW_MAJOR && scale_layout != RMSQ_SF_SWIZZLED) return RMSQ_ERR_DTYPE;
+    if (block_size != 16 && block_size != 32) return RMSQ_ERR_VALUE;
+    const int64_t esz = elem_size(in_dtype);
+    if (rows < 0 || hidden <= 0 || hidden % block_size != 0) return RMSQ_ERR_SHAPE;
+    if (!size_ok(rows, hidden, esz)) return RMSQ_ERR_SHAPE;
+    if (int rc = check_scalars(eps, weight_offset, 1.0f, false)) return rc;
+    const int nvec = (int)(hidden / elems_per_vec(in_dtype));
+    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    if (rows == 0) return RMSQ_OK;
+    if (!x || !gamma || !out || !block_scales) return RMSQ_ERR_NULL;
+    if (resid && (!residual || !residual_out)) return RMSQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(out, 16)) return RMSQ_ERR_ALIGN;
+    if (resid && (!aligned(residual, 16) || !aligned(residual_out, 16))) return RMSQ_ERR_ALIGN;
+    // the global scale is read only for E4M3 scales
+    const float* gsp = scale_format == RMSQ_SF_E4M3 ? global_scale : nullptr;
+    if (gsp && !aligned(gsp, 4)) return RMSQ_ERR_ALIGN;
+    const int64_t tbytes = rows * hidden * esz;
+    const int64_t sbytes = rmsq_fp4_scale_bytes(rows, hidden, block_size, scale_layout);
+    const Span sx(x, tbytes), sg(gamma, hidden * esz), so(out, rows * hidden / 2), ss(block_scales, sbytes);
+    if (overlap(so, ss) || overlap(so, sx) || overlap(so, sg) || overlap(ss, sx) || overlap(ss, sg))
+        return RMSQ_ERR_ALIAS;
+    if (gsp) {
+        const Span sgs(gsp, 4);
+        if (overlap(sgs, so) || overlap(sgs, ss)) return RMSQ_ERR_ALIAS;
+        if (resid && overlap(sgs, Span(residual_out, tbytes))) return RMSQ_ERR_ALIAS;
+    }
+    if (resid) {
+        const Span sr(residual, tbytes), sro(residual_out, tbytes);
+        if (overlap(so, sr) || overlap(ss, sr) || overlap(sro, so) || overlap(sro, ss) || overlap(sro, sg))
+            return RMSQ_ERR_ALIAS;
+        // an in-place residual update at exactly the same address is allowed
+        if (residual_out != x && overlap(sro, sx)) return RMSQ_ERR_ALIAS;
+        if (residual_out != residual && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
+    }
+    Shape shape;
+    if (!choose_shape(rows, nvec, resid ? kPathFp4Residual : kPathFp4, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    FusedArgs a{};
+    a.x = x;
+    a.residual = residual;
+    a.residual_out = residual_out;
+    a.gamma = gamma;
+    a.out = out;
+    a.scales = block_scales;
+    a.global_scale = gsp;
+    a.rows = rows;
+    a.hidden = (int32_t)hidden;
+    a.inv_hidden = 1.0 / (double)hidden;
+    a.nvec = nvec;
+    a.eps = eps;
+    a.weight_offset = weight_offset;
+    a.sf_swizzled = scale_layout == RMSQ_SF_SWIZZLED ? 1 : 0;
+    a.sf_k_tiles = (int32_t)ceil_div(hidden / block_size, 4);
+    const Fp4Format fmt{block_size, scale_format == RMSQ_SF_UE8M0};
+    return launched(launch_fp4(a, in_dtype, resid, fmt, shape, stream));
+}
+
 }  // namespace
 
-bool choose_shape(int64_t rows, int nvec, bool fp4, Shape* s) {
-    (void)fp4;
+bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
     int waves = g_tune_waves.load(std::memory_order_relaxed);
     int vpt = g_tune_vpt.load(std::memory_order_relaxed);
     if (waves == 0 && vpt == 0) {
@@ -141,9 +202,11 @@ bool choose_shape(int64_t rows, int nvec, bool fp4, Shape* s) {
             // SIMDs of a CU get equal work (odd counts measured 20-35% slower
             // on MI355X).  Among those shapes whose lanes hold the row, the one
             // with the fewest idle lanes; ties go to 2 vectors per lane for
-            // FP8 and 4 for FP4 (the faster ones measured).
+            // FP8 and 4 for FP4 (the faster ones measured).  Residual FP4
+            // holds two inputs per row and takes the FP8 order, which keeps
+            // it within its registers.
             const int order_fp8[3] = {2, 4, 1}, order_fp4[3] = {4, 2, 1};
-            const int* order = fp4 ? order_fp4 : order_fp8;
+            const int* order = path == kPathFp4 ? order_fp4 : order_fp8;
             int64_t best_idle = INT64_MAX;
             waves = 0;
             for (int i = 0; i < 3; ++i) {
@@ -221,47 +284,16 @@ int64_t rmsq_fp4_scale_bytes(int64_t rows, int64_t hidden, int block_size, int s
 int rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
                      float weight_offset, const float* global_scale, int block_size, int scale_format,
                      int scale_layout, void* out, void* block_scales, hipStream_t stream) {
-    if (in_dtype != RMSQ_F16 && in_dtype != RMSQ_BF16) return RMSQ_ERR_DTYPE;
-    if (scale_format != RMSQ_SF_E4M3 && scale_format != RMSQ_SF_UE8M0) return RMSQ_ERR_DTYPE;
-    if (scale_layout != RMSQ_SF_ROW_MAJOR && scale_layout != RMSQ_SF_SWIZZLED) return RMSQ_ERR_DTYPE;
-    if (block_size != 16 && block_size != 32) return RMSQ_ERR_VALUE;
-    if (rows < 0 || hidden <= 0 || hidden % block_size != 0) return RMSQ_ERR_SHAPE;
-    if (!size_ok(rows, hidden, 2)) return RMSQ_ERR_SHAPE;
-    if (int rc = check_scalars(eps, weight_offset, 1.0f, false)) return rc;
-    const int nvec = (int)(hidden / 8);
-    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
-    if (rows == 0) return RMSQ_OK;
-    if (!x || !gamma || !out || !block_scales) return RMSQ_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(out, 16)) return RMSQ_ERR_ALIGN;
-    // the global scale is read only for E4M3 scales
-    const float* gsp = scale_format == RMSQ_SF_E4M3 ? global_scale : nullptr;
-    if (gsp && !aligned(gsp, 4)) return RMSQ_ERR_ALIGN;
-    const int64_t sbytes = rmsq_fp4_scale_bytes(rows, hidden, block_size, scale_layout);
-    const Span sx(x, rows * hidden * 2), sg(gamma, hidden * 2), so(out, rows * hidden / 2), ss(block_scales, sbytes);
-    if (overlap(so, ss) || overlap(so, sx) || overlap(so, sg) || overlap(ss, sx) || overlap(ss, sg))
-        return RMSQ_ERR_ALIAS;
-    if (gsp) {
-        const Span sgs(gsp, 4);
-        if (overlap(sgs, so) || overlap(sgs, ss)) return RMSQ_ERR_ALIAS;
-    }
-    Shape shape;
-    if (!choose_shape(rows, nvec, true, &shape)) return RMSQ_ERR_UNSUPPORTED;
-    FusedArgs a{};
-    a.x = x;
-    a.gamma = gamma;
-    a.out = out;
-    a.scales = block_scales;
-    a.global_scale = gsp;
-    a.rows = rows;
-    a.hidden = (int32_t)hidden;
-    a.inv_hidden = 1.0 / (double)hidden;
-    a.nvec = nvec;
-    a.eps = eps;
-    a.weight_offset = weight_offset;
-    a.sf_swizzled = scale_layout == RMSQ_SF_SWIZZLED ? 1 : 0;
-    a.sf_k_tiles = (int32_t)ceil_div(hidden / block_size, 4);
-    const Fp4Format fmt{block_size, scale_format == RMSQ_SF_UE8M0};
-    return launched(launch_fp4(a, in_dtype, fmt, shape, stream));
+    return fp4_common(rows, hidden, in_dtype, x, nullptr, nullptr, false, gamma, eps, weight_offset, global_scale,
+                      block_size, scale_format, scale_layout, out, block_scales, stream);
+}
+
+int residual_rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
+                              void* residual_out, const void* gamma, float eps, float weight_offset,
+                              const float* global_scale, int block_size, int scale_format, int scale_layout,
+                              void* out, void* block_scales, hipStream_t stream) {
+    return fp4_common(rows, hidden, in_dtype, x, residual, residual_out, true, gamma, eps, weight_offset,
+                      global_scale, block_size, scale_format, scale_layout, out, block_scales, stream);
 }
 
 int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
@@ -307,14 +339,15 @@ int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks) {
     return RMSQ_OK;
 }
 
-int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int is_fp4, int* waves_per_row,
+int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path, int* waves_per_row,
                      int* vectors_per_lane, int* rows_per_block) {
     if (!valid_dtype(in_dtype)) return RMSQ_ERR_DTYPE;
     if (hidden <= 0 || hidden % elems_per_vec(in_dtype) != 0) return RMSQ_ERR_SHAPE;
     const int64_t nvec = hidden / elems_per_vec(in_dtype);
     if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
     Shape s;
-    if (!choose_shape(rows, (int)nvec, is_fp4 != 0, &s)) return RMSQ_ERR_UNSUPPORTED;
+    if (path < kPathFp8 || path > kPathFp4Residual) return RMSQ_ERR_VALUE;
+    if (!choose_shape(rows, (int)nvec, path, &s)) return RMSQ_ERR_UNSUPPORTED;
     if (waves_per_row) *waves_per_row = s.waves;
     if (vectors_per_lane) *vectors_per_lane = s.vpt;
     if (rows_per_block) *rows_per_block = s.rpb;

@@ -37,6 +37,9 @@ __device__ __forceinline__ void store_stream(void* base, int64_t i8, const uint2
 __device__ __forceinline__ void store_stream(void* base, int64_t i4, uint32_t v) {
     __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(base) + i4);
 }
+__device__ __forceinline__ void store_stream(void* base, int64_t i2, uint16_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint16_t*>(base) + i2);
+}
 
 // ---- one 16-byte vector of input elements --------------------------------
 template <typename T>
@@ -221,12 +224,29 @@ __device__ __forceinline__ float pair_max_nonneg(float v) {
 }
 
 // max over the lanes 4j .. 4j+3 for non-negative v (the four quarters of a
-// 32-element FP4 block).
+// 32-element FP4 block of 16-bit inputs).
 __device__ __forceinline__ float quad_max_nonneg(float v) {
     int b = __float_as_int(v);
     b = max_bits(b, dpp_i32<DPP_SWAP1>(b));
     b = max_bits(b, dpp_i32<DPP_SWAP2>(b));
     return __int_as_float(b);
+}
+
+// max over the lanes 8j .. 8j+7 for non-negative v (a 32-element FP4 block
+// of fp32 inputs): the two quads' maxima meet through the 8-lane mirror.
+__device__ __forceinline__ float oct_max_nonneg(float v) {
+    int b = __float_as_int(quad_max_nonneg(v));
+    b = max_bits(b, dpp_i32<DPP_HALF_MIRROR>(b));
+    return __int_as_float(b);
+}
+
+// max over the LPB lanes that hold one FP4 block.
+template <int LPB>
+__device__ __forceinline__ float block_max_nonneg(float v) {
+    static_assert(LPB == 2 || LPB == 4 || LPB == 8, "a block spans 2, 4 or 8 lanes");
+    if constexpr (LPB == 2) return pair_max_nonneg(v);
+    else if constexpr (LPB == 4) return quad_max_nonneg(v);
+    else return oct_max_nonneg(v);
 }
 
 // ---- conversions ------------------------------------------------------------
@@ -309,6 +329,14 @@ __device__ __forceinline__ uint32_t e2m1_x8(const float* q) {
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
+    return w;
+}
+
+// Four values -> four nibbles in the low 16 bits (value 2k in the low nibble
+// of byte k); the upper 16 bits are unspecified.
+__device__ __forceinline__ uint32_t e2m1_x4(const float* q) {
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(q[0]), q[0], q[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
     return w;
 }
 

@@ -1,255 +1,18 @@
-// Fused RMSNorm + block-scaled FP4 quantization (E2M1 codes, one scale per
-// block of 16 or 32 contiguous elements), gfx950.
-//
-// Operation: FlashInfer "rmsnorm_fp4quant.py".  E4M3 scales (kernel Phase 3):
-// scale = min(gs * amax / 6, 448) rounded to E4M3, elements quantized as
-// y * gs / decoded_scale.  UE8M0 scales (section "UE8M0 Intrinsics (for
-// MXFP4)"): code = exponent of the smallest power of two >= amax / 6, plus
-// 127, clamped to [0, 255]; elements quantized as y * 2^(127 - code), zero
-// for code 0; no global scale.  E2M1 rounding is RNE with saturation.  Scales
-// are stored row-major or in the page's swizzled 128 x 4 tiles.  The page's
-// kernel reads the row twice (an async copy for the sum of squares, then
-// again from global memory for quantization) and multiplies x * w in 16-bit;
-// here the row is read once into VGPRs and every product is fp32.
-//
-// Work mapping: as the FP8 kernel (`waves` wavefronts per row, lane l owns
-// the 16-byte vectors l, l+T, ...; EXACT when the lanes hold the row
-// exactly).  A vector holds 8 elements, so a block spans LPB = BLOCK / 8
-// adjacent lanes; they combine their partial amax through DPP lane swaps
-// (one for 16, two for 32 elements), all compute the block scale, the first
-// lane stores the scale byte and each lane stores its own 4 bytes of codes.
-// The grid strides over rows, so gamma + weight_offset is unpacked into
-// registers once per block, and the row loop is software-pipelined.
-#include <algorithm>
-
-#include "rmsq_device.h"
-#include "rmsq_internal.h"
+// FP4 launch dispatch by input type, and the bf16 instantiation of the FP4
+// kernel (rmsq_fp4_kernel.h; fp16 and fp32 are instantiated in
+// rmsq_fp4_f16.hip and rmsq_fp4_f32.hip).
+#include "rmsq_fp4_kernel.h"
 
 namespace rmsq {
 
-template <typename InT, int VPT, bool EXACT, bool ONE_ROW, int DEPTH, int BLOCK, bool UE8M0>
-__global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
-    using V = Vec<InT>;
-    constexpr int EPV = 8;
-    static_assert(V::EPV == EPV, "FP4 path takes 16-bit inputs");
-    static_assert(BLOCK == 16 || BLOCK == 32, "16- or 32-element blocks");
-    constexpr int LPB = BLOCK / EPV;  // lanes (vectors) per block: 2 or 4
+template hipError_t launch_fp4_typed<BF16>(const FusedArgs&, bool, Fp4Format, Shape, hipStream_t);
+extern template hipError_t launch_fp4_typed<F16>(const FusedArgs&, bool, Fp4Format, Shape, hipStream_t);
+extern template hipError_t launch_fp4_typed<float>(const FusedArgs&, bool, Fp4Format, Shape, hipStream_t);
 
-    const int waves = a.waves;
-    const int T = waves * 64;
-    // ONE_ROW: the block is one row group, so the row index is uniform
-    const int rpb = ONE_ROW ? 1 : blockDim.x / T;
-    const int tid = threadIdx.x;
-    const int slot = ONE_ROW ? 0 : tid / T;
-    const int lt = tid - slot * T;
-    const int red = slot * waves + (lt >> 6);
-    const int nvec = a.nvec;  // a multiple of LPB: hidden is a multiple of BLOCK
-    const int64_t row_bytes = (int64_t)a.hidden * 2;
-    const int nblk = a.hidden / BLOCK;
-    const bool swz = a.sf_swizzled != 0;
-    const int64_t m_tile_bytes = (int64_t)a.sf_k_tiles * 512;
-    auto live = [&](int k) { return EXACT || lt + k * T < nvec; };
-
-    __shared__ double red_sum[2][16];
-
-    // E4M3 scales only (the API passes no global scale with UE8M0 scales)
-    const double gs = a.global_scale ? (double)*a.global_scale : 1.0;
-
-    float g[VPT][EPV];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        if (live(k)) {
-            V::unpack(reinterpret_cast<const uint4*>(a.gamma)[lt + k * T], g[k]);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) g[k][e] += a.weight_offset;
-        } else {
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) g[k][e] = 0.0f;
-        }
-    }
-
-    // Software pipeline over the rows this block owns: the loads of the next
-    // DEPTH - 1 rows are in flight while the current row is reduced and
-    // quantized.  DEPTH register buffers rotate (the loop body is unrolled
-    // DEPTH times, so buffer indices are compile-time and no row is ever
-    // copied between registers).  A lane's vectors past the end of the row are
-    // the same on every row: they are zeroed once and never loaded.
-    const int64_t stride = (int64_t)gridDim.x * rpb;
-    uint4 xb[DEPTH][VPT];
-#pragma unroll
-    for (int b = 0; b < DEPTH; ++b)
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) xb[b][k] = make_uint4(0, 0, 0, 0);
-    // Swizzled scales: a 128-byte line of the scale buffer holds the scales
-    // of 32 rows (same row / 128, same (row % 32) / 8).  Blocks go to the 8
-    // XCDs round robin and each XCD has its own L2, so in row order a line
-    // would be assembled from pieces written back by up to 8 L2s.  Logical
-    // row index i is therefore mapped to a row so that the indices with
-    // i % 8 == x (those blocks of XCD x take when the grid is a multiple of
-    // 8) are whole 32-row groups; indices past the last multiple of 256 are
-    // not remapped.  The map permutes each run of 256 rows.
-    const int64_t perm_rows = swz ? (a.rows & ~(int64_t)255) : 0;
-    auto row_of = [&](int64_t i) -> int64_t {
-        if (i >= perm_rows) return i;
-        const int64_t grp = (i >> 8) * 8 + (i & 7);  // 32-row group
-        const int m = (int)((i >> 3) & 31);          // member of the group
-        return (grp >> 2) * 128 + (m >> 3) * 32 + (grp & 3) * 8 + (m & 7);
-    };
-
-    auto fetch = [&](uint4 (&xn)[VPT], int64_t i) {
-        if (i < a.rows) {
-            const char* xr = static_cast<const char*>(a.x) + row_of(i) * row_bytes;
-#pragma unroll
-            for (int k = 0; k < VPT; ++k)
-                if (live(k)) xn[k] = load_stream(xr, lt + k * T);
-        }
-    };
-
-    int parity = 0;
-    // One row group: reduce, then quantize.  Every wave of the block calls
-    // this for the same row0 (the barrier inside is uniform).
-    auto process = [&](const uint4 (&xv)[VPT], int64_t row0) {
-        const bool active = row0 + slot < a.rows;
-        const int64_t row = row_of(row0 + slot);
-
-        double ssq = 0.0;
-        if (active) {
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) ssq += (double)V::sumsq(xv[k]);
-        }
-        ssq = wave_sum(ssq);
-        if (waves > 1) {  // uniform over the block
-            if ((lt & 63) == 0) red_sum[parity][red] = ssq;
-            __syncthreads();
-            ssq = 0.0;
-            for (int w = 0; w < waves; ++w) ssq += red_sum[parity][slot * waves + w];
-            parity ^= 1;
-        }
-
-        // A row's lanes are whole wavefronts, so `active` is uniform within a
-        // wave: every lane of a wave that reaches the lane swap below is live.
-        if (active) {
-            const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
-            // E4M3: block scale = gs * (amax_t * rstd) / 6, element factor
-            // gs * rstd / d.  UE8M0 (gs = 1): code from amax_t * rstd / 6,
-            // element factor rstd * 2^(127 - code).
-            const float c_scale = (float)(gs * rstd * (1.0 / 6.0));
-            const float c_elem = (float)(gs * rstd);
-
-            uint8_t* orow = static_cast<uint8_t*>(a.out) + row * (int64_t)(a.hidden >> 1);
-            // this row's scale bytes: row-major, or the row's place in its
-            // 128 x 4 tiles ((row/128) * K * 512 + (row%32) * 16 + ((row%128)/32) * 4)
-            uint8_t* srow = static_cast<uint8_t*>(a.scales) +
-                            (swz ? (row >> 7) * m_tile_bytes + (row & 31) * 16 + ((row & 127) >> 5) * 4
-                                 : row * (int64_t)nblk);
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int v = lt + k * T;
-                float t[EPV];  // s * g'
-                V::unpack(xv[k], t);
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) t[e] *= g[k][e];
-                // all lanes take part in the swaps (vectors past the row are
-                // zero, and a block's lanes are all live or all past the row)
-                float amax = abs_max<EPV>(0.0f, t);
-                amax = LPB == 2 ? pair_max_nonneg(amax) : quad_max_nonneg(amax);
-                uint32_t code;
-                float kq;
-                if constexpr (UE8M0) {
-                    code = ue8m0_code(amax * c_scale);
-                    kq = ue8m0_factor(c_elem, code);
-                } else {
-                    code = e4m3fn_scale_code(amax * c_scale);
-                    const float d = e4m3fn_decode(code);
-                    kq = d > 0.0f ? c_elem * __builtin_amdgcn_rcpf(d) : 0.0f;
-                }
-                if (live(k)) {
-                    float q[EPV];
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) q[e] = t[e] * kq;
-                    store_stream(orow, v, e2m1_x8(q));
-                    if ((v & (LPB - 1)) == 0) {
-                        const int j = v / LPB;  // block index in the row
-                        srow[swz ? (j >> 2) * 512 + (j & 3) : j] = (uint8_t)code;
-                    }
-                }
-            }
-        }
-    };
-
-    int64_t row0 = (int64_t)blockIdx.x * rpb;
-#pragma unroll
-    for (int b = 0; b + 1 < DEPTH; ++b) fetch(xb[b], row0 + b * stride + slot);
-    while (row0 < a.rows) {
-#pragma unroll
-        for (int b = 0; b < DEPTH; ++b) {
-            fetch(xb[(b + DEPTH - 1) % DEPTH], row0 + (DEPTH - 1) * stride + slot);
-            process(xb[b], row0);
-            row0 += stride;
-            if (row0 >= a.rows) break;
-        }
-    }
-}
-
-namespace {
-
-// rows in flight per block: the current one and the next (three measured no
-// faster on MI355X and costs 16 more VGPRs at four vectors per lane)
-constexpr int kDepth = 2;
-
-template <typename InT, int VPT, bool EXACT, bool ONE_ROW, int BLOCK, bool UE8M0>
-hipError_t launch_kernel(const FusedArgs& a, Shape s, hipStream_t stream) {
-    auto kern = fp4_kernel<InT, VPT, EXACT, ONE_ROW, kDepth, BLOCK, UE8M0>;
-    const int threads = s.waves * s.rpb * 64;
-    const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
-    // default: at most 4 row groups per block (MI355X streams this kernel best
-    // that way), and at least one block per resident slot while rows last
-    int64_t grid = s.grid;
-    if (grid <= 0) {
-        const int64_t resident = persistent_blocks(reinterpret_cast<const void*>(kern), threads);
-        grid = std::max(std::min(groups, resident), (groups + 3) / 4);
-    }
-    if (grid > groups) grid = groups;
-    if (grid > INT32_MAX) grid = INT32_MAX;
-    // swizzled scales: a multiple of 8 blocks keeps each XCD on its own rows
-    if (a.sf_swizzled && grid >= 8) grid &= ~(int64_t)7;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, stream, a);
-    return hipGetLastError();
-}
-
-template <typename InT, int VPT, int BLOCK, bool UE8M0>
-hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
-    a.waves = s.waves;
-    const bool exact = a.nvec == VPT * s.waves * 64;
-    if (s.rpb == 1)
-        return exact ? launch_kernel<InT, VPT, true, true, BLOCK, UE8M0>(a, s, stream)
-                     : launch_kernel<InT, VPT, false, true, BLOCK, UE8M0>(a, s, stream);
-    return exact ? launch_kernel<InT, VPT, true, false, BLOCK, UE8M0>(a, s, stream)
-                 : launch_kernel<InT, VPT, false, false, BLOCK, UE8M0>(a, s, stream);
-}
-
-template <typename InT, int BLOCK, bool UE8M0>
-hipError_t by_vpt(const FusedArgs& a, Shape s, hipStream_t st) {
-    switch (s.vpt) {
-    case 1: return launch_vpt<InT, 1, BLOCK, UE8M0>(a, s, st);
-    case 2: return launch_vpt<InT, 2, BLOCK, UE8M0>(a, s, st);
-    default: return launch_vpt<InT, 4, BLOCK, UE8M0>(a, s, st);
-    }
-}
-
-template <typename InT>
-hipError_t by_format(const FusedArgs& a, Fp4Format f, Shape s, hipStream_t st) {
-    if (f.block == 32)
-        return f.ue8m0 ? by_vpt<InT, 32, true>(a, s, st) : by_vpt<InT, 32, false>(a, s, st);
-    return f.ue8m0 ? by_vpt<InT, 16, true>(a, s, st) : by_vpt<InT, 16, false>(a, s, st);
-}
-
-}  // namespace
-
-hipError_t launch_fp4(const FusedArgs& a, int in_dtype, Fp4Format fmt, Shape s, hipStream_t stream) {
-    if (in_dtype == 1) return by_format<F16>(a, fmt, s, stream);
-    return by_format<BF16>(a, fmt, s, stream);
+hipError_t launch_fp4(const FusedArgs& a, int in_dtype, bool residual, Fp4Format fmt, Shape s, hipStream_t stream) {
+    if (in_dtype == 0) return launch_fp4_typed<float>(a, residual, fmt, s, stream);
+    if (in_dtype == 1) return launch_fp4_typed<F16>(a, residual, fmt, s, stream);
+    return launch_fp4_typed<BF16>(a, residual, fmt, s, stream);
 }
 
 }  // namespace rmsq

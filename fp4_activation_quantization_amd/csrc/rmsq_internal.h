@@ -11,8 +11,8 @@ namespace rmsq {
 // by the API layer before this is built.
 struct FusedArgs {
     const void* x;
-    const void* residual;      // FP8 residual variant only
-    void* residual_out;        // FP8 residual variant only
+    const void* residual;      // residual variants only
+    void* residual_out;        // residual variants only
     const void* gamma;
     void* out;                 // FP8: [rows, hidden]; FP4: [rows, hidden/2]
     void* scales;              // FP8: [rows]; FP4: [rows, hidden/block] or swizzled
@@ -46,14 +46,18 @@ struct Shape {
     int grid;
 };
 
+// Which fused path a shape is chosen for (the rmsq_query_shape `path` values).
+enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2 };
+
 // Pick the automatic shape for a row of nvec 16-byte vectors (or apply the
 // process-wide override).  Returns false if no supported shape holds the row.
-bool choose_shape(int64_t rows, int nvec, bool fp4, Shape* s);
+bool choose_shape(int64_t rows, int nvec, int path, Shape* s);
 
 // Kernel launchers (no argument checks).  Return the hipError_t of the launch.
 hipError_t launch_fp8(const FusedArgs& a, int in_dtype, bool residual, int out_fp8,
                       Shape shape, hipStream_t stream);
-hipError_t launch_fp4(const FusedArgs& a, int in_dtype, Fp4Format fmt, Shape shape, hipStream_t stream);
+hipError_t launch_fp4(const FusedArgs& a, int in_dtype, bool residual, Fp4Format fmt, Shape shape,
+                      hipStream_t stream);
 hipError_t launch_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
 hipError_t launch_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, hipStream_t stream);
 

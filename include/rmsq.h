@@ -113,7 +113,8 @@ int residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype,
  * rmsnorm_fp4 -- RMSNorm + block-scaled FP4 (NVFP4-style) quantization:
  * FlashInfer "rmsnorm_fp4quant.py" (rmsnorm_fp4quant, block_size 16, E4M3
  * scale factors, row-major scale layout).
- *   in_dtype     : RMSQ_F16 or RMSQ_BF16.
+ *   in_dtype     : RMSQ_BF16 or RMSQ_F16 (the page's inputs), or RMSQ_F32
+ *                  (an extension; the same arithmetic on fp32 rows).
  *   hidden       : multiple of 16.
  *   weight_offset: added to gamma (0 gives the page's operation).
  *   global_scale : DEVICE pointer to one fp32 value gs (read by the kernel,
@@ -167,6 +168,25 @@ int rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype,
                      float eps, float weight_offset, const float* global_scale,
                      int block_size, int scale_format, int scale_layout,
                      void* out, void* block_scales, hipStream_t stream);
+
+/*
+ * residual_rmsnorm_fp4quant -- rmsnorm_fp4quant of the pre-norm sum: the
+ * residual input and residual_output of Mojo "allreduce_residual_rmsnorm_fp8"
+ * (one GPU's share) in front of the FP4 quantizer.
+ *   residual, residual_out : [rows, hidden] in in_dtype, 16-byte aligned;
+ *                  residual_out = round_to_in_dtype(x + residual) (one
+ *                  rounding), and that stored value is what is normalized and
+ *                  quantized.  residual_out may be exactly x or exactly
+ *                  residual (in-place update); any other overlap is
+ *                  RMSQ_ERR_ALIAS.
+ *   Everything else as rmsnorm_fp4quant.
+ */
+int residual_rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype,
+                              const void* x, const void* residual, void* residual_out,
+                              const void* gamma, float eps, float weight_offset,
+                              const float* global_scale, int block_size, int scale_format,
+                              int scale_layout, void* out, void* block_scales,
+                              hipStream_t stream);
 
 /* Bytes of the block_scales buffer rmsnorm_fp4quant writes into for this
  * shape and layout (rows * hidden / block row-major; whole 128 x 4 tiles
@@ -226,8 +246,10 @@ int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t wr
  */
 int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks);
 
-/* Launch shape the next call with these arguments would use (for logs). */
-int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int is_fp4,
+/* Launch shape the next call with these arguments would use (for logs).
+ * path: 0 for the FP8 entry points, 1 for rmsnorm_fp4 / rmsnorm_fp4quant,
+ * 2 for residual_rmsnorm_fp4quant (RMSQ_ERR_VALUE otherwise). */
+int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path,
                      int* waves_per_row, int* vectors_per_lane, int* rows_per_block);
 
 /* Diagnostics. */

@@ -85,23 +85,26 @@ CANARY = 0xA5  # fill of swizzled scale buffers: padding bytes must keep it
 
 
 def run_fp4(w, inp, gs, *, rows_idx=None, weight_offset=None, stream=None):
-    """Run the workload's FP4 variant; returns (packed, row-major block scales)
-    for the selected rows.  A swizzled buffer is checked to leave its padding
-    untouched and is returned un-swizzled."""
+    """Run the workload's FP4 variant; returns (packed, row-major block scales,
+    residual_out or None) for the selected rows.  A swizzled buffer is checked
+    to leave its padding untouched and is returned un-swizzled."""
     x, g = to_dev(inp["x"]), to_dev(inp["gamma"])
     gst = torch.tensor([gs], dtype=torch.float32, device=DEV) if gs is not None else None
     off = w.weight_offset if weight_offset is None else weight_offset
     rows, hidden = x.shape
-    if w.fp4_block == 16 and w.fp4_scale == "e4m3" and not w.fp4_swizzled:
+    bs = None
+    if w.fp4_swizzled:
+        bs = torch.full((rq.fp4_scale_bytes(rows, hidden, w.fp4_block, True),), CANARY, dtype=torch.uint8,
+                        device=DEV)
+    kw = dict(eps=w.eps, weight_offset=off, global_scale=gst, block_size=w.fp4_block, scale_format=w.fp4_scale,
+              swizzled=w.fp4_swizzled, block_scales=bs, stream=stream)
+    ro = None
+    if w.residual:
+        packed, bs, ro = rq.residual_rmsnorm_fp4quant(x, to_dev(inp["residual"]), g, **kw)
+    elif w.fp4_block == 16 and w.fp4_scale == "e4m3" and not w.fp4_swizzled:
         packed, bs = rq.rmsnorm_fp4(x, g, eps=w.eps, weight_offset=off, global_scale=gst, stream=stream)
     else:
-        bs = None
-        if w.fp4_swizzled:
-            bs = torch.full((rq.fp4_scale_bytes(rows, hidden, w.fp4_block, True),), CANARY, dtype=torch.uint8,
-                            device=DEV)
-        packed, bs = rq.rmsnorm_fp4quant(x, g, eps=w.eps, weight_offset=off, global_scale=gst,
-                                         block_size=w.fp4_block, scale_format=w.fp4_scale, swizzled=w.fp4_swizzled,
-                                         block_scales=bs, stream=stream)
+        packed, bs = rq.rmsnorm_fp4quant(x, g, **kw)
     torch.cuda.synchronize()
     bs = bs.cpu().numpy()
     if w.fp4_swizzled:
@@ -109,20 +112,26 @@ def run_fp4(w, inp, gs, *, rows_idx=None, weight_offset=None, stream=None):
         bs, pad = unswizzle_scales(raw, rows, hidden // w.fp4_block)
         assert np.all(raw[pad] == CANARY), "swizzled padding bytes were written"
     sel = slice(None) if rows_idx is None else np.asarray(rows_idx)
-    return packed.cpu().numpy()[sel], bs[sel]
+    ro = workloads.bits(ro.cpu())[sel] if ro is not None else None
+    return packed.cpu().numpy()[sel], bs[sel], ro
 
 
 def check_fp4(w, inp, gs, *, rows_idx=None, label="", weight_offset=None):
-    p, bs = run_fp4(w, inp, gs, rows_idx=rows_idx, weight_offset=weight_offset)
+    p, bs, ro = run_fp4(w, inp, gs, rows_idx=rows_idx, weight_offset=weight_offset)
     x = workloads.bits(inp["x"])
+    r = workloads.bits(inp["residual"]) if w.residual else None
     if rows_idx is not None:
         x = x[rows_idx]
+        r = r[rows_idx] if r is not None else None
     g = workloads.bits(inp["gamma"])
     off = w.weight_offset if weight_offset is None else weight_offset
     kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=off)
     gsv = 1.0 if gs is None else gs
-    ref = oracle.rmsnorm_fp4(x, g, global_scale=gsv, block_size=w.fp4_block, scale_format=w.fp4_scale, **kw)
-    y = oracle.rmsnorm_y(x, g, **kw)["y"]
+    ref = oracle.rmsnorm_fp4(x, g, global_scale=gsv, block_size=w.fp4_block, scale_format=w.fp4_scale, residual=r,
+                             **kw)
+    if r is not None:
+        assert np.array_equal(ro, ref["residual_out"]), "residual_out differs from the oracle's"
+    y = oracle.rmsnorm_y(x, g, residual=r, **kw)["y"]
     rep = compare_fp4(p, bs, ref, y, global_scale=gsv, block_size=w.fp4_block, scale_format=w.fp4_scale)
     say(f"  parity {label or w.name}: {rep}")
     return rep

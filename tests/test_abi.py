@@ -41,7 +41,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "rmsq_fp4_scale_bytes",
+    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "residual_rmsnorm_fp4quant",
+              "rmsq_fp4_scale_bytes",
               "rmsq_convert", "rmsq_stream_probe",
               "rmsq_set_tuning", "rmsq_query_shape", "rmsq_status_string", "rmsq_abi_version",
               "rmsq_last_hip_error"):
@@ -173,7 +174,7 @@ def test_fp8_alias_errors():
 
 
 def test_fp4_errors():
-    assert fp4(dt=rq.F32) == DTYPE
+    assert fp4(dt=rq.F32) == UNSUP   # fp32 input passes every check
     assert fp4(dt=9) == DTYPE
     assert fp4(hidden=24) == SHAPE
     assert fp4(hidden=0) == SHAPE
@@ -217,6 +218,37 @@ def test_fp4quant_errors():
     below = ctypes.c_void_p(BASE + 2 * MB - 2048)
     assert fp4q(bs=below) == UNSUP
     assert fp4q(bs=below, layout=rq.SF_SWIZZLED) == ALIAS
+
+
+def rfp4q(x=None, r=None, ro=None, g=None, out=None, bs=None, dt=rq.BF16, hidden=4096, gs=None):
+    x = P(0) if x is None else x
+    r = P(4) if r is None else r
+    ro = P(5) if ro is None else ro
+    g = P(1) if g is None else g
+    out = P(2) if out is None else out
+    bs = P(3) if bs is None else bs
+    return rq.lib().residual_rmsnorm_fp4quant(4, hidden, dt, x, r, ro, g, 1e-6, 0.0, gs, 16, rq.SF_E4M3,
+                                              rq.SF_ROW_MAJOR, out, bs, None)
+
+
+def test_residual_fp4quant_errors():
+    z = ctypes.c_void_p(0)
+    near = lambda i, k: ctypes.c_void_p(BASE + i * MB + k)
+    assert rfp4q() == UNSUP and rfp4q(dt=rq.F32) == UNSUP
+    assert rfp4q(r=z) == NULL and rfp4q(ro=z) == NULL
+    assert rfp4q(r=near(4, 4)) == ALIGN and rfp4q(ro=near(5, 8)) == ALIGN
+    assert rfp4q(ro=near(0, 16)) == ALIAS      # partial overlap with x
+    assert rfp4q(ro=near(4, 32)) == ALIAS      # partial overlap with residual
+    assert rfp4q(ro=P(2)) == ALIAS             # over the codes
+    assert rfp4q(ro=P(3)) == ALIAS             # over the scales
+    assert rfp4q(ro=P(1)) == ALIAS             # over gamma
+    assert rfp4q(r=P(2)) == ALIAS              # residual under the codes
+    assert rfp4q(gs=P(5)) == ALIAS             # global scale inside residual_out
+    # exact in-place updates pass every check
+    assert rfp4q(ro=P(0)) == UNSUP and rfp4q(ro=P(4)) == UNSUP
+    L = rq.lib()
+    q = lambda path: L.rmsq_query_shape(16384, 512, rq.BF16, path, None, None, None)  # fits the forced shape
+    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == VALUE
 
 
 def test_fp4_scale_bytes():

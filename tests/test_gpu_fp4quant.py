@@ -1,6 +1,8 @@
-"""GPU parity of rmsnorm_fp4quant (through the C ABI) against the oracle for
-every block size (16, 32), scale format (E4M3, UE8M0) and scale layout
-(row-major, swizzled 128 x 4 tiles), on bf16 and fp16 inputs:
+"""GPU parity of rmsnorm_fp4quant and residual_rmsnorm_fp4quant (through the
+C ABI) against the oracle for every block size (16, 32), scale format (E4M3,
+UE8M0) and scale layout (row-major, swizzled 128 x 4 tiles), on bf16, fp16
+and fp32 inputs (fp32 puts a 16-element block on 4 lanes and a 32-element
+block on 8):
 
 * row counts that leave a ragged last 128-row tile and hidden sizes whose
   scale columns leave a ragged last 4-column tile (swizzled padding must keep
@@ -8,7 +10,8 @@ every block size (16, 32), scale format (E4M3, UE8M0) and scale layout
 * the hand-worked rows of tests/golden/hand_rows.json (fp4_block_rows),
   byte for byte;
 * forced launch shapes (1-16 waves per row, 1-4 vectors per lane), so the
-  4-lane block reduction of 32-element blocks runs in every mapping;
+  2-, 4- and 8-lane block reductions run in every mapping;
+* residual_out bit-exact, including in-place updates over x or residual;
 * the 16-element E4M3 row-major case equals rmsnorm_fp4 bit for bit.
 The comparison rule is in tests/parity.py.
 """
@@ -37,18 +40,20 @@ def default_shape():
     rq.set_tuning(0, 0, 0)
 
 
-def _inputs(rows, hidden, dt, seed):
+def _inputs(rows, hidden, dt, seed, resid=False):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((rows, hidden))
     heavy = rng.choice(hidden, size=max(1, hidden // 100), replace=False)
     x[:, heavy] = rng.standard_t(3.0, size=(rows, heavy.size))
-    x *= np.exp2(rng.integers(-8, 8, (rows, 1)))  # rows of different magnitude
-    return {"x": torch.from_numpy(x).to(TD[dt]), "residual": None,
+    mag = np.exp2(rng.integers(-8, 8, (rows, 1)))  # rows of different magnitude
+    r = torch.from_numpy(rng.standard_normal((rows, hidden)) * mag).to(TD[dt]) if resid else None
+    return {"x": torch.from_numpy(x * mag).to(TD[dt]), "residual": r,
             "gamma": torch.from_numpy(rng.uniform(0.8, 1.2, hidden)).to(TD[dt])}
 
 
-def _wl(rows, hidden, dt, block, fmt, swz, offset=0.0):
-    return workloads.Workload("fp4quant", "rmsnorm_fp4", rows, hidden, dt, 98, eps=1e-6, weight_offset=offset,
+def _wl(rows, hidden, dt, block, fmt, swz, offset=0.0, resid=False):
+    op = "residual_rmsnorm_fp4" if resid else "rmsnorm_fp4"
+    return workloads.Workload("fp4quant", op, rows, hidden, dt, 98, eps=1e-6, weight_offset=offset,
                               fp4_block=block, fp4_scale=fmt, fp4_swizzled=swz)
 
 
@@ -61,7 +66,7 @@ def _gs(inp, w):
 @pytest.mark.parametrize("swz", [False, True], ids=["rowmajor", "swizzled"])
 @pytest.mark.parametrize("fmt", ["e4m3", "ue8m0"])
 @pytest.mark.parametrize("block", [16, 32])
-@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_every_variant(dt, block, fmt, swz):
     for rows, hidden in ((300, 160), (131, 7168), (257, 2080)):
         w = _wl(rows, hidden, dt, block, fmt, swz)
@@ -106,6 +111,47 @@ def test_forced_launch_shapes_block32(fmt):
         rq.set_tuning(waves, vpt, 7)
         say(f"[fp4quant shape] {fmt} waves={waves} vpt={vpt}")
         check_fp4(w, inp, gs, label=f"block32 {fmt} {waves}x{vpt}")
+    rq.set_tuning(0, 0, 0)
+
+
+@pytest.mark.parametrize("swz", [False, True], ids=["rowmajor", "swizzled"])
+@pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0"), (32, "e4m3"), (16, "ue8m0")])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_residual_variants(dt, block, fmt, swz):
+    for rows, hidden in ((300, 160), (131, 7168)):
+        w = _wl(rows, hidden, dt, block, fmt, swz, resid=True)
+        inp = _inputs(rows, hidden, dt, seed=rows + hidden + block + 1, resid=True)
+        say(f"[fp4quant residual] {dt} block={block} {fmt} swizzled={swz} rows={rows} hidden={hidden}")
+        check_fp4(w, inp, _gs(inp, w), label=f"residual {dt} {block} {fmt} swz={swz} {rows}x{hidden}")
+
+
+@pytest.mark.parametrize("where", ["x", "residual"])
+def test_residual_in_place(where):
+    rows, hidden = 77, 2048
+    inp = _inputs(rows, hidden, "bf16", seed=5, resid=True)
+    x, r, g = inp["x"].to(DEV), inp["residual"].to(DEV), inp["gamma"].to(DEV)
+    want_p, want_s, want_ro = rq.residual_rmsnorm_fp4quant(x.clone(), r.clone(), g, block_size=32)
+    target = x if where == "x" else r
+    p, sc, ro = rq.residual_rmsnorm_fp4quant(x, r, g, block_size=32, residual_out=target)
+    torch.cuda.synchronize()
+    say(f"[fp4quant in place] residual_out over {where}")
+    assert ro.data_ptr() == target.data_ptr()
+    assert torch.equal(ro, want_ro) and torch.equal(p, want_p) and torch.equal(sc, want_s)
+
+
+@pytest.mark.parametrize("resid", [False, True])
+@pytest.mark.parametrize("block", [16, 32])
+def test_forced_launch_shapes_f32(block, resid):
+    hidden = 2048  # 512 fp32 vectors
+    inp = _inputs(70, hidden, "f32", seed=13, resid=resid)
+    w = _wl(70, hidden, "f32", block, "ue8m0" if block == 32 else "e4m3", False, resid=resid)
+    gs = _gs(inp, w)
+    for waves, vpt in ((1, 4), (2, 4), (2, 2), (4, 2), (8, 1), (3, 4), (16, 1), (12, 1)):
+        if waves * 64 * vpt * 4 < hidden:
+            continue
+        rq.set_tuning(waves, vpt, 7)
+        say(f"[fp4quant f32 shape] block={block} resid={resid} waves={waves} vpt={vpt}")
+        check_fp4(w, inp, gs, label=f"f32 block{block} resid={resid} {waves}x{vpt}")
     rq.set_tuning(0, 0, 0)
 
 

@@ -26,16 +26,18 @@ from gpu_common import DEV, check_fp4, check_fp8, run_fp8, sample_rows, say
 pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
 W = workloads.WORKLOADS
-FP8_NAMES = [n for n, w in W.items() if w.op != "rmsnorm_fp4"]
+FP8_NAMES = [n for n, w in W.items() if not w.fp4]
 SMALL_ROWS = {"rmsnorm_fp8_bf16_16x512": 16, "residual_rmsnorm_fp8_bf16_8192x4096": 301,
               "rmsnorm_fp8_f16_decode_1x8192": 1, "rmsnorm_fp8_f16_decode_8x8192": 8,
               "rmsnorm_fp8_f16_decode_64x8192": 64, "residual_rmsnorm_fp8_bf16_32768x8192": 203,
               "residual_rmsnorm_fp8_f32_32768x8192": 203, "rmsnorm_fp4_bf16_16384x7168": 157,
-              "rmsnorm_mxfp4_bf16_16384x7168": 157, "rmsnorm_fp4_swizzled_bf16_16384x7168": 300}
+              "rmsnorm_mxfp4_bf16_16384x7168": 157, "rmsnorm_fp4_swizzled_bf16_16384x7168": 300,
+              "residual_rmsnorm_fp4_bf16_16384x7168": 157}
 
 
-def golden_gs():
-    return json.load(open(os.path.join(HERE, "golden", "fp4_global_scale.json")))["global_scale"]
+def golden_gs(name):
+    entry = json.load(open(os.path.join(HERE, "golden", "fp4_global_scale.json")))["workloads"].get(name)
+    return entry["global_scale"] if entry else 1.0
 
 
 def fp4_gs_for(inp, w=None):
@@ -56,8 +58,8 @@ def default_shape():
 def test_workload_small_all_elements(name):
     w = W[name]
     inp = workloads.make(name, rows=SMALL_ROWS[name])
-    say(f"[small] {name} rows={SMALL_ROWS[name]} shape={rq.query_shape(SMALL_ROWS[name], w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.op == 'rmsnorm_fp4')}")
-    if w.op == "rmsnorm_fp4":
+    say(f"[small] {name} rows={SMALL_ROWS[name]} shape={rq.query_shape(SMALL_ROWS[name], w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.fp4, w.residual)}")
+    if w.fp4:
         check_fp4(w, inp, fp4_gs_for(inp))
     else:
         check_fp8(w, inp)
@@ -73,8 +75,8 @@ def test_workload_full_size_sampled_rows(name):
     if sel.get("outlier_rows") is not None:
         must = list(sel["outlier_rows"][:8])
     rows = sample_rows(w.rows, 40, seed=17, must=must)
-    if w.op == "rmsnorm_fp4":
-        check_fp4(w, inp, golden_gs(), rows_idx=rows)
+    if w.fp4:
+        check_fp4(w, inp, golden_gs(name), rows_idx=rows)
     else:
         check_fp8(w, inp, rows_idx=rows)
 

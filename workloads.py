@@ -13,7 +13,8 @@ size with a few hot outlier channels, single-token decode batches with a
 Gemma-style (1 + gamma) weight, a 70B-class prefill batch with heavy-tailed
 (Laplace) activations and a few hot rows, and a 7168-wide FP4 tensor whose
 1% heavy channels follow Student-t(3) (quantized three ways: 16-element E4M3
-scales row-major or swizzled, and 32-element UE8M0 scales).
+scales row-major or swizzled, and 32-element UE8M0 scales; and once more
+behind a residual add).
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    op: str                 # "rmsnorm_fp8" | "residual_rmsnorm_fp8" | "rmsnorm_fp4"
+    op: str  # "rmsnorm_fp8" | "residual_rmsnorm_fp8" | "rmsnorm_fp4" | "residual_rmsnorm_fp4"
     rows: int
     hidden: int
     in_dtype: str           # "bf16" | "f16" | "f32"
@@ -56,7 +57,11 @@ class Workload:
 
     @property
     def residual(self) -> bool:
-        return self.op == "residual_rmsnorm_fp8"
+        return self.op.startswith("residual_")
+
+    @property
+    def fp4(self) -> bool:
+        return self.op.endswith("_fp4")
 
     def with_rows(self, rows: int) -> "Workload":
         return dataclasses.replace(self, rows=rows)
@@ -90,6 +95,9 @@ WORKLOADS = {w.name: w for w in [
              gamma_lo=0.8, gamma_hi=1.2, heavy_channel_frac=0.01, fp4_block=32, fp4_scale="ue8m0"),
     Workload("rmsnorm_fp4_swizzled_bf16_16384x7168", "rmsnorm_fp4", 16384, 7168, "bf16", 4, eps=1e-6,
              gamma_lo=0.8, gamma_hi=1.2, heavy_channel_frac=0.01, fp4_swizzled=True),
+    # a residual stream in front of the FP4 quantizer (x and residual drawn alike)
+    Workload("residual_rmsnorm_fp4_bf16_16384x7168", "residual_rmsnorm_fp4", 16384, 7168, "bf16", 5, eps=1e-6,
+             gamma_lo=0.8, gamma_hi=1.2, heavy_channel_frac=0.01),
 ]}
 
 # The workload the headline throughput is quoted on.
