@@ -91,6 +91,7 @@ class Case:
         g = inp["gamma"].to(dev)
         r0 = inp["residual"].to(dev) if inp["residual"] is not None else None
         self.keep = [g]
+        self.outs = []  # tensors the calls write
         self.calls = []
         L = rq.lib()
         dt = {"bf16": rq.BF16, "f16": rq.F16, "f32": rq.F32}[w.in_dtype]
@@ -104,12 +105,14 @@ class Case:
                                  dtype=torch.uint8, device=dev)
                 gst = torch.tensor([gs], dtype=torch.float32, device=dev)
                 self.keep += [x, out, bs, gst]
+                self.outs += [out, bs]
                 sfmt = rq.SF_UE8M0 if w.fp4_scale == "ue8m0" else rq.SF_E4M3
                 layout = rq.SF_SWIZZLED if w.fp4_swizzled else rq.SF_ROW_MAJOR
                 if w.residual:
                     r = r0 if i == 0 else r0.clone()
                     ro = torch.empty_like(x)
                     self.keep += [r, ro]
+                    self.outs.append(ro)
                     args = (w.rows, w.hidden, dt, P(x), P(r), P(ro), P(g), w.eps, w.weight_offset, P(gst), w.fp4_block,
                             sfmt, layout, P(out), P(bs), stream)
                     self.calls.append((L.residual_rmsnorm_fp4quant, args))
@@ -126,20 +129,28 @@ class Case:
                 r = r0 if i == 0 else r0.clone()
                 ro = torch.empty_like(x)
                 self.keep += [x, r, ro, out, sc]
+                self.outs += [ro, out, sc]
                 args = (w.rows, w.hidden, dt, P(x), P(r), P(ro), P(g), w.eps, w.weight_offset, w.scale_ub, fmt,
                         P(out), sdt, P(sc), stream)
                 self.calls.append((L.residual_rmsnorm_fp8, args))
             else:
                 self.keep += [x, out, sc]
+                self.outs += [out, sc]
                 args = (w.rows, w.hidden, dt, P(x), P(g), w.eps, w.weight_offset, w.scale_ub, fmt, P(out), sdt,
                         P(sc), stream)
                 self.calls.append((L.rmsnorm_fp8, args))
 
-    def step(self, i: int) -> None:
+    def step(self, i: int, stream: ctypes.c_void_p | None = None) -> None:
         fn, args = self.calls[i % len(self.calls)]
+        if stream is not None:  # every entry point takes the stream last
+            args = args[:-1] + (stream,)
         rc = fn(*args)
         if rc != 0:
             raise rq.RmsqError(fn.__name__, rc, rq.lib().rmsq_last_hip_error())
+
+    def outputs(self) -> list:
+        """The device tensors the calls write (for replay checks)."""
+        return self.outs
 
 
 def time_case(case: Case, steps: int, warmup: int) -> dict:
@@ -164,6 +175,47 @@ def time_case(case: Case, steps: int, warmup: int) -> dict:
     b = algorithmic_bytes(case.w)
     return {"steps": steps, "ms_per_step": total_ms / steps, "wall_s": wall, "launch_us": per_us, "bytes": b,
             "gbps": b / (per_us * 1e-6) / 1e9, "rows_per_s": case.w.rows / (per_us * 1e-6)}
+
+
+def time_graph(case: Case, calls: int, replays: int) -> dict:
+    """Per-call GPU time of latency-sized launches without host launch
+    overhead: `calls` back-to-back calls captured into one HIP graph (on the
+    capture stream), replayed `replays` times between two events.  Each
+    replay's outputs are checked against an eager run first."""
+    eager = None
+    torch.cuda.synchronize()
+    for i in range(calls):
+        case.step(i)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in case.outputs()]
+    for t in case.outputs():
+        t.fill_(0)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for i in range(calls):
+                case.step(i, sp)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(3):  # several replays, each checked against the eager run
+        for t in case.outputs():
+            t.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e in zip(case.outputs(), eager):
+            if not torch.equal(t, e):
+                raise RuntimeError(f"{case.w.name}: graph replay differs from the eager run")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    per_us = t0.elapsed_time(t1) * 1e3 / (replays * calls)
+    del g
+    return {"graph_us": per_us, "graph_calls": calls, "graph_replays": replays}
 
 
 def stream_ceiling(w: workloads.Workload, copies: int, steps: int, warmup: int) -> float:
@@ -307,6 +359,8 @@ def main() -> int:
         res = time_case(case, steps, args.warmup)
         res["buffer_sets"] = k
         res["launch"] = rq.query_shape(w.rows, w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.fp4, w.residual)
+        # latency-sized calls: also their GPU time inside a graph (decode steps run graphed)
+        res.update(time_graph(case, 100, max(5, steps // 100)) if algorithmic_bytes(w) < STREAM_MIN_BYTES else {})
         results[name] = res
         del case
         torch.cuda.empty_cache()
@@ -314,6 +368,8 @@ def main() -> int:
         res["stream_gbps"] = (stream_ceiling(w, k, steps, args.warmup)
                               if algorithmic_bytes(w) >= STREAM_MIN_BYTES and not args.no_stream_ceiling else None)
         ceil = f", streaming reference {res['stream_gbps']:.0f} GB/s" if res["stream_gbps"] else ""
+        if "graph_us" in res:
+            ceil += f", {res['graph_us']:.2f} us per call in a graph"
         print(f"# {name}: {res['launch_us']:.2f} us/launch, {res['gbps']:.0f} GB/s{ceil}, {k} buffer set(s), "
               f"launch {res['launch']}", file=sys.stderr, flush=True)
 
@@ -345,6 +401,7 @@ def main() -> int:
         "workloads": {n: {"launch_us": round(r["launch_us"], 3), "gbps": round(r["gbps"], 1),
                           "frac_hbm": round(r["gbps"] / HBM_PEAK_GBS, 4), "rows_per_s": round(r["rows_per_s"], 1),
                           "bytes": r["bytes"], "buffer_sets": r["buffer_sets"], "launch": r["launch"],
+                          "graph_us": round(r["graph_us"], 3) if "graph_us" in r else None,
                           "stream_reference_gbps": round(r["stream_gbps"], 1) if r["stream_gbps"] else None,
                           "frac_of_stream_reference": round(r["gbps"] / r["stream_gbps"], 4)
                           if r["stream_gbps"] else None}

@@ -294,8 +294,14 @@ def test_tuning_and_query_shape():
     try:
         s = rq.query_shape(8192, 4096, rq.torch.bfloat16)
         assert s["waves_per_row"] * 64 * s["vectors_per_lane"] * 8 >= 4096
-        assert rq.query_shape(1, 8192, rq.torch.float16) == {"waves_per_row": 16, "vectors_per_lane": 1,
+        # small batches: 2 vectors per lane over up to 16 waves
+        assert rq.query_shape(1, 8192, rq.torch.float16) == {"waves_per_row": 8, "vectors_per_lane": 2,
                                                               "rows_per_block": 1}
+        assert rq.query_shape(1, 16384, rq.torch.float32)["waves_per_row"] == 16
+        assert rq.query_shape(1, 32768, rq.torch.bfloat16) == {"waves_per_row": 16, "vectors_per_lane": 4,
+                                                               "rows_per_block": 1}
+        assert rq.query_shape(1, 512, rq.torch.bfloat16) == {"waves_per_row": 1, "vectors_per_lane": 1,
+                                                             "rows_per_block": 4}
         rq.set_tuning(1, 1, 0)
         with pytest.raises(rq.RmsqError):
             rq.query_shape(8, 4096, rq.torch.bfloat16)  # 64 lanes x 1 vector cannot hold 512 vectors
