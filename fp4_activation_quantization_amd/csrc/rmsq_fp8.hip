@@ -50,19 +50,26 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
     __shared__ double red_sum[2][16];
     __shared__ int red_max[2][16];
 
-    // gamma + weight_offset for this lane's columns, fp32 (zero past the row)
+    // gamma + weight_offset for this lane's columns, fp32 (zero past the row).
+    // Without a residual it is loaded and unpacked once, before the rows; the
+    // residual variant loads it with each row instead, in flight together
+    // with the row's x and residual (measured on MI355X: the residual variant
+    // streams ~1% faster that way, the plain one has ~6% lower latency for a
+    // one-row call the first way).
     float g[VPT][EPV];
+    auto load_gamma = [&]() {
+        uint4 gv[VPT];
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        if (live(k)) {
-            V::unpack(reinterpret_cast<const uint4*>(a.gamma)[lt + k * T], g[k]);
+        for (int k = 0; k < VPT; ++k)
+            gv[k] = live(k) ? reinterpret_cast<const uint4*>(a.gamma)[lt + k * T] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) g[k][e] += a.weight_offset;
-        } else {
+        for (int k = 0; k < VPT; ++k) {
+            V::unpack(gv[k], g[k]);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) g[k][e] = 0.0f;
+            for (int e = 0; e < EPV; ++e) g[k][e] = live(k) ? g[k][e] + a.weight_offset : 0.0f;
         }
-    }
+    };
+    if constexpr (!RESID) load_gamma();
 
     int parity = 0;
     for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
@@ -78,17 +85,25 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
             uint4 xv[VPT];
 #pragma unroll
             for (int k = 0; k < VPT; ++k) xv[k] = live(k) ? load_stream(xr, lt + k * T) : make_uint4(0, 0, 0, 0);
+            // every load of the row is issued before any store: residual_out
+            // may alias residual, so a load placed after a store could not be
+            // moved ahead of it and each vector would cost a round trip
+            uint4 rv[RESID ? VPT : 1];
+            if constexpr (RESID) {
+                const char* rr = static_cast<const char*>(a.residual) + row * row_bytes;
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) rv[k] = live(k) ? load_stream(rr, lt + k * T) : make_uint4(0, 0, 0, 0);
+            }
+            if constexpr (RESID) load_gamma();  // an L2 hit after the first block
             if constexpr (RESID) {
                 // residual_out may be x or residual itself: each vector is read
-                // and then written by the one lane that owns it
-                const char* rr = static_cast<const char*>(a.residual) + row * row_bytes;
+                // (above) and then written by the one lane that owns it
                 char* ro = static_cast<char*>(a.residual_out) + row * row_bytes;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
-                    const uint4 rv = live(k) ? load_stream(rr, lt + k * T) : make_uint4(0, 0, 0, 0);
                     float xf[EPV], rf[EPV];
                     V::unpack(xv[k], xf);
-                    V::unpack(rv, rf);
+                    V::unpack(rv[k], rf);
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) xf[e] += rf[e];
                     // one rounding of the fp32 sum to the element type; fp32 keeps
