@@ -53,9 +53,9 @@ def lib() -> ctypes.CDLL:
     L.oracle_rmsnorm_fp8.restype = I
     L.oracle_rmsnorm_fp4.argtypes = [I64, I64, I, P, P, D, D, D, P, P, P, P]
     L.oracle_rmsnorm_fp4.restype = I
-    L.oracle_rmsnorm_fp4q.argtypes = [I64, I64, I, P, P, P, P, D, D, D, I, I, P, P, P, P]
+    L.oracle_rmsnorm_fp4q.argtypes = [I64, I64, I, P, P, P, P, D, D, D, I, I, I, P, P, P, P]
     L.oracle_rmsnorm_fp4q.restype = I
-    L.oracle_rmsnorm_y.argtypes = [I64, I64, I, P, P, P, P, D, D, P, P]
+    L.oracle_rmsnorm_y.argtypes = [I64, I64, I, P, P, P, P, D, D, I, P, P]
     L.oracle_rmsnorm_y.restype = I
     L.oracle_rmsnorm_absmax.argtypes = [I64, I64, I, P, P, D, D]
     L.oracle_rmsnorm_absmax.restype = D
@@ -136,7 +136,7 @@ def rmsnorm_fp8(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, sc
 
 def rmsnorm_fp4(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, global_scale: float,
                 threads: int | None = None, want_q: bool = True, block_size: int = 16,
-                scale_format: str = "e4m3", residual=None) -> dict:
+                scale_format: str = "e4m3", residual=None, round_product: bool = False) -> dict:
     """Reference FP4 (E2M1) path with one scale per block of block_size (16 or
     32) elements: E4M3 scales (gs * amax / 6 clamped to 448) or UE8M0 scales
     (power of two >= amax / 6, no global scale).
@@ -146,7 +146,8 @@ def rmsnorm_fp4(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, gl
     [rows, hidden] float64 and sf [rows, hidden/block_size] float64 (the
     unrounded block scale: after the clamp for E4M3, amax / 6 for UE8M0).
     With a residual, the row is s = round(x + residual) (also returned as
-    residual_out bits) and the quantizer runs on it.
+    residual_out bits) and the quantizer runs on it.  round_product: the FP4
+    page's numerics, y = round_to_in_dtype(s * g') * rstd.
     """
     L = lib()
     x = _bits_array(x, in_dtype)
@@ -173,7 +174,7 @@ def rmsnorm_fp4(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, gl
         return L.oracle_rmsnorm_fp4q(n, hidden, DTYPES[in_dtype], _ptr(x[r0:r1]),
                                      _ptr(res[r0:r1]) if res is not None else None,
                                      _ptr(rout[r0:r1]) if rout is not None else None, _ptr(g), e, o, gs,
-                                     block_size, sfmt, _ptr(packed[r0:r1]), _ptr(bs[r0:r1]),
+                                     block_size, sfmt, int(round_product), _ptr(packed[r0:r1]), _ptr(bs[r0:r1]),
                                      _ptr(q[r0:r1]) if q is not None else None, _ptr(sf[r0:r1]))
 
     _run(work, rows, threads)
@@ -213,8 +214,9 @@ def swizzle_scales(block_scales: np.ndarray, out: np.ndarray | None = None, fill
 
 
 def rmsnorm_y(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, residual=None,
-              threads: int | None = None) -> dict:
-    """Normalized values y (float64), rstd per row and residual_out bits."""
+              threads: int | None = None, round_product: bool = False) -> dict:
+    """Normalized values y (float64), rstd per row and residual_out bits
+    (round_product: the FP4 page-compatible y, see rmsnorm_fp4)."""
     L = lib()
     x = _bits_array(x, in_dtype)
     g = _bits_array(gamma, in_dtype)
@@ -232,7 +234,7 @@ def rmsnorm_y(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, resi
         return L.oracle_rmsnorm_y(n, hidden, DTYPES[in_dtype], _ptr(x[r0:r1]),
                                   _ptr(res[r0:r1]) if res is not None else None,
                                   _ptr(rout[r0:r1]) if rout is not None else None,
-                                  _ptr(g), e, o, _ptr(y[r0:r1]), _ptr(rstd[r0:r1]))
+                                  _ptr(g), e, o, int(round_product), _ptr(y[r0:r1]), _ptr(rstd[r0:r1]))
 
     _run(work, rows, threads)
     return {"y": y, "rstd": rstd, "residual_out": rout}

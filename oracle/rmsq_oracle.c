@@ -38,6 +38,9 @@
  *     on the pages and in the kernel take), after an exact float64 path.
  *   - Residual: s = round_to_in_dtype(x + r) (exact sum, one rounding) and
  *     the normalized value is this stored s.
+ *   - FP4 page-compatible mode (optional): the product s * g' is rounded once
+ *     to the input type before the rstd scaling, as [P3]'s kernel multiplies
+ *     x and w in 16 bits; everything else stays exact.
  *
  * Formats (magnitude code m = (exponent field << mbits) | mantissa field):
  *   E4M3FN  : 4 exp bits, 3 mantissa, bias 7, largest finite code 0x7E = 448,
@@ -245,9 +248,31 @@ static double store_elem(int dt, void* p, int64_t i, double v) {
 /* Steps shared by both outputs, one row: s (optionally x + residual, rounded
  * and written to residual_out), then y = s * rstd * (gamma + offset).
  * Returns rstd.  s and y are caller buffers of length hidden. */
+/* The product s * g' rounded once to the input type ([P3] kernel: it
+ * multiplies x and w as 16-bit pairs, mul.bf16x2 / mul.f16x2, before scaling
+ * by rstd); fp32 inputs are rounded to fp32.  Used by the FP4 path's
+ * page-compatible mode only. */
+static double round_to_dt(int dt, double v) {
+    if (dt == ORQ_F32) return (double)(float)v;
+    if (dt == ORQ_F16) return value_f16(bits_f16(v));
+    return value_bf16(bits_bf16(v));
+}
+
+static double norm_row_mode(int64_t hidden, int in_dt, const void* x, const void* residual,
+                            void* residual_out, const void* gamma, double eps, double offset,
+                            int round_product, double* s, double* y);
+
 static double norm_row(int64_t hidden, int in_dt, const void* x, const void* residual,
                        void* residual_out, const void* gamma, double eps, double offset,
                        double* s, double* y) {
+    return norm_row_mode(hidden, in_dt, x, residual, residual_out, gamma, eps, offset, 0, s, y);
+}
+
+/* With round_product, y = round_to_dt(s * g') * rstd (the FP4 page's order);
+ * otherwise y = s * rstd * g'. */
+static double norm_row_mode(int64_t hidden, int in_dt, const void* x, const void* residual,
+                            void* residual_out, const void* gamma, double eps, double offset,
+                            int round_product, double* s, double* y) {
     for (int64_t j = 0; j < hidden; j++) {
         double xj = load_elem(in_dt, x, j);
         if (residual) {
@@ -263,7 +288,7 @@ static double norm_row(int64_t hidden, int in_dt, const void* x, const void* res
     double rstd = 1.0 / sqrt(mean_sq + eps);
     for (int64_t j = 0; j < hidden; j++) {
         double g = load_elem(in_dt, gamma, j) + offset;
-        y[j] = s[j] * rstd * g;
+        y[j] = round_product ? round_to_dt(in_dt, s[j] * g) * rstd : s[j] * rstd * g;
     }
     return rstd;
 }
@@ -322,6 +347,8 @@ int oracle_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dt,
  *   row is s = round_to_in_dt(x + r), written to residual_out, as in the FP8
  *   path ([P2] residual_output; the FP4 page has no residual, so this pairs
  *   its quantizer with [P2]'s pre-norm sum).  residual may be NULL.
+ *   round_product: the FP4 page's numerics -- s * g' is rounded once to the
+ *   input type before the rstd scaling ([P3] kernel, 16-bit x * w).
  *   out: [rows, hidden/2] bytes, element 2k in the low nibble of byte k.
  *   block_scales: [rows, hidden/block] scale codes, row-major.
  *   global_scale: the fp32 value, widened.
@@ -332,8 +359,8 @@ int oracle_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dt,
 int oracle_rmsnorm_fp4q(int64_t rows, int64_t hidden, int in_dt,
                         const void* x, const void* residual, void* residual_out,
                         const void* gamma, double eps, double offset,
-                        double global_scale, int block, int sfmt, uint8_t* out, uint8_t* block_scales,
-                        double* q_out, double* sf_out) {
+                        double global_scale, int block, int sfmt, int round_product,
+                        uint8_t* out, uint8_t* block_scales, double* q_out, double* sf_out) {
     minifloat e4m3 = fmt_of(ORQ_E4M3FN), e2m1 = fmt_of(ORQ_E2M1);
     const double e4m3_max = mag_value(&e4m3, e4m3.max_mag); /* 448 */
     const double e2m1_max = mag_value(&e2m1, e2m1.max_mag); /* 6 */
@@ -349,7 +376,7 @@ int oracle_rmsnorm_fp4q(int64_t rows, int64_t hidden, int in_dt,
         const char* xr = (const char*)x + (size_t)r * hidden * esz;
         const char* rr = residual ? (const char*)residual + (size_t)r * hidden * esz : NULL;
         char* ro = residual ? (char*)residual_out + (size_t)r * hidden * esz : NULL;
-        norm_row(hidden, in_dt, xr, rr, ro, gamma, eps, offset, s, y);
+        norm_row_mode(hidden, in_dt, xr, rr, ro, gamma, eps, offset, round_product, s, y);
         for (int64_t b = 0; b < nblk; b++) {
             double amax = 0.0;
             for (int k = 0; k < block; k++)
@@ -391,7 +418,7 @@ int oracle_rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dt,
                        double global_scale, uint8_t* out, uint8_t* block_scales,
                        double* q_out, double* sf_out) {
     return oracle_rmsnorm_fp4q(rows, hidden, in_dt, x, NULL, NULL, gamma, eps, offset, global_scale, 16,
-                               ORQ_SF_E4M3, out, block_scales, q_out, sf_out);
+                               ORQ_SF_E4M3, 0, out, block_scales, q_out, sf_out);
 }
 
 /* The normalized values y = s * rstd * (gamma + offset) as float64
@@ -399,7 +426,7 @@ int oracle_rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dt,
  * residual is given.  rstd_out (optional): [rows]. */
 int oracle_rmsnorm_y(int64_t rows, int64_t hidden, int in_dt,
                      const void* x, const void* residual, void* residual_out,
-                     const void* gamma, double eps, double offset,
+                     const void* gamma, double eps, double offset, int round_product,
                      double* y_out, double* rstd_out) {
     size_t esz = in_dt == ORQ_F32 ? 4 : 2;
     double* s = (double*)malloc(sizeof(double) * (size_t)hidden);
@@ -408,7 +435,8 @@ int oracle_rmsnorm_y(int64_t rows, int64_t hidden, int in_dt,
         const char* xr = (const char*)x + (size_t)r * hidden * esz;
         const char* rr = residual ? (const char*)residual + (size_t)r * hidden * esz : NULL;
         char* ro = residual ? (char*)residual_out + (size_t)r * hidden * esz : NULL;
-        double rstd = norm_row(hidden, in_dt, xr, rr, ro, gamma, eps, offset, s, y_out + r * hidden);
+        double rstd = norm_row_mode(hidden, in_dt, xr, rr, ro, gamma, eps, offset, round_product, s,
+                                    y_out + r * hidden);
         if (rstd_out) rstd_out[r] = rstd;
     }
     free(s);

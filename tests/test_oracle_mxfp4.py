@@ -233,3 +233,47 @@ def test_fp4_fp32_input_of_bf16_values_matches_bf16(block, fmt):
     b = oracle.rmsnorm_fp4(workloads.bits(xb.float()), workloads.bits(gb.float()), in_dtype="f32", **kw)
     for k in ("packed", "block_scales"):
         assert np.array_equal(a[k], b[k])
+
+
+# ---- the FP4 page's numerics (16-bit x * w), optional ------------------------------
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("row", GOLDEN["fp4_compat_rows"], ids=lambda r: r["id"])
+def test_fp4_compat_hand_row(row, dt):
+    x, g = as_bits([row["x"]], dt), as_bits(row["gamma"], dt)
+    kw = dict(in_dtype=dt, eps=row["eps"], weight_offset=0.0, global_scale=row["global_scale"],
+              block_size=row["block_size"], scale_format=row["scale_format"])
+    exact = oracle.rmsnorm_fp4(x, g, **kw)
+    compat = oracle.rmsnorm_fp4(x, g, round_product=True, **kw)
+    assert hexes(exact["block_scales"][0]) == row["expect_block_scales"]
+    assert hexes(compat["block_scales"][0]) == row["expect_block_scales"]
+    assert hexes(exact["packed"][0]) == row["expect_packed_exact"]
+    assert hexes(compat["packed"][0]) == row["expect_packed_compat"]
+
+
+@pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0")])
+def test_fp4_compat_equals_exact_when_products_are_exact(block, fmt):
+    """With gamma a power of two every bf16 product x * gamma is a bf16 value,
+    so rounding it changes nothing."""
+    rng = np.random.default_rng(50 + block)
+    x = as_bits(rng.standard_normal((10, 640)).tolist(), "bf16")
+    g = as_bits(np.exp2(rng.integers(-3, 4, 640)).tolist(), "bf16")
+    kw = dict(in_dtype="bf16", eps=1e-6, weight_offset=0.0, global_scale=150.0, block_size=block, scale_format=fmt)
+    a = oracle.rmsnorm_fp4(x, g, **kw)
+    b = oracle.rmsnorm_fp4(x, g, round_product=True, **kw)
+    for k in ("packed", "block_scales", "q"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_fp4_compat_y_is_rounded_product_times_rstd():
+    rng = np.random.default_rng(60)
+    xs, gs = rng.standard_normal((6, 256)), rng.uniform(0.5, 1.5, 256)
+    x, g = as_bits(xs.tolist(), "bf16"), as_bits(gs.tolist(), "bf16")
+    kw = dict(in_dtype="bf16", eps=1e-6, weight_offset=0.0)
+    plain = oracle.rmsnorm_y(x, g, **kw)
+    comp = oracle.rmsnorm_y(x, g, round_product=True, **kw)
+    xv = workloads.from_bits(x, "bf16").to(torch.float64)
+    gv = workloads.from_bits(g, "bf16").to(torch.float64)
+    prod = (xv * gv).to(torch.bfloat16).to(torch.float64).numpy()  # torch: one RNE rounding
+    assert np.array_equal(comp["rstd"], plain["rstd"])
+    assert np.array_equal(comp["y"], prod * comp["rstd"][:, None])
