@@ -114,11 +114,11 @@ class Case:
                     self.keep += [r, ro]
                     self.outs.append(ro)
                     args = (w.rows, w.hidden, dt, P(x), P(r), P(ro), P(g), w.eps, w.weight_offset, P(gst), w.fp4_block,
-                            sfmt, layout, P(out), P(bs), stream)
+                            sfmt, layout, 0, P(out), P(bs), stream)
                     self.calls.append((L.residual_rmsnorm_fp4quant, args))
                 else:
                     args = (w.rows, w.hidden, dt, P(x), P(g), w.eps, w.weight_offset, P(gst), w.fp4_block, sfmt,
-                            layout, P(out), P(bs), stream)
+                            layout, 0, P(out), P(bs), stream)
                     self.calls.append((L.rmsnorm_fp4quant, args))
                 continue
             out = torch.empty((w.rows, w.hidden), dtype=torch.uint8, device=dev)

@@ -28,6 +28,7 @@ F32, F16, BF16 = 0, 1, 2
 E4M3FN, E4M3FNUZ = 0, 1
 SF_E4M3, SF_UE8M0 = 0, 1            # FP4 block-scale formats
 SF_ROW_MAJOR, SF_SWIZZLED = 0, 1    # FP4 block-scale layouts
+FP4_ROUND_PRODUCT = 1               # FP4 flag: the page's 16-bit x * w
 CVT_F32_TO_E4M3FN, CVT_F32_TO_E4M3FNUZ, CVT_F32_TO_E2M1, CVT_F32_TO_BF16, CVT_F32_TO_F16, CVT_E4M3FN_TO_F32 = range(6)
 STATUS = {0: "RMSQ_OK", -1: "RMSQ_ERR_NULL", -2: "RMSQ_ERR_DTYPE", -3: "RMSQ_ERR_SHAPE", -4: "RMSQ_ERR_ALIGN",
           -5: "RMSQ_ERR_VALUE", -6: "RMSQ_ERR_ALIAS", -7: "RMSQ_ERR_UNSUPPORTED", -8: "RMSQ_ERR_LAUNCH"}
@@ -61,8 +62,8 @@ def lib() -> ctypes.CDLL:
     L.rmsnorm_fp8.argtypes = [I64, I64, I, P, P, F, F, F, I, P, I, P, P]
     L.residual_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4.argtypes = [I64, I64, I, P, P, F, F, P, P, P, P]
-    L.rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, F, F, P, I, I, I, P, P, P]
-    L.residual_rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, P, P, F, F, P, I, I, I, P, P, P]
+    L.rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, F, F, P, I, I, I, I, P, P, P]
+    L.residual_rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, P, P, F, F, P, I, I, I, I, P, P, P]
     L.rmsq_fp4_scale_bytes.argtypes = [I64, I64, I, I]
     L.rmsq_fp4_scale_bytes.restype = I64
     L.rmsq_convert.argtypes = [I, P, P, I64, P]
@@ -172,7 +173,8 @@ def fp4_scale_bytes(rows: int, hidden: int, block_size: int = 16, swizzled: bool
 
 
 def rmsnorm_fp4quant(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, block_size=16,
-                     scale_format=None, swizzled=False, out=None, block_scales=None, stream=None):
+                     scale_format=None, swizzled=False, out=None, block_scales=None, stream=None,
+                     round_product=False):
     """RMSNorm + FP4 E2M1 with one scale per block_size (16 or 32) elements
     (C: rmsnorm_fp4quant).
 
@@ -181,6 +183,8 @@ def rmsnorm_fp4quant(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, b
     device tensor, or None for 1.0) is used by E4M3 scales only.
     swizzled: 128 x 4-tile scale layout (a flat uint8 buffer of
     fp4_scale_bytes() bytes) instead of [..., H/block_size] row-major.
+    round_product: the FP4 page's numerics (x * w rounded to the input type
+    before the rstd scaling); exact products otherwise.
     Returns (packed uint8 [..., H/2], block_scales uint8).
     """
     rows, hidden = _rows_hidden(x)
@@ -201,13 +205,14 @@ def rmsnorm_fp4quant(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, b
         raise ValueError("global_scale must be a one-element float32 tensor")
     _check("rmsnorm_fp4quant", lib().rmsnorm_fp4quant(
         rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset, _ptr(global_scale), block_size, sfmt,
-        SF_SWIZZLED if swizzled else SF_ROW_MAJOR, _ptr(_u8(out)), _ptr(_u8(block_scales)), _stream(x, stream)))
+        SF_SWIZZLED if swizzled else SF_ROW_MAJOR, FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)),
+        _ptr(_u8(block_scales)), _stream(x, stream)))
     return out, block_scales
 
 
 def residual_rmsnorm_fp4quant(x, residual, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, block_size=16,
                               scale_format=None, swizzled=False, out=None, block_scales=None, residual_out=None,
-                              stream=None):
+                              stream=None, round_product=False):
     """residual_out = x + residual (rounded once to x's dtype), then
     rmsnorm_fp4quant of residual_out (C: residual_rmsnorm_fp4quant).
     residual_out may be x or residual itself (in-place update).
@@ -234,8 +239,8 @@ def residual_rmsnorm_fp4quant(x, residual, gamma, eps=1e-6, weight_offset=0.0, g
         raise ValueError("global_scale must be a one-element float32 tensor")
     _check("residual_rmsnorm_fp4quant", lib().residual_rmsnorm_fp4quant(
         rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), eps, weight_offset,
-        _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR, _ptr(_u8(out)),
-        _ptr(_u8(block_scales)), _stream(x, stream)))
+        _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR,
+        FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)), _ptr(_u8(block_scales)), _stream(x, stream)))
     return out, block_scales, residual_out
 
 

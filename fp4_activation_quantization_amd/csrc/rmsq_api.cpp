@@ -128,12 +128,13 @@ int vpt_for(int nvec, int waves) {
 
 int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
                void* residual_out, bool resid, const void* gamma, float eps, float weight_offset,
-               const float* global_scale, int block_size, int scale_format, int scale_layout, void* out,
-               void* block_scales, hipStream_t stream) {
+               const float* global_scale, int block_size, int scale_format, int scale_layout, int flags,
+               void* out, void* block_scales, hipStream_t stream) {
     if (!valid_dtype(in_dtype)) return RMSQ_ERR_DTYPE;
     if (scale_format != RMSQ_SF_E4M3 && scale_format != RMSQ_SF_UE8M0) return RMSQ_ERR_DTYPE;
     if (scale_layout != RMSQ_SF_ROW_MAJOR && scale_layout != RMSQ_SF_SWIZZLED) return RMSQ_ERR_DTYPE;
     if (block_size != 16 && block_size != 32) return RMSQ_ERR_VALUE;
+    if (flags & ~RMSQ_FP4_ROUND_PRODUCT) return RMSQ_ERR_VALUE;
     const int64_t esz = elem_size(in_dtype);
     if (rows < 0 || hidden <= 0 || hidden % block_size != 0) return RMSQ_ERR_SHAPE;
     if (!size_ok(rows, hidden, esz)) return RMSQ_ERR_SHAPE;
@@ -184,6 +185,7 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
     a.weight_offset = weight_offset;
     a.sf_swizzled = scale_layout == RMSQ_SF_SWIZZLED ? 1 : 0;
     a.sf_k_tiles = (int32_t)ceil_div(hidden / block_size, 4);
+    a.round_product = (flags & RMSQ_FP4_ROUND_PRODUCT) ? 1 : 0;
     const Fp4Format fmt{block_size, scale_format == RMSQ_SF_UE8M0};
     return launched(launch_fp4(a, in_dtype, resid, fmt, shape, stream));
 }
@@ -286,24 +288,24 @@ int64_t rmsq_fp4_scale_bytes(int64_t rows, int64_t hidden, int block_size, int s
 
 int rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
                      float weight_offset, const float* global_scale, int block_size, int scale_format,
-                     int scale_layout, void* out, void* block_scales, hipStream_t stream) {
+                     int scale_layout, int flags, void* out, void* block_scales, hipStream_t stream) {
     return fp4_common(rows, hidden, in_dtype, x, nullptr, nullptr, false, gamma, eps, weight_offset, global_scale,
-                      block_size, scale_format, scale_layout, out, block_scales, stream);
+                      block_size, scale_format, scale_layout, flags, out, block_scales, stream);
 }
 
 int residual_rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
                               void* residual_out, const void* gamma, float eps, float weight_offset,
                               const float* global_scale, int block_size, int scale_format, int scale_layout,
-                              void* out, void* block_scales, hipStream_t stream) {
+                              int flags, void* out, void* block_scales, hipStream_t stream) {
     return fp4_common(rows, hidden, in_dtype, x, residual, residual_out, true, gamma, eps, weight_offset,
-                      global_scale, block_size, scale_format, scale_layout, out, block_scales, stream);
+                      global_scale, block_size, scale_format, scale_layout, flags, out, block_scales, stream);
 }
 
 int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
                 float weight_offset, const float* global_scale, void* out, void* block_scales,
                 hipStream_t stream) {
     return rmsnorm_fp4quant(rows, hidden, in_dtype, x, gamma, eps, weight_offset, global_scale, 16, RMSQ_SF_E4M3,
-                            RMSQ_SF_ROW_MAJOR, out, block_scales, stream);
+                            RMSQ_SF_ROW_MAJOR, 0, out, block_scales, stream);
 }
 
 int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream) {

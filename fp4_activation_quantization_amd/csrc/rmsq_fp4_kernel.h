@@ -55,6 +55,7 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
     const int64_t row_bytes = (int64_t)a.hidden * V::BYTES;
     const int nblk = a.hidden / BLOCK;
     const bool swz = a.sf_swizzled != 0;
+    const bool round_prod = a.round_product != 0;
     const int64_t m_tile_bytes = (int64_t)a.sf_k_tiles * 512;
     auto live = [&](int k) { return EXACT || lt + k * T < nvec; };
 
@@ -185,6 +186,9 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
                 V::unpack(sv[k], t);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) t[e] *= g[k][e];
+                // the page's numerics (optional, uniform): its kernel forms
+                // x * w as a 16-bit product, i.e. s * g' rounded once
+                if (round_prod) V::unpack(V::pack(t), t);
                 // all lanes take part in the swaps (vectors past the row are
                 // zero, and a block's lanes are all live or all past the row)
                 const float amax = block_max_nonneg<LPB>(abs_max<EPV>(0.0f, t));

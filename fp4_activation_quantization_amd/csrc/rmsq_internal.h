@@ -28,6 +28,7 @@ struct FusedArgs {
     int32_t waves;             // wavefronts per row (set by the launcher)
     int32_t sf_swizzled;       // FP4: 1 for the 128x4-tile scale layout
     int32_t sf_k_tiles;        // FP4 swizzled: ceil((hidden / block) / 4)
+    int32_t round_product;     // FP4: round s * g' to the input type (page numerics)
 };
 
 // FP4 variant: elements per block scale and the scale format.

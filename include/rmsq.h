@@ -132,9 +132,10 @@ int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype,
                 float eps, float weight_offset, const float* global_scale,
                 void* out, void* block_scales, hipStream_t stream);
 
-/* FP4 block-scale formats and layouts (rmsnorm_fp4quant). */
+/* FP4 block-scale formats and layouts, and option flags (rmsnorm_fp4quant). */
 enum { RMSQ_SF_E4M3 = 0, RMSQ_SF_UE8M0 = 1 };
 enum { RMSQ_SF_ROW_MAJOR = 0, RMSQ_SF_SWIZZLED = 1 };
+enum { RMSQ_FP4_ROUND_PRODUCT = 1 };
 
 /*
  * rmsnorm_fp4quant -- the general form of rmsnorm_fp4, with the options of
@@ -158,15 +159,20 @@ enum { RMSQ_SF_ROW_MAJOR = 0, RMSQ_SF_SWIZZLED = 1 };
  *                    + ((row%128)/32) * 4 + j%4,   K = ceil((hidden/block)/4),
  *                  in a buffer of rmsq_fp4_scale_bytes() bytes; bytes of the
  *                  tiles' padding rows and columns are not written.
+ *   flags        : 0, or RMSQ_FP4_ROUND_PRODUCT -- the page's numerics: its
+ *                  kernel multiplies x and w as 16-bit pairs, so s * g' is
+ *                  rounded once to in_dtype (RNE) before the rstd scaling.
+ *                  Without it the product is exact.  Other bits:
+ *                  RMSQ_ERR_VALUE.
  *   Other arguments, the code layout and the errors are as rmsnorm_fp4;
  *   RMSQ_ERR_DTYPE for an unknown scale_format or scale_layout.
  * rmsnorm_fp4(...) == rmsnorm_fp4quant(..., 16, RMSQ_SF_E4M3,
- * RMSQ_SF_ROW_MAJOR, ...).
+ * RMSQ_SF_ROW_MAJOR, 0, ...).
  */
 int rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype,
                      const void* x, const void* gamma,
                      float eps, float weight_offset, const float* global_scale,
-                     int block_size, int scale_format, int scale_layout,
+                     int block_size, int scale_format, int scale_layout, int flags,
                      void* out, void* block_scales, hipStream_t stream);
 
 /*
@@ -185,7 +191,7 @@ int residual_rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype,
                               const void* x, const void* residual, void* residual_out,
                               const void* gamma, float eps, float weight_offset,
                               const float* global_scale, int block_size, int scale_format,
-                              int scale_layout, void* out, void* block_scales,
+                              int scale_layout, int flags, void* out, void* block_scales,
                               hipStream_t stream);
 
 /* Bytes of the block_scales buffer rmsnorm_fp4quant writes into for this

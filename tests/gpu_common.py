@@ -66,7 +66,7 @@ def oracle_fp8(w, inp, *, rows_idx=None, ub=None, out_fmt=None, scales_dtype=Non
     kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset if weight_offset is None else weight_offset)
     ref = oracle.rmsnorm_fp8(x, g, scale_ub=w.scale_ub if ub is None else ub, out_fmt=out_fmt or w.out_fmt,
                              scales_dtype=scales_dtype or w.scales_dtype, residual=r, **kw)
-    y = oracle.rmsnorm_y(x, g, residual=r, **kw)["y"]
+    y = oracle.rmsnorm_y(x, g, residual=r, round_product=w.fp4_round_product, **kw)["y"]
     return ref, y
 
 
@@ -97,11 +97,11 @@ def run_fp4(w, inp, gs, *, rows_idx=None, weight_offset=None, stream=None):
         bs = torch.full((rq.fp4_scale_bytes(rows, hidden, w.fp4_block, True),), CANARY, dtype=torch.uint8,
                         device=DEV)
     kw = dict(eps=w.eps, weight_offset=off, global_scale=gst, block_size=w.fp4_block, scale_format=w.fp4_scale,
-              swizzled=w.fp4_swizzled, block_scales=bs, stream=stream)
+              swizzled=w.fp4_swizzled, block_scales=bs, stream=stream, round_product=w.fp4_round_product)
     ro = None
     if w.residual:
         packed, bs, ro = rq.residual_rmsnorm_fp4quant(x, to_dev(inp["residual"]), g, **kw)
-    elif w.fp4_block == 16 and w.fp4_scale == "e4m3" and not w.fp4_swizzled:
+    elif w.fp4_block == 16 and w.fp4_scale == "e4m3" and not w.fp4_swizzled and not w.fp4_round_product:
         packed, bs = rq.rmsnorm_fp4(x, g, eps=w.eps, weight_offset=off, global_scale=gst, stream=stream)
     else:
         packed, bs = rq.rmsnorm_fp4quant(x, g, **kw)
@@ -128,10 +128,10 @@ def check_fp4(w, inp, gs, *, rows_idx=None, label="", weight_offset=None):
     kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=off)
     gsv = 1.0 if gs is None else gs
     ref = oracle.rmsnorm_fp4(x, g, global_scale=gsv, block_size=w.fp4_block, scale_format=w.fp4_scale, residual=r,
-                             **kw)
+                             round_product=w.fp4_round_product, **kw)
     if r is not None:
         assert np.array_equal(ro, ref["residual_out"]), "residual_out differs from the oracle's"
-    y = oracle.rmsnorm_y(x, g, residual=r, **kw)["y"]
+    y = oracle.rmsnorm_y(x, g, residual=r, round_product=w.fp4_round_product, **kw)["y"]
     rep = compare_fp4(p, bs, ref, y, global_scale=gsv, block_size=w.fp4_block, scale_format=w.fp4_scale)
     say(f"  parity {label or w.name}: {rep}")
     return rep

@@ -190,13 +190,13 @@ def test_fp4_errors():
     assert fp4(gs=ctypes.c_void_p(BASE + 3 * MB)) == ALIAS
 
 
-def fp4q(rows=4, hidden=4096, block=16, sfmt=None, layout=None, gs=None, out=None, bs=None):
+def fp4q(rows=4, hidden=4096, block=16, sfmt=None, layout=None, gs=None, out=None, bs=None, flags=0):
     sfmt = rq.SF_E4M3 if sfmt is None else sfmt
     layout = rq.SF_ROW_MAJOR if layout is None else layout
     out = P(2) if out is None else out
     bs = P(3) if bs is None else bs
-    return rq.lib().rmsnorm_fp4quant(rows, hidden, rq.BF16, P(0), P(1), 1e-6, 0.0, gs, block, sfmt, layout, out, bs,
-                                     None)
+    return rq.lib().rmsnorm_fp4quant(rows, hidden, rq.BF16, P(0), P(1), 1e-6, 0.0, gs, block, sfmt, layout, flags,
+                                     out, bs, None)
 
 
 def test_fp4quant_errors():
@@ -205,6 +205,8 @@ def test_fp4quant_errors():
     assert fp4q(sfmt=2) == DTYPE
     assert fp4q(layout=2) == DTYPE
     assert fp4q(hidden=48, block=32) == SHAPE
+    assert fp4q(flags=2) == VALUE and fp4q(flags=-1) == VALUE
+    assert fp4q(flags=rq.FP4_ROUND_PRODUCT) == UNSUP
     for block in (16, 32):
         for sfmt in (rq.SF_E4M3, rq.SF_UE8M0):
             for layout in (rq.SF_ROW_MAJOR, rq.SF_SWIZZLED):
@@ -228,7 +230,7 @@ def rfp4q(x=None, r=None, ro=None, g=None, out=None, bs=None, dt=rq.BF16, hidden
     out = P(2) if out is None else out
     bs = P(3) if bs is None else bs
     return rq.lib().residual_rmsnorm_fp4quant(4, hidden, dt, x, r, ro, g, 1e-6, 0.0, gs, 16, rq.SF_E4M3,
-                                              rq.SF_ROW_MAJOR, out, bs, None)
+                                              rq.SF_ROW_MAJOR, 0, out, bs, None)
 
 
 def test_residual_fp4quant_errors():

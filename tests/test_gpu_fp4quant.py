@@ -51,10 +51,10 @@ def _inputs(rows, hidden, dt, seed, resid=False):
             "gamma": torch.from_numpy(rng.uniform(0.8, 1.2, hidden)).to(TD[dt])}
 
 
-def _wl(rows, hidden, dt, block, fmt, swz, offset=0.0, resid=False):
+def _wl(rows, hidden, dt, block, fmt, swz, offset=0.0, resid=False, round_product=False):
     op = "residual_rmsnorm_fp4" if resid else "rmsnorm_fp4"
     return workloads.Workload("fp4quant", op, rows, hidden, dt, 98, eps=1e-6, weight_offset=offset,
-                              fp4_block=block, fp4_scale=fmt, fp4_swizzled=swz)
+                              fp4_block=block, fp4_scale=fmt, fp4_swizzled=swz, fp4_round_product=round_product)
 
 
 def _gs(inp, w):
@@ -153,6 +153,34 @@ def test_forced_launch_shapes_f32(block, resid):
         say(f"[fp4quant f32 shape] block={block} resid={resid} waves={waves} vpt={vpt}")
         check_fp4(w, inp, gs, label=f"f32 block{block} resid={resid} {waves}x{vpt}")
     rq.set_tuning(0, 0, 0)
+
+
+@pytest.mark.parametrize("resid", [False, True])
+@pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0")])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_round_product_mode(dt, block, fmt, resid):
+    """The page's numerics (x * w rounded to the input type) against the
+    oracle's same mode."""
+    for rows, hidden in ((150, 2080), (64, 7168)):
+        w = _wl(rows, hidden, dt, block, fmt, False, resid=resid, round_product=True)
+        inp = _inputs(rows, hidden, dt, seed=rows + block + 7, resid=resid)
+        say(f"[fp4quant round_product] {dt} block={block} {fmt} resid={resid} {rows}x{hidden}")
+        check_fp4(w, inp, _gs(inp, w), label=f"round_product {dt} {block} {fmt} resid={resid}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("row", GOLDEN["fp4_compat_rows"], ids=lambda r: r["id"])
+def test_round_product_hand_row(row, dt):
+    n = len(row["x"])
+    x = torch.tensor([row["x"]], dtype=torch.float64).to(TD[dt]).to(DEV)
+    g = torch.tensor(row["gamma"], dtype=torch.float64).to(TD[dt]).to(DEV)
+    say(f"[fp4quant round_product hand row] {row['id']} {dt}")
+    for rp, key in ((False, "expect_packed_exact"), (True, "expect_packed_compat")):
+        packed, bs = rq.rmsnorm_fp4quant(x, g, eps=row["eps"], block_size=row["block_size"],
+                                         scale_format=row["scale_format"], round_product=rp)
+        torch.cuda.synchronize()
+        assert [f"0x{v:02X}" for v in bs.cpu().numpy()[0]] == row["expect_block_scales"]
+        assert [f"0x{v:02X}" for v in packed.cpu().numpy()[0]] == row[key], (rp, key)
 
 
 def test_weight_offset_and_f16_block32():

@@ -54,6 +54,7 @@ class Workload:
     fp4_block: int = 16              # FP4 only: elements per block scale (16 or 32)
     fp4_scale: str = "e4m3"          # FP4 only: "e4m3" or "ue8m0" block scales
     fp4_swizzled: bool = False       # FP4 only: 128 x 4-tile scale layout
+    fp4_round_product: bool = False  # FP4 only: the page's 16-bit x * w numerics
 
     @property
     def residual(self) -> bool:
