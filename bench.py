@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 CACHE_DEFEAT_BYTES = 1 << 30
 STREAM_MIN_BYTES = 16 << 20  # smaller workloads are latency-bound: no bandwidth reference
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["rmsq_fp8.hip", "rmsq_fp4.hip", "rmsq_fp4_kernel.h", "rmsq_device.h", "rmsq_api.cpp"]
+KERNEL_SOURCES = ["rmsq_fp8_kernel.h", "rmsq_fp4_kernel.h", "rmsq_device.h", "rmsq_api.cpp"]
 SC_T = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.residual_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4.argtypes = [I64, I64, I, P, P, F, F, P, P, P, P]
     L.rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, F, F, P, I, I, I, I, P, P, P]
+    L.rmsnorm_fp8_strided.argtypes = [I64, I64, I, P, I64, P, I64, P, I64, P, F, F, F, I, P, I64, I, P, P]
+    L.rmsnorm_fp4quant_strided.argtypes = [I64, I64, I, P, I64, P, I64, P, I64, P, F, F, P, I, I, I, I, P, I64, P, P]
     L.residual_rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, P, P, F, F, P, I, I, I, I, P, P, P]
     L.rmsq_fp4_scale_bytes.argtypes = [I64, I64, I, I]
     L.rmsq_fp4_scale_bytes.restype = I64
@@ -73,7 +75,7 @@ def lib() -> ctypes.CDLL:
     L.rmsq_status_string.argtypes = [I]
     L.rmsq_status_string.restype = ctypes.c_char_p
     for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant",
-               "residual_rmsnorm_fp4quant", "rmsq_convert",
+               "residual_rmsnorm_fp4quant", "rmsnorm_fp8_strided", "rmsnorm_fp4quant_strided", "rmsq_convert",
                "rmsq_stream_probe",
                "rmsq_set_tuning",
                "rmsq_query_shape", "rmsq_abi_version", "rmsq_last_hip_error"):
@@ -241,6 +243,87 @@ def residual_rmsnorm_fp4quant(x, residual, gamma, eps=1e-6, weight_offset=0.0, g
         rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), eps, weight_offset,
         _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR,
         FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)), _ptr(_u8(block_scales)), _stream(x, stream)))
+    return out, block_scales, residual_out
+
+
+def _row_view(t: torch.Tensor, name: str):
+    """(rows, row stride in elements) of a tensor whose last dim is
+    contiguous and whose leading dims collapse to one row stride."""
+    if t.dim() == 0 or t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    try:
+        v = t.view(-1, t.shape[-1])
+    except RuntimeError as e:
+        raise ValueError(f"{name}: leading dimensions must collapse to one row stride") from e
+    return v.shape[0], (v.stride(0) if v.shape[0] > 1 else t.shape[-1])
+
+
+def rmsnorm_fp8_strided(x, gamma, residual=None, eps=1e-6, weight_offset=0.0, scale_ub=float("inf"),
+                        out_fp8="e4m3fn", out=None, scales=None, residual_out=None, scales_dtype=torch.float32,
+                        stream=None):
+    """rmsnorm_fp8 / residual_rmsnorm_fp8 on row-strided tensors (C:
+    rmsnorm_fp8_strided): x, residual, residual_out and out may be views
+    whose rows are not adjacent (e.g. x = buf[:, :hidden]).  Outputs are
+    allocated contiguous when not given.  Returns (codes, scales,
+    residual_out or None)."""
+    rows, xs = _row_view(x, "x")
+    hidden = x.shape[-1]
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=scales_dtype, device=x.device)
+    rs = ros = hidden
+    if residual is not None:
+        if residual.dtype != x.dtype or residual.shape != x.shape:
+            raise ValueError("residual must match x in dtype and shape")
+        if residual_out is None:
+            residual_out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+        _, rs = _row_view(residual, "residual")
+        _, ros = _row_view(residual_out, "residual_out")
+    _, os_ = _row_view(_u8(out), "out")
+    _check("rmsnorm_fp8_strided", lib().rmsnorm_fp8_strided(
+        rows, hidden, _DT[x.dtype], _ptr(x), xs, _ptr(residual), rs, _ptr(residual_out), ros, _ptr(gamma), eps,
+        weight_offset, scale_ub, _FMT[out_fp8], _ptr(_u8(out)), os_, _DT[scales.dtype], _ptr(scales),
+        _stream(x, stream)))
+    return out, scales, residual_out
+
+
+def rmsnorm_fp4quant_strided(x, gamma, residual=None, eps=1e-6, weight_offset=0.0, global_scale=None,
+                             block_size=16, scale_format=None, swizzled=False, round_product=False, out=None,
+                             block_scales=None, residual_out=None, stream=None):
+    """rmsnorm_fp4quant / residual_rmsnorm_fp4quant on row-strided tensors
+    (C: rmsnorm_fp4quant_strided).  Returns (packed, block_scales,
+    residual_out or None)."""
+    rows, xs = _row_view(x, "x")
+    hidden = x.shape[-1]
+    if scale_format is None:
+        scale_format = "ue8m0" if block_size == 32 else "e4m3"
+    sfmt = {"e4m3": SF_E4M3, "ue8m0": SF_UE8M0}[scale_format]
+    if out is None:
+        out = torch.empty((*x.shape[:-1], hidden // 2), dtype=torch.uint8, device=x.device)
+    if block_scales is None:
+        block_scales = (torch.empty((fp4_scale_bytes(rows, hidden, block_size, True),), dtype=torch.uint8,
+                                    device=x.device) if swizzled else
+                        torch.empty((*x.shape[:-1], hidden // block_size), dtype=torch.uint8, device=x.device))
+    elif not block_scales.is_contiguous() or \
+            block_scales.numel() * block_scales.element_size() < fp4_scale_bytes(rows, hidden, block_size, swizzled):
+        raise ValueError("block_scales must be contiguous and hold fp4_scale_bytes() bytes")
+    if global_scale is not None and (global_scale.dtype != torch.float32 or global_scale.numel() != 1):
+        raise ValueError("global_scale must be a one-element float32 tensor")
+    rs = ros = hidden
+    if residual is not None:
+        if residual.dtype != x.dtype or residual.shape != x.shape:
+            raise ValueError("residual must match x in dtype and shape")
+        if residual_out is None:
+            residual_out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+        _, rs = _row_view(residual, "residual")
+        _, ros = _row_view(residual_out, "residual_out")
+    _, os_ = _row_view(_u8(out), "out")
+    _check("rmsnorm_fp4quant_strided", lib().rmsnorm_fp4quant_strided(
+        rows, hidden, _DT[x.dtype], _ptr(x), xs, _ptr(residual), rs, _ptr(residual_out), ros, _ptr(gamma), eps,
+        weight_offset, _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR,
+        FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)), os_, _ptr(_u8(block_scales)),
+        _stream(x, stream)))
     return out, block_scales, residual_out
 
 

@@ -38,6 +38,17 @@ struct Span {
 };
 bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Bytes from the first element of a row tensor to past its last one.
+int64_t extent(int64_t rows, int64_t row_bytes, int64_t stride_bytes) {
+    return rows == 0 ? 0 : (rows - 1) * stride_bytes + row_bytes;
+}
+
+// A row stride (elements of esz bytes) is valid when it holds the row and
+// keeps every row start on a `quantum`-byte boundary.
+bool stride_ok(int64_t stride, int64_t row_elems, int64_t esz, int64_t quantum) {
+    return stride >= row_elems && stride <= INT32_MAX && (stride * esz) % quantum == 0;
+}
+
 // rows * hidden * esz must fit comfortably in int64 (and hidden in int32)
 bool size_ok(int64_t rows, int64_t hidden, int64_t esz) {
     if (hidden > INT32_MAX / 2) return false;
@@ -59,16 +70,21 @@ int launched(hipError_t e) {
     return RMSQ_OK;
 }
 
-int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
-               void* residual_out, bool resid, const void* gamma, float eps, float weight_offset,
-               float scale_ub, int out_fp8, void* out, int scales_dtype, void* scales, hipStream_t stream) {
+int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_t x_stride, const void* residual,
+               int64_t r_stride, void* residual_out, int64_t ro_stride, bool resid, const void* gamma, float eps,
+               float weight_offset, float scale_ub, int out_fp8, void* out, int64_t out_stride, int scales_dtype,
+               void* scales, hipStream_t stream) {
     if (!valid_dtype(in_dtype) || !valid_dtype(scales_dtype)) return RMSQ_ERR_DTYPE;
     if (out_fp8 != RMSQ_E4M3FN && out_fp8 != RMSQ_E4M3FNUZ) return RMSQ_ERR_DTYPE;
-    const int64_t esz = elem_size(in_dtype);
-    if (rows < 0 || hidden <= 0 || hidden % elems_per_vec(in_dtype) != 0) return RMSQ_ERR_SHAPE;
-    if (!size_ok(rows, hidden, esz)) return RMSQ_ERR_SHAPE;
+    const int64_t esz = elem_size(in_dtype), epv = elems_per_vec(in_dtype);
+    if (rows < 0 || hidden <= 0 || hidden % epv != 0) return RMSQ_ERR_SHAPE;
+    if (!stride_ok(x_stride, hidden, esz, 16) || !stride_ok(out_stride, hidden, 1, epv)) return RMSQ_ERR_SHAPE;
+    if (resid && (!stride_ok(r_stride, hidden, esz, 16) || !stride_ok(ro_stride, hidden, esz, 16)))
+        return RMSQ_ERR_SHAPE;
+    const int64_t widest = std::max({x_stride, out_stride / esz + 1, resid ? std::max(r_stride, ro_stride) : 0});
+    if (!size_ok(rows, widest, esz)) return RMSQ_ERR_SHAPE;
     if (int rc = check_scalars(eps, weight_offset, scale_ub, true)) return rc;
-    const int nvec = (int)(hidden / elems_per_vec(in_dtype));
+    const int nvec = (int)(hidden / epv);
     if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
     if (rows == 0) return RMSQ_OK;
     if (!x || !gamma || !out || !scales) return RMSQ_ERR_NULL;
@@ -78,18 +94,23 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
         return RMSQ_ERR_ALIGN;
     if (resid && (!aligned(residual, 16) || !aligned(residual_out, 16))) return RMSQ_ERR_ALIGN;
 
-    const int64_t tbytes = rows * hidden * esz;
-    const Span sx(x, tbytes), sg(gamma, hidden * esz), so(out, rows * hidden), ss(scales, rows * ssz);
+    // spans cover every row; strided tensors are compared by their extents
+    const int64_t rb = hidden * esz;
+    const Span sx(x, extent(rows, rb, x_stride * esz)), sg(gamma, rb), so(out, extent(rows, hidden, out_stride)),
+        ss(scales, rows * ssz);
     // outputs never overlap inputs or each other ...
     if (overlap(so, ss) || overlap(so, sx) || overlap(so, sg) || overlap(ss, sx) || overlap(ss, sg))
         return RMSQ_ERR_ALIAS;
     if (resid) {
-        const Span sr(residual, tbytes), sro(residual_out, tbytes);
+        const Span sr(residual, extent(rows, rb, r_stride * esz)), sro(residual_out, extent(rows, rb, ro_stride * esz));
         if (overlap(so, sr) || overlap(ss, sr) || overlap(sro, so) || overlap(sro, ss) || overlap(sro, sg))
             return RMSQ_ERR_ALIAS;
         // ... except an in-place residual update at exactly the same address
-        if (residual_out != x && overlap(sro, sx)) return RMSQ_ERR_ALIAS;
-        if (residual_out != residual && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
+        // and row stride
+        const bool on_x = residual_out == x && ro_stride == x_stride;
+        const bool on_r = residual_out == residual && ro_stride == r_stride;
+        if (!on_x && overlap(sro, sx)) return RMSQ_ERR_ALIAS;
+        if (!on_r && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
     }
 
     Shape shape;
@@ -110,6 +131,10 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
     a.weight_offset = weight_offset;
     a.scale_ub = scale_ub;
     a.scales_dtype = scales_dtype;
+    a.x_stride = x_stride * esz;
+    a.residual_stride = r_stride * esz;
+    a.residual_out_stride = ro_stride * esz;
+    a.out_stride = out_stride;
     return launched(launch_fp8(a, in_dtype, resid, out_fp8, shape, stream));
 }
 
@@ -126,10 +151,10 @@ int vpt_for(int nvec, int waves) {
     return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 0;
 }
 
-int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
-               void* residual_out, bool resid, const void* gamma, float eps, float weight_offset,
-               const float* global_scale, int block_size, int scale_format, int scale_layout, int flags,
-               void* out, void* block_scales, hipStream_t stream) {
+int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_t x_stride, const void* residual,
+               int64_t r_stride, void* residual_out, int64_t ro_stride, bool resid, const void* gamma, float eps,
+               float weight_offset, const float* global_scale, int block_size, int scale_format, int scale_layout,
+               int flags, void* out, int64_t out_stride, void* block_scales, hipStream_t stream) {
     if (!valid_dtype(in_dtype)) return RMSQ_ERR_DTYPE;
     if (scale_format != RMSQ_SF_E4M3 && scale_format != RMSQ_SF_UE8M0) return RMSQ_ERR_DTYPE;
     if (scale_layout != RMSQ_SF_ROW_MAJOR && scale_layout != RMSQ_SF_SWIZZLED) return RMSQ_ERR_DTYPE;
@@ -137,7 +162,12 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
     if (flags & ~RMSQ_FP4_ROUND_PRODUCT) return RMSQ_ERR_VALUE;
     const int64_t esz = elem_size(in_dtype);
     if (rows < 0 || hidden <= 0 || hidden % block_size != 0) return RMSQ_ERR_SHAPE;
-    if (!size_ok(rows, hidden, esz)) return RMSQ_ERR_SHAPE;
+    // code rows: hidden / 2 bytes, stored 2 or 4 bytes per lane -> 8-byte row starts
+    if (!stride_ok(x_stride, hidden, esz, 16) || !stride_ok(out_stride, hidden / 2, 1, 8)) return RMSQ_ERR_SHAPE;
+    if (resid && (!stride_ok(r_stride, hidden, esz, 16) || !stride_ok(ro_stride, hidden, esz, 16)))
+        return RMSQ_ERR_SHAPE;
+    const int64_t widest = std::max({x_stride, out_stride / esz + 1, resid ? std::max(r_stride, ro_stride) : 0});
+    if (!size_ok(rows, widest, esz)) return RMSQ_ERR_SHAPE;
     if (int rc = check_scalars(eps, weight_offset, 1.0f, false)) return rc;
     const int nvec = (int)(hidden / elems_per_vec(in_dtype));
     if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
@@ -149,23 +179,28 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
     // the global scale is read only for E4M3 scales
     const float* gsp = scale_format == RMSQ_SF_E4M3 ? global_scale : nullptr;
     if (gsp && !aligned(gsp, 4)) return RMSQ_ERR_ALIGN;
-    const int64_t tbytes = rows * hidden * esz;
+    const int64_t rb = hidden * esz;
     const int64_t sbytes = rmsq_fp4_scale_bytes(rows, hidden, block_size, scale_layout);
-    const Span sx(x, tbytes), sg(gamma, hidden * esz), so(out, rows * hidden / 2), ss(block_scales, sbytes);
+    const Span sx(x, extent(rows, rb, x_stride * esz)), sg(gamma, rb), so(out, extent(rows, hidden / 2, out_stride)),
+        ss(block_scales, sbytes);
     if (overlap(so, ss) || overlap(so, sx) || overlap(so, sg) || overlap(ss, sx) || overlap(ss, sg))
         return RMSQ_ERR_ALIAS;
+    const Span sro(residual_out, resid ? extent(rows, rb, ro_stride * esz) : 0);
     if (gsp) {
         const Span sgs(gsp, 4);
         if (overlap(sgs, so) || overlap(sgs, ss)) return RMSQ_ERR_ALIAS;
-        if (resid && overlap(sgs, Span(residual_out, tbytes))) return RMSQ_ERR_ALIAS;
+        if (resid && overlap(sgs, sro)) return RMSQ_ERR_ALIAS;
     }
     if (resid) {
-        const Span sr(residual, tbytes), sro(residual_out, tbytes);
+        const Span sr(residual, extent(rows, rb, r_stride * esz));
         if (overlap(so, sr) || overlap(ss, sr) || overlap(sro, so) || overlap(sro, ss) || overlap(sro, sg))
             return RMSQ_ERR_ALIAS;
-        // an in-place residual update at exactly the same address is allowed
-        if (residual_out != x && overlap(sro, sx)) return RMSQ_ERR_ALIAS;
-        if (residual_out != residual && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
+        // an in-place residual update at exactly the same address and row
+        // stride is allowed
+        const bool on_x = residual_out == x && ro_stride == x_stride;
+        const bool on_r = residual_out == residual && ro_stride == r_stride;
+        if (!on_x && overlap(sro, sx)) return RMSQ_ERR_ALIAS;
+        if (!on_r && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
     }
     Shape shape;
     if (!choose_shape(rows, nvec, resid ? kPathFp4Residual : kPathFp4, &shape)) return RMSQ_ERR_UNSUPPORTED;
@@ -186,6 +221,10 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, const 
     a.sf_swizzled = scale_layout == RMSQ_SF_SWIZZLED ? 1 : 0;
     a.sf_k_tiles = (int32_t)ceil_div(hidden / block_size, 4);
     a.round_product = (flags & RMSQ_FP4_ROUND_PRODUCT) ? 1 : 0;
+    a.x_stride = x_stride * esz;
+    a.residual_stride = r_stride * esz;
+    a.residual_out_stride = ro_stride * esz;
+    a.out_stride = out_stride;
     const Fp4Format fmt{block_size, scale_format == RMSQ_SF_UE8M0};
     return launched(launch_fp4(a, in_dtype, resid, fmt, shape, stream));
 }
@@ -266,15 +305,25 @@ extern "C" {
 int rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
                 float weight_offset, float scale_ub, int out_fp8, void* out, int scales_dtype, void* scales,
                 hipStream_t stream) {
-    return fp8_common(rows, hidden, in_dtype, x, nullptr, nullptr, false, gamma, eps, weight_offset, scale_ub,
-                      out_fp8, out, scales_dtype, scales, stream);
+    return fp8_common(rows, hidden, in_dtype, x, hidden, nullptr, hidden, nullptr, hidden, false, gamma, eps,
+                      weight_offset, scale_ub, out_fp8, out, hidden, scales_dtype, scales, stream);
 }
 
 int residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
                          void* residual_out, const void* gamma, float eps, float weight_offset, float scale_ub,
                          int out_fp8, void* out, int scales_dtype, void* scales, hipStream_t stream) {
-    return fp8_common(rows, hidden, in_dtype, x, residual, residual_out, true, gamma, eps, weight_offset,
-                      scale_ub, out_fp8, out, scales_dtype, scales, stream);
+    return fp8_common(rows, hidden, in_dtype, x, hidden, residual, hidden, residual_out, hidden, true, gamma, eps,
+                      weight_offset, scale_ub, out_fp8, out, hidden, scales_dtype, scales, stream);
+}
+
+int rmsnorm_fp8_strided(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_t x_stride,
+                        const void* residual, int64_t residual_stride, void* residual_out,
+                        int64_t residual_out_stride, const void* gamma, float eps, float weight_offset,
+                        float scale_ub, int out_fp8, void* out, int64_t out_stride, int scales_dtype, void* scales,
+                        hipStream_t stream) {
+    return fp8_common(rows, hidden, in_dtype, x, x_stride, residual, residual_stride, residual_out,
+                      residual_out_stride, residual != nullptr, gamma, eps, weight_offset, scale_ub, out_fp8, out,
+                      out_stride, scales_dtype, scales, stream);
 }
 
 int64_t rmsq_fp4_scale_bytes(int64_t rows, int64_t hidden, int block_size, int scale_layout) {
@@ -289,16 +338,28 @@ int64_t rmsq_fp4_scale_bytes(int64_t rows, int64_t hidden, int block_size, int s
 int rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,
                      float weight_offset, const float* global_scale, int block_size, int scale_format,
                      int scale_layout, int flags, void* out, void* block_scales, hipStream_t stream) {
-    return fp4_common(rows, hidden, in_dtype, x, nullptr, nullptr, false, gamma, eps, weight_offset, global_scale,
-                      block_size, scale_format, scale_layout, flags, out, block_scales, stream);
+    return fp4_common(rows, hidden, in_dtype, x, hidden, nullptr, hidden, nullptr, hidden, false, gamma, eps,
+                      weight_offset, global_scale, block_size, scale_format, scale_layout, flags, out, hidden / 2,
+                      block_scales, stream);
 }
 
 int residual_rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* residual,
                               void* residual_out, const void* gamma, float eps, float weight_offset,
                               const float* global_scale, int block_size, int scale_format, int scale_layout,
                               int flags, void* out, void* block_scales, hipStream_t stream) {
-    return fp4_common(rows, hidden, in_dtype, x, residual, residual_out, true, gamma, eps, weight_offset,
-                      global_scale, block_size, scale_format, scale_layout, flags, out, block_scales, stream);
+    return fp4_common(rows, hidden, in_dtype, x, hidden, residual, hidden, residual_out, hidden, true, gamma, eps,
+                      weight_offset, global_scale, block_size, scale_format, scale_layout, flags, out, hidden / 2,
+                      block_scales, stream);
+}
+
+int rmsnorm_fp4quant_strided(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_t x_stride,
+                             const void* residual, int64_t residual_stride, void* residual_out,
+                             int64_t residual_out_stride, const void* gamma, float eps, float weight_offset,
+                             const float* global_scale, int block_size, int scale_format, int scale_layout, int flags,
+                             void* out, int64_t out_stride, void* block_scales, hipStream_t stream) {
+    return fp4_common(rows, hidden, in_dtype, x, x_stride, residual, residual_stride, residual_out,
+                      residual_out_stride, residual != nullptr, gamma, eps, weight_offset, global_scale, block_size,
+                      scale_format, scale_layout, flags, out, out_stride, block_scales, stream);
 }
 
 int rmsnorm_fp4(int64_t rows, int64_t hidden, int in_dtype, const void* x, const void* gamma, float eps,

@@ -52,7 +52,6 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
     const int lt = tid - slot * T;
     const int red = slot * waves + (lt >> 6);
     const int nvec = a.nvec;  // a multiple of LPB: hidden is a multiple of BLOCK
-    const int64_t row_bytes = (int64_t)a.hidden * V::BYTES;
     const int nblk = a.hidden / BLOCK;
     const bool swz = a.sf_swizzled != 0;
     const bool round_prod = a.round_product != 0;
@@ -110,13 +109,13 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
 
     auto fetch = [&](uint4 (&xn)[VPT], uint4 (&rn)[RV], int64_t i) {
         if (i < a.rows) {
-            const int64_t off = row_of(i) * row_bytes;
-            const char* xr = static_cast<const char*>(a.x) + off;
+            const int64_t row = row_of(i);
+            const char* xr = static_cast<const char*>(a.x) + row * a.x_stride;
 #pragma unroll
             for (int k = 0; k < VPT; ++k)
                 if (live(k)) xn[k] = load_stream(xr, lt + k * T);
             if constexpr (RESID) {
-                const char* rr = static_cast<const char*>(a.residual) + off;
+                const char* rr = static_cast<const char*>(a.residual) + row * a.residual_stride;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k)
                     if (live(k)) rn[k] = load_stream(rr, lt + k * T);
@@ -147,7 +146,8 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) xf[e] += rf[e];
                     sv[k] = V::pack(xf);
-                    if (live(k)) store_stream(static_cast<char*>(a.residual_out) + row * row_bytes, lt + k * T, sv[k]);
+                    if (live(k))
+                        store_stream(static_cast<char*>(a.residual_out) + row * a.residual_out_stride, lt + k * T, sv[k]);
                 } else {
                     sv[k] = xv[k];
                 }
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
             const float c_scale = (float)(gs * rstd * (1.0 / 6.0));
             const float c_elem = (float)(gs * rstd);
 
-            uint8_t* orow = static_cast<uint8_t*>(a.out) + row * (int64_t)(a.hidden >> 1);
+            uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
             // this row's scale bytes: row-major, or the row's place in its
             // 128 x 4 tiles ((row/128) * K * 512 + (row%32) * 16 + ((row%128)/32) * 4)
             uint8_t* srow = static_cast<uint8_t*>(a.scales) +

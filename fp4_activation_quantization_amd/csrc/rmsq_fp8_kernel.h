@@ -1,0 +1,238 @@
+// Fused (residual +) RMSNorm + per-row dynamic FP8 quantization, gfx950.
+//
+// Operation: Mojo docs "rms_norm_fused_fp8" (epsilon, weight_offset, scale_ub,
+// per-row scale output) and the local share of
+// "allreduce_residual_rmsnorm_fp8" (residual, residual_output = pre-norm sum).
+//
+// One pass over HBM: every input element is read once into VGPRs, the row
+// stays in registers between the reduction and the quantization, and every
+// output byte is written once, all with non-temporal hints.
+//
+// Work mapping: `waves` wavefronts (1..16, a launch parameter) cooperate on
+// one row; a block holds one row, or 4/waves rows for 1-2 waves.  Lane l of a
+// row group owns the 16-byte vectors l, l + T, l + 2T, ... (T = 64 * waves,
+// VPT vectors per lane, a compile-time constant), so each wave instruction
+// moves 1 KiB of contiguous input.  EXACT (compile time) means the lanes hold
+// the row exactly (nvec == VPT * T): no lane is idle and no access needs a
+// guard.  Blocks stride over row groups; by default the grid has one block per
+// row group (large batches stream best that way on MI355X, and
+// gamma + weight_offset comes from L2).  STRIDED (compile time) reads each
+// row tensor's row stride from the arguments; otherwise rows are adjacent.
+//
+// Precision: s^2 is summed in fp32 within a 16-byte vector (v_dot2c on packed
+// 16-bit pairs, whose squares are exact), then in fp64 per lane and across
+// lanes; rstd, the scale and the quantization factor are formed in fp64 once
+// per row.  Per element the kernel computes t = s * g' and q = t * k
+// (k = rstd / stored_scale) in fp32, so a code sees at most three fp32
+// roundings of relative error.
+#pragma once
+
+#include "rmsq_device.h"
+#include "rmsq_internal.h"
+
+namespace rmsq {
+
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW, bool STRIDED>
+__global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
+    using V = Vec<InT>;
+    constexpr int EPV = V::EPV;
+    constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
+
+    const int waves = a.waves;       // wavefronts per row
+    const int T = waves * 64;        // lanes per row
+    // ONE_ROW: the block is one row group, so the row index is uniform
+    const int rpb = ONE_ROW ? 1 : blockDim.x / T;  // rows per block
+    const int tid = threadIdx.x;
+    const int slot = ONE_ROW ? 0 : tid / T;        // row slot within the block
+    const int lt = tid - slot * T;  // lane within the row group
+    const int red = slot * waves + (lt >> 6);  // this wave's reduction slot
+    const int nvec = a.nvec;
+    auto live = [&](int k) { return EXACT || lt + k * T < nvec; };
+    // bytes between rows: one value for the adjacent-row case
+    const int64_t row_bytes = (int64_t)a.hidden * V::BYTES;
+    const int64_t x_stride = STRIDED ? a.x_stride : row_bytes;
+    const int64_t r_stride = STRIDED ? a.residual_stride : row_bytes;
+    const int64_t ro_stride = STRIDED ? a.residual_out_stride : row_bytes;
+    const int64_t out_stride = STRIDED ? a.out_stride : (int64_t)a.hidden;
+
+    __shared__ double red_sum[2][16];
+    __shared__ int red_max[2][16];
+
+    // gamma + weight_offset for this lane's columns, fp32 (zero past the row).
+    // Without a residual it is loaded and unpacked once, before the rows; the
+    // residual variant loads it with each row instead, in flight together
+    // with the row's x and residual (measured on MI355X: the residual variant
+    // streams ~1% faster that way, the plain one has ~6% lower latency for a
+    // one-row call the first way).
+    float g[VPT][EPV];
+    auto load_gamma = [&]() {
+        uint4 gv[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+            gv[k] = live(k) ? reinterpret_cast<const uint4*>(a.gamma)[lt + k * T] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            V::unpack(gv[k], g[k]);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) g[k][e] = live(k) ? g[k][e] + a.weight_offset : 0.0f;
+        }
+    };
+    if constexpr (!RESID) load_gamma();
+
+    int parity = 0;
+    for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
+        const int64_t row = row0 + slot;
+        const bool active = row < a.rows;
+
+        float t[VPT][EPV];  // s * g'
+        double ssq = 0.0;
+        float amax = 0.0f;
+        if (active) {
+            const char* xr = static_cast<const char*>(a.x) + row * x_stride;
+            // vectors past the end of the row are zero: they add nothing
+            uint4 xv[VPT];
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) xv[k] = live(k) ? load_stream(xr, lt + k * T) : make_uint4(0, 0, 0, 0);
+            // every load of the row is issued before any store: residual_out
+            // may alias residual, so a load placed after a store could not be
+            // moved ahead of it and each vector would cost a round trip
+            uint4 rv[RESID ? VPT : 1];
+            if constexpr (RESID) {
+                const char* rr = static_cast<const char*>(a.residual) + row * r_stride;
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) rv[k] = live(k) ? load_stream(rr, lt + k * T) : make_uint4(0, 0, 0, 0);
+            }
+            if constexpr (RESID) load_gamma();  // an L2 hit after the first block
+            if constexpr (RESID) {
+                // residual_out may be x or residual itself: each vector is read
+                // (above) and then written by the one lane that owns it
+                char* ro = static_cast<char*>(a.residual_out) + row * ro_stride;
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    float xf[EPV], rf[EPV];
+                    V::unpack(xv[k], xf);
+                    V::unpack(rv[k], rf);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) xf[e] += rf[e];
+                    // one rounding of the fp32 sum to the element type; fp32 keeps
+                    // at least 2p+2 bits of a 16-bit sum, so this equals rounding
+                    // the exact sum once
+                    xv[k] = V::pack(xf);
+                    if (live(k)) store_stream(ro, lt + k * T, xv[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                ssq += (double)V::sumsq(xv[k]);
+                float s[EPV];
+                V::unpack(xv[k], s);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) t[k][e] = s[e] * g[k][e];
+                amax = abs_max<EPV>(amax, t[k]);
+            }
+        }
+
+        ssq = wave_sum(ssq);
+        amax = wave_max_nonneg(amax);
+        if (waves > 1) {  // uniform over the block
+            if ((lt & 63) == 0) {
+                red_sum[parity][red] = ssq;
+                red_max[parity][red] = __float_as_int(amax);
+            }
+            __syncthreads();
+            ssq = 0.0;
+            int m = 0;
+            for (int w = 0; w < waves; ++w) {
+                ssq += red_sum[parity][slot * waves + w];
+                m = max_bits(m, red_max[parity][slot * waves + w]);
+            }
+            amax = __int_as_float(m);
+            // the other parity's slots are rewritten only after the next
+            // barrier, which every wave reaches after finishing these reads
+            parity ^= 1;
+        }
+
+        if (active) {
+            const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
+            double sc = (double)amax * rstd * INV_FMAX;
+            if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
+            uint32_t sbits;
+            const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
+            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
+
+            uint8_t* orow = static_cast<uint8_t*>(a.out) + row * out_stride;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                if (live(k)) {
+                    if constexpr (EPV == 8) {
+                        uint2 w;
+                        w.x = fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq);
+                        w.y = fp8_x4<FNUZ>(t[k][4] * kq, t[k][5] * kq, t[k][6] * kq, t[k][7] * kq);
+                        store_stream(orow, lt + k * T, w);
+                    } else {
+                        store_stream(orow, lt + k * T,
+                                     fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq));
+                    }
+                }
+            }
+            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+        }
+    }
+}
+
+namespace fp8_launch {
+
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED>
+hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
+    a.waves = s.waves;
+    const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
+    // default: one block per row group
+    int64_t grid = s.grid > 0 ? s.grid : groups;
+    if (grid > groups) grid = groups;
+    if (grid > INT32_MAX) grid = INT32_MAX;
+    if (grid < 1) grid = 1;
+    const dim3 gd((unsigned)grid), bd(s.waves * s.rpb * 64);
+    const bool exact = a.nvec == VPT * s.waves * 64;
+    if (s.rpb == 1) {
+        if (exact)
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, true, STRIDED>), gd, bd, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, true, STRIDED>), gd, bd, 0, stream, a);
+    } else {
+        if (exact)
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, false, STRIDED>), gd, bd, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, false, STRIDED>), gd, bd, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename InT, bool RESID, bool FNUZ, bool STRIDED>
+hipError_t by_vpt(const FusedArgs& a, Shape s, hipStream_t st) {
+    switch (s.vpt) {
+    case 1: return launch_vpt<InT, RESID, FNUZ, 1, STRIDED>(a, s, st);
+    case 2: return launch_vpt<InT, RESID, FNUZ, 2, STRIDED>(a, s, st);
+    default: return launch_vpt<InT, RESID, FNUZ, 4, STRIDED>(a, s, st);
+    }
+}
+
+template <typename InT, bool STRIDED>
+hipError_t by_variant(const FusedArgs& a, bool resid, bool fnuz, Shape s, hipStream_t st) {
+    if (resid) return fnuz ? by_vpt<InT, true, true, STRIDED>(a, s, st) : by_vpt<InT, true, false, STRIDED>(a, s, st);
+    return fnuz ? by_vpt<InT, false, true, STRIDED>(a, s, st) : by_vpt<InT, false, false, STRIDED>(a, s, st);
+}
+
+}  // namespace fp8_launch
+
+// All FP8 variants for one input type (instantiated once per type, each in
+// its own translation unit so they compile in parallel).
+template <typename InT>
+hipError_t launch_fp8_typed(const FusedArgs& a, bool residual, bool fnuz, Shape s, hipStream_t stream) {
+    const int64_t rb = (int64_t)a.hidden * Vec<InT>::BYTES;
+    const bool adjacent = a.x_stride == rb && a.out_stride == a.hidden &&
+                          (!residual || (a.residual_stride == rb && a.residual_out_stride == rb));
+    return adjacent ? fp8_launch::by_variant<InT, false>(a, residual, fnuz, s, stream)
+                    : fp8_launch::by_variant<InT, true>(a, residual, fnuz, s, stream);
+}
+
+}  // namespace rmsq

@@ -29,6 +29,12 @@ struct FusedArgs {
     int32_t sf_swizzled;       // FP4: 1 for the 128x4-tile scale layout
     int32_t sf_k_tiles;        // FP4 swizzled: ceil((hidden / block) / 4)
     int32_t round_product;     // FP4: round s * g' to the input type (page numerics)
+    // bytes between consecutive rows of each row tensor (16-byte multiples;
+    // the contiguous values unless a strided entry point set them)
+    int64_t x_stride;
+    int64_t residual_stride;
+    int64_t residual_out_stride;
+    int64_t out_stride;
 };
 
 // FP4 variant: elements per block scale and the scale format.

@@ -194,6 +194,45 @@ int residual_rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype,
                               int scale_layout, int flags, void* out, void* block_scales,
                               hipStream_t stream);
 
+/*
+ * Strided forms -- the same operations on row tensors whose rows are not
+ * adjacent (a slice of a wider buffer, rows of a larger tensor): Mojo
+ * "rms_norm_fused_fp8" reads its input through an index function over a
+ * rank-N shape; with the leading dims flattened to rows, a row stride per
+ * tensor covers the layouts such a function describes with unit stride
+ * along the row.
+ *   *_stride     : distance between consecutive rows.  x, residual and
+ *                  residual_out: in in_dtype elements, >= hidden, and
+ *                  stride * element size a multiple of 16 bytes.  out: in
+ *                  bytes, >= the code bytes of a row (FP8: hidden; FP4:
+ *                  hidden / 2) and a multiple of 8 (FP8 with 16-bit input,
+ *                  FP4) or 4 (FP8 with fp32 input).  Else RMSQ_ERR_SHAPE.
+ *   residual     : NULL for no residual add (residual_out and the two
+ *                  residual strides are then ignored).
+ *   Aliasing is judged on each tensor's whole extent (first byte of row 0
+ *   to last byte of the last row), so interleaved tensors that share an
+ *   extent are rejected; residual_out may be exactly x or exactly residual
+ *   only with the same row stride.  Scales stay contiguous (FP8 [rows]; FP4
+ *   row-major or swizzled as rmsnorm_fp4quant).
+ * With every stride at its contiguous value these equal rmsnorm_fp8 /
+ * residual_rmsnorm_fp8 and rmsnorm_fp4quant / residual_rmsnorm_fp4quant.
+ */
+int rmsnorm_fp8_strided(int64_t rows, int64_t hidden, int in_dtype,
+                        const void* x, int64_t x_stride,
+                        const void* residual, int64_t residual_stride,
+                        void* residual_out, int64_t residual_out_stride,
+                        const void* gamma, float eps, float weight_offset, float scale_ub,
+                        int out_fp8, void* out, int64_t out_stride,
+                        int scales_dtype, void* scales, hipStream_t stream);
+int rmsnorm_fp4quant_strided(int64_t rows, int64_t hidden, int in_dtype,
+                             const void* x, int64_t x_stride,
+                             const void* residual, int64_t residual_stride,
+                             void* residual_out, int64_t residual_out_stride,
+                             const void* gamma, float eps, float weight_offset,
+                             const float* global_scale, int block_size, int scale_format,
+                             int scale_layout, int flags, void* out, int64_t out_stride,
+                             void* block_scales, hipStream_t stream);
+
 /* Bytes of the block_scales buffer rmsnorm_fp4quant writes into for this
  * shape and layout (rows * hidden / block row-major; whole 128 x 4 tiles
  * swizzled), or a negative RMSQ_ERR_* for invalid arguments.  No HIP call. */

@@ -42,7 +42,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     fns = declared_functions()
     for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "residual_rmsnorm_fp4quant",
-              "rmsq_fp4_scale_bytes",
+              "rmsnorm_fp8_strided", "rmsnorm_fp4quant_strided", "rmsq_fp4_scale_bytes",
               "rmsq_convert", "rmsq_stream_probe",
               "rmsq_set_tuning", "rmsq_query_shape", "rmsq_status_string", "rmsq_abi_version",
               "rmsq_last_hip_error"):
@@ -251,6 +251,41 @@ def test_residual_fp4quant_errors():
     L = rq.lib()
     q = lambda path: L.rmsq_query_shape(16384, 512, rq.BF16, path, None, None, None)  # fits the forced shape
     assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == VALUE
+
+
+def s8(x_stride=4096, r=None, r_stride=4096, ro=None, ro_stride=4096, out_stride=4096, dt=rq.BF16, x=None,
+       out=None, hidden=4096):
+    x = P(0) if x is None else x
+    out = P(2) if out is None else out
+    return rq.lib().rmsnorm_fp8_strided(4, hidden, dt, x, x_stride, r, r_stride, ro, ro_stride, P(1), 1e-6, 0.0,
+                                        1200.0, rq.E4M3FN, out, out_stride, rq.F32, P(3), None)
+
+
+def s4(x_stride=4096, out_stride=2048, r=None, r_stride=4096, ro=None, ro_stride=4096, dt=rq.BF16, out=None):
+    out = P(2) if out is None else out
+    return rq.lib().rmsnorm_fp4quant_strided(4, 4096, dt, P(0), x_stride, r, r_stride, ro, ro_stride, P(1), 1e-6,
+                                             0.0, None, 16, rq.SF_E4M3, rq.SF_ROW_MAJOR, 0, out, out_stride, P(3),
+                                             None)
+
+
+def test_strided_argument_checks():
+    assert s8() == UNSUP and s4() == UNSUP                      # contiguous strides pass
+    assert s8(x_stride=8192, out_stride=8192) == UNSUP          # wider rows pass
+    assert s8(x_stride=4095) == SHAPE                           # shorter than the row
+    assert s8(x_stride=4100) == SHAPE                           # 8200 bytes: not a 16-byte multiple
+    assert s8(out_stride=4095) == SHAPE and s8(out_stride=4100) == SHAPE
+    assert s8(out_stride=4100, dt=rq.F32, hidden=4096, x_stride=4100) == UNSUP  # fp32: 4-byte code rows, 16-byte x
+    assert s8(r=P(4), r_stride=4100, ro=P(5)) == SHAPE
+    assert s4(out_stride=2047) == SHAPE and s4(out_stride=2052) == SHAPE and s4(out_stride=2056) == UNSUP
+    # extents grow with the stride: 4 contiguous bf16 rows of 4096 span 32 KiB,
+    # with rows 8192 elements apart they span 3 * 16 KiB + 8 KiB = 56 KiB
+    after_x = ctypes.c_void_p(BASE + 32768)
+    assert s8(out=after_x) == UNSUP
+    assert s8(out=after_x, x_stride=8192) == ALIAS
+    # residual_out over x is in place only with the same row stride
+    assert s8(r=P(4), ro=P(0)) == UNSUP
+    assert s8(r=P(4), ro=P(0), ro_stride=8192) == ALIAS
+    assert s4(r=P(4), ro=P(4)) == UNSUP and s4(r=P(4), ro=P(4), r_stride=8192) == ALIAS
 
 
 def test_fp4_scale_bytes():
