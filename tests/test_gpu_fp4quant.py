@@ -68,11 +68,22 @@ def _gs(inp, w):
 @pytest.mark.parametrize("block", [16, 32])
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_every_variant(dt, block, fmt, swz):
-    for rows, hidden in ((300, 160), (131, 7168), (257, 2080)):
+    # 256 x 3072: a whole number of 256-row runs of the swizzled row map
+    for rows, hidden in ((300, 160), (131, 7168), (257, 2080), (256, 3072)):
         w = _wl(rows, hidden, dt, block, fmt, swz)
         inp = _inputs(rows, hidden, dt, seed=rows + hidden + block)
         say(f"[fp4quant] {dt} block={block} {fmt} swizzled={swz} rows={rows} hidden={hidden}")
         check_fp4(w, inp, _gs(inp, w), label=f"{dt} {block} {fmt} swz={swz} {rows}x{hidden}")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "ue8m0"])
+def test_swizzled_tile_slots_widest_row(fmt):
+    # the widest bf16 row with 16-element blocks: 2048 scale columns per row
+    rows, hidden = 256, 32768
+    w = _wl(rows, hidden, "bf16", 16, fmt, True)
+    inp = _inputs(rows, hidden, "bf16", seed=11)
+    say(f"[fp4quant widest swizzled] {fmt} rows={rows} hidden={hidden}")
+    check_fp4(w, inp, _gs(inp, w), label=f"widest swizzled {fmt}")
 
 
 @pytest.mark.parametrize("row", GOLDEN["fp4_block_rows"], ids=lambda r: r["id"])
@@ -118,7 +129,7 @@ def test_forced_launch_shapes_block32(fmt):
 @pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0"), (32, "e4m3"), (16, "ue8m0")])
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_residual_variants(dt, block, fmt, swz):
-    for rows, hidden in ((300, 160), (131, 7168)):
+    for rows, hidden in ((300, 160), (131, 7168), (512, 3072)):
         w = _wl(rows, hidden, dt, block, fmt, swz, resid=True)
         inp = _inputs(rows, hidden, dt, seed=rows + hidden + block + 1, resid=True)
         say(f"[fp4quant residual] {dt} block={block} {fmt} swizzled={swz} rows={rows} hidden={hidden}")
