@@ -77,22 +77,28 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     if (!valid_dtype(in_dtype) || !valid_dtype(scales_dtype)) return RMSQ_ERR_DTYPE;
     if (out_fp8 != RMSQ_E4M3FN && out_fp8 != RMSQ_E4M3FNUZ) return RMSQ_ERR_DTYPE;
     const int64_t esz = elem_size(in_dtype), epv = elems_per_vec(in_dtype);
-    if (rows < 0 || hidden <= 0 || hidden % epv != 0) return RMSQ_ERR_SHAPE;
-    if (!stride_ok(x_stride, hidden, esz, 16) || !stride_ok(out_stride, hidden, 1, epv)) return RMSQ_ERR_SHAPE;
-    if (resid && (!stride_ok(r_stride, hidden, esz, 16) || !stride_ok(ro_stride, hidden, esz, 16)))
+    // any row width and any element-aligned rows: the vector kernel takes
+    // rows of whole, 16-byte aligned vectors, the element kernel the rest
+    if (rows < 0 || hidden <= 0) return RMSQ_ERR_SHAPE;
+    if (!stride_ok(x_stride, hidden, esz, esz) || !stride_ok(out_stride, hidden, 1, 1)) return RMSQ_ERR_SHAPE;
+    if (resid && (!stride_ok(r_stride, hidden, esz, esz) || !stride_ok(ro_stride, hidden, esz, esz)))
         return RMSQ_ERR_SHAPE;
     const int64_t widest = std::max({x_stride, out_stride / esz + 1, resid ? std::max(r_stride, ro_stride) : 0});
     if (!size_ok(rows, widest, esz)) return RMSQ_ERR_SHAPE;
     if (int rc = check_scalars(eps, weight_offset, scale_ub, true)) return rc;
-    const int nvec = (int)(hidden / epv);
-    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    if (hidden > std::max(kMaxVec * epv, kMaxElemHidden)) return RMSQ_ERR_UNSUPPORTED;
     if (rows == 0) return RMSQ_OK;
     if (!x || !gamma || !out || !scales) return RMSQ_ERR_NULL;
     if (resid && (!residual || !residual_out)) return RMSQ_ERR_NULL;
     const int64_t ssz = elem_size(scales_dtype);
-    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(out, 16) || !aligned(scales, (uintptr_t)ssz))
-        return RMSQ_ERR_ALIGN;
-    if (resid && (!aligned(residual, 16) || !aligned(residual_out, 16))) return RMSQ_ERR_ALIGN;
+    if (!aligned(x, esz) || !aligned(gamma, esz) || !aligned(scales, (uintptr_t)ssz)) return RMSQ_ERR_ALIGN;
+    if (resid && (!aligned(residual, esz) || !aligned(residual_out, esz))) return RMSQ_ERR_ALIGN;
+    const bool vec = hidden % epv == 0 && hidden / epv <= kMaxVec && aligned(x, 16) && aligned(gamma, 16) &&
+                     aligned(out, 16) && (x_stride * esz) % 16 == 0 && out_stride % epv == 0 &&
+                     (!resid || (aligned(residual, 16) && aligned(residual_out, 16) && (r_stride * esz) % 16 == 0 &&
+                                 (ro_stride * esz) % 16 == 0));
+    if (!vec && hidden > kMaxElemHidden) return RMSQ_ERR_UNSUPPORTED;
+    const int nvec = vec ? (int)(hidden / epv) : 0;
 
     // spans cover every row; strided tensors are compared by their extents
     const int64_t rb = hidden * esz;
@@ -114,7 +120,8 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     }
 
     Shape shape;
-    if (!choose_shape(rows, nvec, kPathFp8, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    if (vec ? !choose_shape(rows, nvec, kPathFp8, &shape) : !choose_elem_shape(rows, hidden, &shape))
+        return RMSQ_ERR_UNSUPPORTED;
     FusedArgs a{};
     a.x = x;
     a.residual = residual;
@@ -135,7 +142,8 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     a.residual_stride = r_stride * esz;
     a.residual_out_stride = ro_stride * esz;
     a.out_stride = out_stride;
-    return launched(launch_fp8(a, in_dtype, resid, out_fp8, shape, stream));
+    return launched(vec ? launch_fp8(a, in_dtype, resid, out_fp8, shape, stream)
+                        : launch_fp8_elem(a, in_dtype, resid, out_fp8, shape, stream));
 }
 
 }  // namespace
@@ -278,6 +286,42 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
     return true;
 }
 
+bool choose_elem_shape(int64_t rows, int64_t hidden, Shape* s) {
+    (void)rows;
+    // elements per lane for w waves: the smallest compiled count that holds
+    // the row, or 0
+    auto epl_for = [&](int w) {
+        const int64_t need = ceil_div(hidden, (int64_t)w * 64);
+        for (int e : kElemPerLane)
+            if (e >= need) return e;
+        return 0;
+    };
+    int waves = g_tune_waves.load(std::memory_order_relaxed), epl = 0;
+    if (waves > 0) {
+        epl = epl_for(waves);
+    } else {
+        // the fewest element slots that hold the row; ties to more waves
+        // (shorter per-lane chains, more loads in flight)
+        int64_t best = INT64_MAX;
+        for (int w : {1, 2, 4, 8, 12, 16}) {
+            const int e = epl_for(w);
+            if (e == 0) continue;
+            const int64_t slots = (int64_t)w * 64 * e;
+            if (slots <= best) {
+                best = slots;
+                waves = w;
+                epl = e;
+            }
+        }
+    }
+    if (epl == 0) return false;
+    s->waves = waves;
+    s->vpt = epl;
+    s->rpb = waves >= 4 ? 1 : 4 / waves;
+    s->grid = g_tune_blocks.load(std::memory_order_relaxed);
+    return true;
+}
+
 int persistent_blocks(const void* kernel, int block_threads) {
     static std::mutex mu;
     static std::map<std::pair<std::pair<int, int>, const void*>, int> cache;
@@ -408,6 +452,16 @@ int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks) {
 int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path, int* waves_per_row,
                      int* vectors_per_lane, int* rows_per_block) {
     if (!valid_dtype(in_dtype)) return RMSQ_ERR_DTYPE;
+    if (path == kPathFp8Elem) {
+        if (hidden <= 0) return RMSQ_ERR_SHAPE;
+        if (hidden > kMaxElemHidden) return RMSQ_ERR_UNSUPPORTED;
+        Shape s;
+        if (!choose_elem_shape(rows, hidden, &s)) return RMSQ_ERR_UNSUPPORTED;
+        if (waves_per_row) *waves_per_row = s.waves;
+        if (vectors_per_lane) *vectors_per_lane = s.vpt;
+        if (rows_per_block) *rows_per_block = s.rpb;
+        return RMSQ_OK;
+    }
     if (hidden <= 0 || hidden % elems_per_vec(in_dtype) != 0) return RMSQ_ERR_SHAPE;
     const int64_t nvec = hidden / elems_per_vec(in_dtype);
     if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;

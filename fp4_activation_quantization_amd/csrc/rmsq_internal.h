@@ -29,7 +29,8 @@ struct FusedArgs {
     int32_t sf_swizzled;       // FP4: 1 for the 128x4-tile scale layout
     int32_t sf_k_tiles;        // FP4 swizzled: ceil((hidden / block) / 4)
     int32_t round_product;     // FP4: round s * g' to the input type (page numerics)
-    // bytes between consecutive rows of each row tensor (16-byte multiples;
+    // bytes between consecutive rows of each row tensor (16-byte multiples
+    // for the vector kernels, element multiples for the FP8 element path;
     // the contiguous values unless a strided entry point set them)
     int64_t x_stride;
     int64_t residual_stride;
@@ -44,7 +45,8 @@ struct Fp4Format {
 };
 
 // Launch shape: one row is handled by `waves` wavefronts (64 lanes each, any
-// count 1..16), each lane holding `vpt` 16-byte vectors of the row; a block
+// count 1..16), each lane holding `vpt` 16-byte vectors of the row (on the
+// FP8 element path: `vpt` single elements, one of kElemPerLane); a block
 // holds `rpb` rows (waves * rpb wavefronts); `grid` blocks (0 = default).
 struct Shape {
     int waves;
@@ -54,15 +56,27 @@ struct Shape {
 };
 
 // Which fused path a shape is chosen for (the rmsq_query_shape `path` values).
-enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2 };
+enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3 };
 
 // Pick the automatic shape for a row of nvec 16-byte vectors (or apply the
 // process-wide override).  Returns false if no supported shape holds the row.
 bool choose_shape(int64_t rows, int nvec, int path, Shape* s);
 
+// Elements per lane the FP8 element kernel is compiled for, and the widest
+// row it holds (16 waves x 64 lanes x 16 elements; more per lane would spill
+// the 128 VGPRs a 1024-thread block allows).
+constexpr int kElemPerLane[] = {1, 2, 4, 8, 12, 16};
+constexpr int64_t kMaxElemHidden = 16 * 64 * 16;
+
+// Shape for the FP8 element path (honours the override's wave count and
+// grid; its vectors per lane do not apply).  False if no shape holds the row.
+bool choose_elem_shape(int64_t rows, int64_t hidden, Shape* s);
+
 // Kernel launchers (no argument checks).  Return the hipError_t of the launch.
 hipError_t launch_fp8(const FusedArgs& a, int in_dtype, bool residual, int out_fp8,
                       Shape shape, hipStream_t stream);
+hipError_t launch_fp8_elem(const FusedArgs& a, int in_dtype, bool residual, int out_fp8, Shape shape,
+                           hipStream_t stream);
 hipError_t launch_fp4(const FusedArgs& a, int in_dtype, bool residual, Fp4Format fmt, Shape shape,
                       hipStream_t stream);
 hipError_t launch_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);

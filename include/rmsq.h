@@ -53,17 +53,19 @@ enum {
     RMSQ_OK = 0,
     RMSQ_ERR_NULL = -1,        /* a required pointer is NULL */
     RMSQ_ERR_DTYPE = -2,       /* unknown enum or unsupported combination */
-    RMSQ_ERR_SHAPE = -3,       /* rows < 0, hidden <= 0, hidden not a multiple of the
-                                  16-byte vector width (8 for 16-bit, 4 for fp32 input),
-                                  FP4 hidden not a multiple of 16, or size overflow */
-    RMSQ_ERR_ALIGN = -4,       /* a tensor pointer is not aligned (16 B for x, residual,
-                                  residual_out, gamma, out; element size for scales) */
+    RMSQ_ERR_SHAPE = -3,       /* rows < 0, hidden <= 0, FP4 hidden not a multiple of
+                                  the block (16 or 32), a row stride shorter than a row
+                                  or off its granule, or size overflow */
+    RMSQ_ERR_ALIGN = -4,       /* a tensor pointer is not aligned (FP4: 16 B for x,
+                                  residual, residual_out, gamma, out; FP8: the element
+                                  size for those; both: element size for scales) */
     RMSQ_ERR_VALUE = -5,       /* eps < 0 or non-finite; scale_ub <= 0 or NaN;
                                   weight_offset non-finite */
     RMSQ_ERR_ALIAS = -6,       /* an output overlaps an input or another output
                                   (other than residual_out == x or == residual) */
     RMSQ_ERR_UNSUPPORTED = -7, /* hidden above the largest row the kernels hold
-                                  (32768 for 16-bit inputs, 16384 for fp32) */
+                                  (32768 for 16-bit inputs, 16384 for fp32; FP8 rows
+                                  off the vector path: 16384) */
     RMSQ_ERR_LAUNCH = -8       /* the kernel launch failed; see rmsq_last_hip_error() */
 };
 
@@ -71,6 +73,13 @@ enum {
  * rmsnorm_fp8 -- RMSNorm + per-row dynamic FP8 quantization
  * (Mojo docs "rms_norm_fused_fp8", Args).
  *   rows, hidden : tensor shape; normalization runs over the last dimension.
+ *                  Any hidden >= 1 (the page's input_fn is generic in its SIMD
+ *                  width).  Rows of whole 16-byte vectors (hidden a multiple
+ *                  of 8 for 16-bit, 4 for fp32 input; x, gamma, out 16-byte
+ *                  aligned) take the vector kernel; any other hidden, or
+ *                  pointers aligned only to the element size, take an
+ *                  element-wise kernel with the same results, slower, for
+ *                  hidden <= 16384.
  *   in_dtype     : RMSQ_F32 / RMSQ_F16 / RMSQ_BF16, the type of x and gamma.
  *   x            : [rows, hidden] input.
  *   gamma        : [hidden] weight; the multiplier is gamma + weight_offset,
@@ -94,7 +103,8 @@ int rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype,
  * residual_rmsnorm_fp8 -- residual add + RMSNorm + per-row FP8 quantization:
  * one GPU's share of Mojo docs "allreduce_residual_rmsnorm_fp8" (Args:
  * residual, residual_output as the pre-norm sum).
- *   residual     : [rows, hidden] in in_dtype.
+ *   residual     : [rows, hidden] in in_dtype (the vector kernel also needs
+ *                  residual and residual_out 16-byte aligned).
  *   residual_out : [rows, hidden] in in_dtype; receives s = x + residual
  *                  rounded once to in_dtype (RNE).  The normalization uses
  *                  exactly this stored s.  residual_out may be the same
@@ -202,11 +212,15 @@ int residual_rmsnorm_fp4quant(int64_t rows, int64_t hidden, int in_dtype,
  * tensor covers the layouts such a function describes with unit stride
  * along the row.
  *   *_stride     : distance between consecutive rows.  x, residual and
- *                  residual_out: in in_dtype elements, >= hidden, and
+ *                  residual_out: in in_dtype elements, >= hidden; for FP4
  *                  stride * element size a multiple of 16 bytes.  out: in
  *                  bytes, >= the code bytes of a row (FP8: hidden; FP4:
- *                  hidden / 2) and a multiple of 8 (FP8 with 16-bit input,
- *                  FP4) or 4 (FP8 with fp32 input).  Else RMSQ_ERR_SHAPE.
+ *                  hidden / 2); for FP4 a multiple of 8.  Else
+ *                  RMSQ_ERR_SHAPE.  FP8 takes any such strides: rows that
+ *                  start on 16-byte boundaries (element strides of 16 bytes'
+ *                  multiples, out strides a multiple of 8 for 16-bit or 4 for
+ *                  fp32 input) use the vector kernel, others the element-wise
+ *                  kernel.
  *   residual     : NULL for no residual add (residual_out and the two
  *                  residual strides are then ignored).
  *   Aliasing is judged on each tensor's whole extent (first byte of row 0
@@ -292,8 +306,11 @@ int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t wr
 int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks);
 
 /* Launch shape the next call with these arguments would use (for logs).
- * path: 0 for the FP8 entry points, 1 for rmsnorm_fp4 / rmsnorm_fp4quant,
- * 2 for residual_rmsnorm_fp4quant (RMSQ_ERR_VALUE otherwise). */
+ * path: 0 for the FP8 entry points on the vector kernel, 1 for rmsnorm_fp4 /
+ * rmsnorm_fp4quant, 2 for residual_rmsnorm_fp4quant, 3 for the FP8 entry
+ * points on the element-wise kernel (vectors_per_lane then receives the
+ * elements per lane; rmsq_set_tuning's wave count and grid apply to it, its
+ * vectors per lane do not).  RMSQ_ERR_VALUE for another path. */
 int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path,
                      int* waves_per_row, int* vectors_per_lane, int* rows_per_block);
 

@@ -106,9 +106,11 @@ def test_fp8_shape_errors():
     assert fp8(rows=-1) == SHAPE
     assert fp8(hidden=0) == SHAPE
     assert fp8(hidden=-8) == SHAPE
-    assert fp8(hidden=12) == SHAPE            # 16-bit input: multiple of 8
-    assert fp8(hidden=6, dt=rq.F32) == SHAPE  # fp32 input: multiple of 4
     assert fp8(rows=1 << 62, hidden=1 << 20) == SHAPE
+    # any width passes: rows that are not whole 16-byte vectors go to the
+    # element-wise kernel (which the forced one-wave shape cannot hold either)
+    assert fp8(hidden=4100) == UNSUP
+    assert fp8(hidden=4102, dt=rq.F32) == UNSUP
 
 
 def test_fp8_value_errors():
@@ -123,6 +125,12 @@ def test_fp8_value_errors():
 def test_fp8_unsupported_width():
     assert fp8(hidden=8 * 4096 + 8) == UNSUP
     assert fp8(hidden=4 * 4096 + 4, dt=rq.F32) == UNSUP
+    rq.set_tuning(0, 0, 0)  # automatic shapes: only the width limits remain
+    try:
+        assert fp8(hidden=16384 + 2) == UNSUP               # beyond the element-wise kernel
+        assert fp8(hidden=16384 + 8, x=ctypes.c_void_p(BASE + 2)) == UNSUP  # off the vector path
+    finally:
+        rq.set_tuning(1, 1, 0)
 
 
 def test_zero_rows_is_a_noop_even_with_null_pointers():
@@ -145,14 +153,17 @@ def test_fp8_null_errors():
 
 
 def test_fp8_alignment_errors():
+    # FP8 tensors need only element alignment (rows off 16-byte boundaries
+    # take the element-wise kernel); codes have none
     odd = lambda i, k: ctypes.c_void_p(BASE + i * MB + k)
-    assert fp8(x=odd(0, 8)) == ALIGN
-    assert fp8(g=odd(1, 2)) == ALIGN
-    assert fp8(out=odd(2, 8)) == ALIGN
+    assert fp8(x=odd(0, 1)) == ALIGN and fp8(x=odd(0, 2)) == UNSUP and fp8(x=odd(0, 8)) == UNSUP
+    assert fp8(x=odd(0, 2), dt=rq.F32) == ALIGN and fp8(x=odd(0, 4), dt=rq.F32) == UNSUP
+    assert fp8(g=odd(1, 1)) == ALIGN and fp8(g=odd(1, 2)) == UNSUP
+    assert fp8(out=odd(2, 1)) == UNSUP
     assert fp8(sc=odd(3, 2)) == ALIGN                  # fp32 scales need 4 bytes
     assert fp8(sc=odd(3, 2), sdt=rq.BF16) == UNSUP     # bf16 scales need 2: all checks pass
-    assert rfp8(r=odd(4, 4)) == ALIGN
-    assert rfp8(ro=odd(5, 4)) == ALIGN
+    assert rfp8(r=odd(4, 1)) == ALIGN and rfp8(r=odd(4, 4)) == UNSUP
+    assert rfp8(ro=odd(5, 3)) == ALIGN and rfp8(ro=odd(5, 4)) == UNSUP
 
 
 def test_fp8_alias_errors():
@@ -250,7 +261,7 @@ def test_residual_fp4quant_errors():
     assert rfp4q(ro=P(0)) == UNSUP and rfp4q(ro=P(4)) == UNSUP
     L = rq.lib()
     q = lambda path: L.rmsq_query_shape(16384, 512, rq.BF16, path, None, None, None)  # fits the forced shape
-    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == VALUE
+    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == OK and q(4) == VALUE
 
 
 def s8(x_stride=4096, r=None, r_stride=4096, ro=None, ro_stride=4096, out_stride=4096, dt=rq.BF16, x=None,
@@ -272,10 +283,11 @@ def test_strided_argument_checks():
     assert s8() == UNSUP and s4() == UNSUP                      # contiguous strides pass
     assert s8(x_stride=8192, out_stride=8192) == UNSUP          # wider rows pass
     assert s8(x_stride=4095) == SHAPE                           # shorter than the row
-    assert s8(x_stride=4100) == SHAPE                           # 8200 bytes: not a 16-byte multiple
-    assert s8(out_stride=4095) == SHAPE and s8(out_stride=4100) == SHAPE
-    assert s8(out_stride=4100, dt=rq.F32, hidden=4096, x_stride=4100) == UNSUP  # fp32: 4-byte code rows, 16-byte x
-    assert s8(r=P(4), r_stride=4100, ro=P(5)) == SHAPE
+    assert s8(x_stride=4100) == UNSUP                           # 8200 bytes: the element-wise kernel
+    assert s8(out_stride=4095) == SHAPE and s8(out_stride=4100) == UNSUP
+    assert s8(out_stride=4100, dt=rq.F32, hidden=4096, x_stride=4100) == UNSUP
+    assert s8(r=P(4), r_stride=4100, ro=P(5)) == UNSUP
+    assert s8(r=P(4), r_stride=4095, ro=P(5)) == SHAPE and s8(r=P(4), ro=P(5), ro_stride=4095) == SHAPE
     assert s4(out_stride=2047) == SHAPE and s4(out_stride=2052) == SHAPE and s4(out_stride=2056) == UNSUP
     # extents grow with the stride: 4 contiguous bf16 rows of 4096 span 32 KiB,
     # with rows 8192 elements apart they span 3 * 16 KiB + 8 KiB = 56 KiB
@@ -344,6 +356,23 @@ def test_tuning_and_query_shape():
             rq.query_shape(8, 4096, rq.torch.bfloat16)  # 64 lanes x 1 vector cannot hold 512 vectors
         rq.set_tuning(4, 4, 0)
         assert rq.query_shape(8, 4096, rq.torch.bfloat16)["rows_per_block"] == 1
+        # the element-wise kernel takes the forced wave count, not the vectors
+        rq.set_tuning(8, 4, 0)
+        assert rq.query_shape(8, 4100, rq.torch.bfloat16, elementwise=True) == {
+            "waves_per_row": 8, "vectors_per_lane": 12, "rows_per_block": 1}
+        rq.set_tuning(0, 0, 0)
+        # automatic element-wise shapes: the fewest element slots, ties to more waves
+        assert rq.query_shape(512, 7, rq.torch.bfloat16, elementwise=True) == {
+            "waves_per_row": 1, "vectors_per_lane": 1, "rows_per_block": 4}
+        assert rq.query_shape(512, 100, rq.torch.float16, elementwise=True) == {
+            "waves_per_row": 2, "vectors_per_lane": 1, "rows_per_block": 2}
+        assert rq.query_shape(512, 4100, rq.torch.bfloat16, elementwise=True) == {
+            "waves_per_row": 12, "vectors_per_lane": 8, "rows_per_block": 1}
+        assert rq.query_shape(1, 16384, rq.torch.float32, elementwise=True) == {
+            "waves_per_row": 16, "vectors_per_lane": 16, "rows_per_block": 1}
+        for bad in (16385, 0):
+            with pytest.raises(rq.RmsqError):
+                rq.query_shape(1, bad, rq.torch.bfloat16, elementwise=True)
     finally:
         rq.set_tuning(1, 1, 0)
 
