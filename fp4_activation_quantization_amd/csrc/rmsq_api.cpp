@@ -30,6 +30,7 @@ bool valid_dtype(int dt) { return dt == RMSQ_F32 || dt == RMSQ_F16 || dt == RMSQ
 int64_t elem_size(int dt) { return dt == RMSQ_F32 ? 4 : 2; }
 int64_t elems_per_vec(int dt) { return 16 / elem_size(dt); }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Span {
     uintptr_t lo, hi;  // [lo, hi)
@@ -93,12 +94,26 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     const int64_t ssz = elem_size(scales_dtype);
     if (!aligned(x, esz) || !aligned(gamma, esz) || !aligned(scales, (uintptr_t)ssz)) return RMSQ_ERR_ALIGN;
     if (resid && (!aligned(residual, esz) || !aligned(residual_out, esz))) return RMSQ_ERR_ALIGN;
+    // Three kernels: rows of whole, 16-byte aligned vectors (the vector
+    // kernel); rows at a common offset from the 16-byte grid (the phased
+    // kernel: residual and residual_out at x's offset on every row, codes at
+    // the same offset modulo epv, gamma aligned); anything else (the
+    // element-wise kernel)
     const bool vec = hidden % epv == 0 && hidden / epv <= kMaxVec && aligned(x, 16) && aligned(gamma, 16) &&
                      aligned(out, 16) && (x_stride * esz) % 16 == 0 && out_stride % epv == 0 &&
                      (!resid || (aligned(residual, 16) && aligned(residual_out, 16) && (r_stride * esz) % 16 == 0 &&
                                  (ro_stride * esz) % 16 == 0));
-    if (!vec && hidden > kMaxElemHidden) return RMSQ_ERR_UNSUPPORTED;
-    const int nvec = vec ? (int)(hidden / epv) : 0;
+    const uintptr_t xph = reinterpret_cast<uintptr_t>(x) % 16;  // bytes past the 16-byte grid
+    auto same_phase = [&](const void* p, int64_t stride) {
+        return reinterpret_cast<uintptr_t>(p) % 16 == xph && ((stride - x_stride) * esz) % 16 == 0;
+    };
+    const int64_t phased_nvec = ceil_div(hidden + epv - 1, epv);  // the grid vectors a row can touch
+    const bool phased = !vec && phased_nvec <= kMaxVec && aligned(gamma, 16) &&
+                        (int64_t)(reinterpret_cast<uintptr_t>(out) % epv) == (int64_t)(xph / esz) % epv &&
+                        (out_stride - x_stride) % epv == 0 &&
+                        (!resid || (same_phase(residual, r_stride) && same_phase(residual_out, ro_stride)));
+    if (!vec && !phased && hidden > kMaxElemHidden) return RMSQ_ERR_UNSUPPORTED;
+    const int nvec = vec ? (int)(hidden / epv) : phased ? (int)phased_nvec : 0;
 
     // spans cover every row; strided tensors are compared by their extents
     const int64_t rb = hidden * esz;
@@ -120,7 +135,9 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     }
 
     Shape shape;
-    if (vec ? !choose_shape(rows, nvec, kPathFp8, &shape) : !choose_elem_shape(rows, hidden, &shape))
+    const int path = !vec ? kPathFp8Phased : resid ? kPathFp8Residual : kPathFp8;
+    if ((vec || phased) ? !choose_shape(rows, nvec, path, &shape)
+                        : !choose_elem_shape(rows, hidden, &shape))
         return RMSQ_ERR_UNSUPPORTED;
     FusedArgs a{};
     a.x = x;
@@ -142,15 +159,15 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     a.residual_stride = r_stride * esz;
     a.residual_out_stride = ro_stride * esz;
     a.out_stride = out_stride;
-    return launched(vec ? launch_fp8(a, in_dtype, resid, out_fp8, shape, stream)
-                        : launch_fp8_elem(a, in_dtype, resid, out_fp8, shape, stream));
+    return launched(vec      ? launch_fp8(a, in_dtype, resid, out_fp8, shape, stream)
+                    : phased ? launch_fp8_phased(a, in_dtype, resid, out_fp8, shape, stream)
+                             : launch_fp8_elem(a, in_dtype, resid, out_fp8, shape, stream));
 }
 
 }  // namespace
 
 namespace {
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Vectors per lane for a given wave count: the smallest supported one that
 // holds the row, or 0.
@@ -249,21 +266,43 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
             // 8 x 2 on MI355X, 3.0 us as 16 x 1 and 2.8 us as 4 x 4)
             vpt = nvec <= 64 ? 1 : (nvec <= 16 * 64 * 2 ? 2 : 4);
             waves = (int)std::min<int64_t>(16, ceil_div(nvec, 64 * vpt));
+        } else if (path == kPathFp8Phased) {
+            // the phased kernel: the fewest waves that hold the row at up to
+            // 4 vectors per lane, then the fewest vectors per lane (measured
+            // on MI355X: a 513-vector row runs 1.2-1.3x faster as 4 x 4 than
+            // as 12 x 1, the shape with the fewest idle lanes)
+            waves = 0;
+            for (int w : {1, 2, 4, 8, 12, 16}) {
+                if ((int64_t)w * 64 * 4 >= nvec) {
+                    waves = w;
+                    break;
+                }
+            }
+            if (waves == 0) return false;
+            vpt = vpt_for(nvec, waves);
         } else {
             // large batches: blocks of a multiple of 4 wavefronts, so the 4
             // SIMDs of a CU get equal work (odd counts measured 20-35% slower
             // on MI355X).  Among those shapes whose lanes hold the row, the one
             // with the fewest idle lanes; ties go to 2 vectors per lane for
-            // FP8 and 4 for FP4 (the faster ones measured).  Residual FP4
-            // holds two inputs per row and takes the FP8 order, which keeps
-            // it within its registers.
-            const int order_fp8[3] = {2, 4, 1}, order_fp4[3] = {4, 2, 1};
-            const int* order = path == kPathFp4 ? order_fp4 : order_fp8;
+            // residual FP8 and FP4 and to 4 for FP4 (the faster ones
+            // measured; residual FP4 holds two inputs per row and stays
+            // within its registers that way).  FP8 rows of more than 256
+            // vectors take at least 4 waves, one vector per lane only at 4
+            // waves, and without a residual prefer 4 vectors per lane
+            // (measured on MI355X, bf16: 12 x 1 runs 640- and 768-vector rows
+            // 1.1-1.5x slower than 8 x 2 / 4 x 4, 16 x 2 a 2048-vector row
+            // 1.3x slower than 8 x 4 without a residual).
+            const int order_2[3] = {2, 4, 1}, order_4[3] = {4, 2, 1};
+            const bool fp8 = path == kPathFp8 || path == kPathFp8Residual;
+            const int* order =
+                (path == kPathFp4 || (path == kPathFp8 && nvec > 256)) ? order_4 : order_2;
             int64_t best_idle = INT64_MAX;
             waves = 0;
             for (int i = 0; i < 3; ++i) {
                 const int v = order[i];
                 for (int w : {1, 2, 4, 8, 12, 16}) {
+                    if (fp8 && nvec > 256 && (w < 4 || (v == 1 && w > 4))) continue;
                     const int64_t idle = (int64_t)w * 64 * v - nvec;
                     if (idle >= 0 && idle < best_idle) {
                         best_idle = idle;
@@ -462,11 +501,23 @@ int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path, int* 
         if (rows_per_block) *rows_per_block = s.rpb;
         return RMSQ_OK;
     }
+    if (path == kPathFp8Phased) {
+        if (hidden <= 0) return RMSQ_ERR_SHAPE;
+        const int64_t epv = elems_per_vec(in_dtype), nv = ceil_div(hidden + epv - 1, epv);
+        if (nv > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+        Shape s;
+        if (!choose_shape(rows, (int)nv, kPathFp8Phased, &s)) return RMSQ_ERR_UNSUPPORTED;
+        if (waves_per_row) *waves_per_row = s.waves;
+        if (vectors_per_lane) *vectors_per_lane = s.vpt;
+        if (rows_per_block) *rows_per_block = s.rpb;
+        return RMSQ_OK;
+    }
     if (hidden <= 0 || hidden % elems_per_vec(in_dtype) != 0) return RMSQ_ERR_SHAPE;
     const int64_t nvec = hidden / elems_per_vec(in_dtype);
     if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
     Shape s;
-    if (path < kPathFp8 || path > kPathFp4Residual) return RMSQ_ERR_VALUE;
+    if (path != kPathFp8 && path != kPathFp4 && path != kPathFp4Residual && path != kPathFp8Residual)
+        return RMSQ_ERR_VALUE;
     if (!choose_shape(rows, (int)nvec, path, &s)) return RMSQ_ERR_UNSUPPORTED;
     if (waves_per_row) *waves_per_row = s.waves;
     if (vectors_per_lane) *vectors_per_lane = s.vpt;

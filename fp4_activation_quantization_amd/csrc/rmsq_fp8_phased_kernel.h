@@ -1,0 +1,335 @@
+// Fused (residual +) RMSNorm + per-row dynamic FP8 quantization for rows that
+// are not whole 16-byte vectors but all sit at a common offset ("phase") from
+// the 16-byte grid: a hidden size that is not a multiple of the vector width
+// (8 16-bit or 4 fp32 elements) in contiguous tensors, or tensors that all
+// start the same number of elements past a 16-byte boundary.  gfx950.
+//
+// Operation: as the vector kernel (rmsq_fp8_kernel.h): Mojo docs
+// "rms_norm_fused_fp8" and the local share of
+// "allreduce_residual_rmsnorm_fp8".  Their input_fn is generic in its SIMD
+// width, so a row need not be a whole number of vectors.
+//
+// Work mapping: as the vector kernel, on the 16-byte grid rather than on the
+// row.  A row whose first element lies h elements past a 16-byte boundary
+// covers nv = ceil((h + hidden) / EPV) aligned vectors; lane l owns vectors
+// l, l + T, ... of them.  Interior vectors are whole; in the first and the
+// last, the bytes outside the row are zeroed after the load (the aligned
+// 16 bytes around an element of the row never leave its page, so these
+// loads cannot fault) and only the row's own elements are stored back, one
+// by one, so rows that share a vector never write each other's elements.
+// Codes and residual_out are stored 8 / 16 bytes at a time: the host takes
+// this kernel only when every tensor has x's phase (codes: the same offset
+// modulo the code bytes of a vector).  gamma' for the lane's vector is the
+// window h elements back across gamma's aligned vectors d - 1 and d (d held
+// by the lane, d - 1 by the previous lane), cut with byte funnel shifts
+// (v_alignbyte_b32) chosen by a switch on h, which is uniform over the
+// wavefronts of a row.
+#pragma once
+
+#include "rmsq_device.h"
+#include "rmsq_internal.h"
+
+namespace rmsq {
+
+// Bytes [lo, hi) of a 16-byte vector kept, the others zeroed (dword w holds
+// bytes 4w .. 4w+3).
+__device__ __forceinline__ uint32_t dword_keep(int lo, int hi, int w) {
+    const int a = max(lo - 4 * w, 0), b = min(hi - 4 * w, 4);
+    return b > a ? (0xFFFFFFFFu >> (32 - 8 * (b - a))) << (8 * a) : 0u;
+}
+__device__ __forceinline__ uint4 keep_bytes(uint4 v, int lo, int hi) {
+    v.x &= dword_keep(lo, hi, 0);
+    v.y &= dword_keep(lo, hi, 1);
+    v.z &= dword_keep(lo, hi, 2);
+    v.w &= dword_keep(lo, hi, 3);
+    return v;
+}
+
+// The 16 bytes starting OFF bytes into the 32-byte concatenation p | c.
+template <int OFF>
+__device__ __forceinline__ uint4 window_at(const uint4& p, const uint4& c) {
+    const uint32_t w[8] = {p.x, p.y, p.z, p.w, c.x, c.y, c.z, c.w};
+    constexpr int q = OFF / 4, r = OFF % 4;
+    if constexpr (r == 0) {
+        return make_uint4(w[q], w[q + 1], w[q + 2], w[q + 3]);
+    } else {
+        return make_uint4(__builtin_amdgcn_alignbyte(w[q + 1], w[q], r), __builtin_amdgcn_alignbyte(w[q + 2], w[q + 1], r),
+                          __builtin_amdgcn_alignbyte(w[q + 3], w[q + 2], r), __builtin_amdgcn_alignbyte(w[q + 4], w[q + 3], r));
+    }
+}
+
+// Elements EPV - h .. 2 EPV - h - 1 of p | c (h elements of ESZ bytes back
+// from the start of c), 0 <= h < EPV.
+template <int ESZ>
+__device__ __forceinline__ uint4 window_back(const uint4& p, const uint4& c, int h) {
+    if constexpr (ESZ == 2) {
+        switch (h) {
+        case 0: return c;
+        case 1: return window_at<14>(p, c);
+        case 2: return window_at<12>(p, c);
+        case 3: return window_at<10>(p, c);
+        case 4: return window_at<8>(p, c);
+        case 5: return window_at<6>(p, c);
+        case 6: return window_at<4>(p, c);
+        default: return window_at<2>(p, c);
+        }
+    } else {
+        switch (h) {
+        case 0: return c;
+        case 1: return window_at<12>(p, c);
+        case 2: return window_at<8>(p, c);
+        default: return window_at<4>(p, c);
+        }
+    }
+}
+
+// Lane (lane - 1)'s v within the wavefront (lane 0 gets its own), through
+// ds_bpermute.
+__device__ __forceinline__ uint4 from_prev_lane(const uint4& v, int lane) {
+    const int addr = (lane == 0 ? 0 : lane - 1) << 2;
+    return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w));
+}
+
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool ONE_ROW>
+__global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
+    using V = Vec<InT>;
+    constexpr int EPV = V::EPV;    // elements per 16-byte vector
+    constexpr int ESZ = V::BYTES;  // bytes per element
+    constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
+
+    const int waves = a.waves;
+    const int T = waves * 64;
+    const int rpb = ONE_ROW ? 1 : blockDim.x / T;
+    const int tid = threadIdx.x;
+    const int slot = ONE_ROW ? 0 : tid / T;
+    const int lt = tid - slot * T;
+    const int red = slot * waves + (lt >> 6);
+    const int hidden = a.hidden;
+    const int ngv = (hidden + EPV - 1) / EPV;  // gamma's vectors (gamma is 16-byte aligned)
+
+    // gamma's aligned vector d for each of this lane's vectors d (zero past
+    // gamma), raw, held for the block.  A row's window also needs vector
+    // d - 1: lane l - 1 holds it (same k), except for the first lane of each
+    // wavefront, which loads it (an L2 hit).
+    uint4 gc[VPT];
+    const uint4* gv = static_cast<const uint4*>(a.gamma);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int d = lt + k * T;
+        gc[k] = d < ngv ? gv[d] : make_uint4(0, 0, 0, 0);
+    }
+    const int lane = lt & 63;
+
+    __shared__ double red_sum[2][16];
+    __shared__ int red_max[2][16];
+
+    int parity = 0;
+    for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
+        const int64_t row = row0 + slot;
+        const bool active = row < a.rows;
+
+        // the row's phase h and its vectors on the 16-byte grid: the first
+        // holds elements h .. EPV-1 of the row's first EPV - h, the last the
+        // first `tail` of its EPV
+        const char* xr = static_cast<const char*>(a.x) + row * a.x_stride;
+        const int h = (int)((reinterpret_cast<uintptr_t>(xr) & 15) / ESZ);
+        const int nv = (h + hidden + EPV - 1) / EPV;
+        const int tail = h + hidden - (nv - 1) * EPV;
+        // bytes of vector d that belong to the row: [lo, hi)
+        auto lo_of = [&](int d) { return d == 0 ? h * ESZ : 0; };
+        auto hi_of = [&](int d) { return d == nv - 1 ? tail * ESZ : 16; };
+        auto whole = [&](int d) { return (d != 0 || h == 0) && (d != nv - 1 || tail == EPV); };
+
+        float t[VPT][EPV];  // s * g' (zero outside the row)
+        double ssq = 0.0;
+        float amax = 0.0f;
+        if (active) {
+            const char* xb = xr - h * ESZ;  // 16-byte aligned
+            uint4 xv[VPT];
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int d = lt + k * T;
+                xv[k] = d < nv ? load_stream(xb, d) : make_uint4(0, 0, 0, 0);
+            }
+            // all of the row's loads before any store (residual_out may be
+            // x or residual itself)
+            uint4 rv[RESID ? VPT : 1];
+            if constexpr (RESID) {
+                const char* rb = static_cast<const char*>(a.residual) + row * a.residual_stride - h * ESZ;
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int d = lt + k * T;
+                    rv[k] = d < nv ? load_stream(rb, d) : make_uint4(0, 0, 0, 0);
+                }
+            }
+            // gamma vectors d - 1 (only needed off the grid); every lane of
+            // the wavefront takes part in the lane exchange
+            uint4 gp[VPT];
+            if (h != 0) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    gp[k] = from_prev_lane(gc[k], lane);
+                    const int d = lt + k * T;
+                    if (lane == 0) gp[k] = (d >= 1 && d - 1 < ngv) ? gv[d - 1] : make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int d = lt + k * T;
+                if (d < nv && !whole(d)) {
+                    xv[k] = keep_bytes(xv[k], lo_of(d), hi_of(d));
+                    if constexpr (RESID) rv[k] = keep_bytes(rv[k], lo_of(d), hi_of(d));
+                }
+            }
+            if constexpr (RESID) {
+                char* rob = static_cast<char*>(a.residual_out) + row * a.residual_out_stride - h * ESZ;
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int d = lt + k * T;
+                    float xf[EPV], rf[EPV];
+                    V::unpack(xv[k], xf);
+                    V::unpack(rv[k], rf);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) xf[e] += rf[e];
+                    // one rounding of the fp32 sum to the element type
+                    // (bytes outside the row are zero and stay zero)
+                    xv[k] = V::pack(xf);
+                    if (d < nv) {
+                        if (whole(d)) {
+                            store_stream(rob, d, xv[k]);
+                        } else {
+                            const int lo = lo_of(d), hi = hi_of(d);
+                            const uint32_t wd[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+#pragma unroll
+                            for (int e = 0; e < EPV; ++e) {
+                                if (e * ESZ < lo || e * ESZ >= hi) continue;
+                                if constexpr (ESZ == 2)
+                                    reinterpret_cast<uint16_t*>(rob)[d * EPV + e] =
+                                        (uint16_t)(wd[e >> 1] >> (16 * (e & 1)));
+                                else
+                                    reinterpret_cast<uint32_t*>(rob)[d * EPV + e] = wd[e];
+                            }
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int d = lt + k * T;
+                if (d < nv) {
+                    ssq += (double)V::sumsq(xv[k]);
+                    uint4 gw = h != 0 ? window_back<ESZ>(gp[k], gc[k], h) : gc[k];
+                    // gamma' past either end of the row is not gamma (or not
+                    // a number): zero, so that t = 0 there
+                    if (!whole(d)) gw = keep_bytes(gw, lo_of(d), hi_of(d));
+                    float s[EPV], gf[EPV];
+                    V::unpack(xv[k], s);
+                    V::unpack(gw, gf);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) t[k][e] = s[e] * (gf[e] + a.weight_offset);
+                    amax = abs_max<EPV>(amax, t[k]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) t[k][e] = 0.0f;
+                }
+            }
+        }
+
+        ssq = wave_sum(ssq);
+        amax = wave_max_nonneg(amax);
+        if (waves > 1) {  // uniform over the block
+            if ((lt & 63) == 0) {
+                red_sum[parity][red] = ssq;
+                red_max[parity][red] = __float_as_int(amax);
+            }
+            __syncthreads();
+            ssq = 0.0;
+            int m = 0;
+            for (int w = 0; w < waves; ++w) {
+                ssq += red_sum[parity][slot * waves + w];
+                m = max_bits(m, red_max[parity][slot * waves + w]);
+            }
+            amax = __int_as_float(m);
+            // the other parity's slots are rewritten only after the next
+            // barrier, which every wave reaches after finishing these reads
+            parity ^= 1;
+        }
+
+        if (active) {
+            const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
+            double sc = (double)amax * rstd * INV_FMAX;
+            if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
+            uint32_t sbits;
+            const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
+            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
+
+            // codes of vector d start at ob + d * EPV (the host checked that
+            // this is EPV-byte aligned on every row)
+            uint8_t* ob = static_cast<uint8_t*>(a.out) + row * a.out_stride - h;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int d = lt + k * T;
+                if (d >= nv) continue;
+                uint32_t wd[EPV / 4];
+                wd[0] = fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq);
+                if constexpr (EPV == 8)
+                    wd[1] = fp8_x4<FNUZ>(t[k][4] * kq, t[k][5] * kq, t[k][6] * kq, t[k][7] * kq);
+                if (whole(d)) {
+                    if constexpr (EPV == 8)
+                        store_stream(ob, d, make_uint2(wd[0], wd[1]));
+                    else
+                        store_stream(ob, d, wd[0]);
+                } else {
+                    const int lo = lo_of(d) / ESZ, hi = hi_of(d) / ESZ;  // elements
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e)
+                        if (e >= lo && e < hi) ob[d * EPV + e] = (uint8_t)(wd[e >> 2] >> (8 * (e & 3)));
+                }
+            }
+            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+        }
+    }
+}
+
+namespace fp8_phased_launch {
+
+template <typename InT, bool RESID, bool FNUZ, int VPT>
+hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
+    a.waves = s.waves;
+    const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
+    // default: one block per row group
+    int64_t grid = s.grid > 0 ? s.grid : groups;
+    if (grid > groups) grid = groups;
+    if (grid > INT32_MAX) grid = INT32_MAX;
+    if (grid < 1) grid = 1;
+    const dim3 gd((unsigned)grid), bd(s.waves * s.rpb * 64);
+    if (s.rpb == 1)
+        hipLaunchKernelGGL((fp8_phased_kernel<InT, RESID, FNUZ, VPT, true>), gd, bd, 0, stream, a);
+    else
+        hipLaunchKernelGGL((fp8_phased_kernel<InT, RESID, FNUZ, VPT, false>), gd, bd, 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename InT, bool RESID, bool FNUZ>
+hipError_t by_vpt(const FusedArgs& a, Shape s, hipStream_t st) {
+    switch (s.vpt) {
+    case 1: return launch_vpt<InT, RESID, FNUZ, 1>(a, s, st);
+    case 2: return launch_vpt<InT, RESID, FNUZ, 2>(a, s, st);
+    default: return launch_vpt<InT, RESID, FNUZ, 4>(a, s, st);
+    }
+}
+
+}  // namespace fp8_phased_launch
+
+// All phased variants for one input type (one translation unit each).
+template <typename InT>
+hipError_t launch_fp8_phased_typed(const FusedArgs& a, bool residual, bool fnuz, Shape s, hipStream_t stream) {
+    using namespace fp8_phased_launch;
+    if (residual) return fnuz ? by_vpt<InT, true, true>(a, s, stream) : by_vpt<InT, true, false>(a, s, stream);
+    return fnuz ? by_vpt<InT, false, true>(a, s, stream) : by_vpt<InT, false, false>(a, s, stream);
+}
+
+}  // namespace rmsq

@@ -56,7 +56,7 @@ struct Shape {
 };
 
 // Which fused path a shape is chosen for (the rmsq_query_shape `path` values).
-enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3 };
+enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPathFp8Phased = 4, kPathFp8Residual = 5 };
 
 // Pick the automatic shape for a row of nvec 16-byte vectors (or apply the
 // process-wide override).  Returns false if no supported shape holds the row.
@@ -75,6 +75,8 @@ bool choose_elem_shape(int64_t rows, int64_t hidden, Shape* s);
 // Kernel launchers (no argument checks).  Return the hipError_t of the launch.
 hipError_t launch_fp8(const FusedArgs& a, int in_dtype, bool residual, int out_fp8,
                       Shape shape, hipStream_t stream);
+hipError_t launch_fp8_phased(const FusedArgs& a, int in_dtype, bool residual, int out_fp8, Shape shape,
+                             hipStream_t stream);
 hipError_t launch_fp8_elem(const FusedArgs& a, int in_dtype, bool residual, int out_fp8, Shape shape,
                            hipStream_t stream);
 hipError_t launch_fp4(const FusedArgs& a, int in_dtype, bool residual, Fp4Format fmt, Shape shape,

@@ -74,12 +74,21 @@ enum {
  * (Mojo docs "rms_norm_fused_fp8", Args).
  *   rows, hidden : tensor shape; normalization runs over the last dimension.
  *                  Any hidden >= 1 (the page's input_fn is generic in its SIMD
- *                  width).  Rows of whole 16-byte vectors (hidden a multiple
- *                  of 8 for 16-bit, 4 for fp32 input; x, gamma, out 16-byte
- *                  aligned) take the vector kernel; any other hidden, or
- *                  pointers aligned only to the element size, take an
- *                  element-wise kernel with the same results, slower, for
- *                  hidden <= 16384.
+ *                  width).  Three kernels compute the same results:
+ *                  - rows of whole 16-byte vectors (hidden a multiple of 8
+ *                    for 16-bit, 4 for fp32 input; x, gamma, out, residual,
+ *                    residual_out 16-byte aligned): the vector kernel;
+ *                  - otherwise, rows that all sit at x's offset from the
+ *                    16-byte grid (residual, residual_out: the same address
+ *                    modulo 16 and row strides congruent modulo 16 bytes;
+ *                    out: address and row stride congruent to x's element
+ *                    offset and row stride modulo 8 for 16-bit, 4 for fp32
+ *                    input; gamma 16-byte aligned), e.g. any hidden in
+ *                    contiguous tensors: the phased kernel, at close to the
+ *                    vector kernel's rate, hidden <= 32761 (16-bit) or
+ *                    16381 (fp32);
+ *                  - anything else element-aligned: the element-wise kernel
+ *                    (several times slower), hidden <= 16384.
  *   in_dtype     : RMSQ_F32 / RMSQ_F16 / RMSQ_BF16, the type of x and gamma.
  *   x            : [rows, hidden] input.
  *   gamma        : [hidden] weight; the multiplier is gamma + weight_offset,
@@ -306,11 +315,14 @@ int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t wr
 int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks);
 
 /* Launch shape the next call with these arguments would use (for logs).
- * path: 0 for the FP8 entry points on the vector kernel, 1 for rmsnorm_fp4 /
+ * path: 0 for the FP8 entry points without a residual on the vector kernel,
+ * 5 for those with a residual on the vector kernel, 1 for rmsnorm_fp4 /
  * rmsnorm_fp4quant, 2 for residual_rmsnorm_fp4quant, 3 for the FP8 entry
  * points on the element-wise kernel (vectors_per_lane then receives the
  * elements per lane; rmsq_set_tuning's wave count and grid apply to it, its
- * vectors per lane do not).  RMSQ_ERR_VALUE for another path. */
+ * vectors per lane do not), 4 for the FP8 entry points on the phased kernel
+ * (rows at a common offset from the 16-byte grid; see rmsnorm_fp8).
+ * RMSQ_ERR_VALUE for another path. */
 int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path,
                      int* waves_per_row, int* vectors_per_lane, int* rows_per_block);
 

@@ -108,7 +108,8 @@ def test_fp8_shape_errors():
     assert fp8(hidden=-8) == SHAPE
     assert fp8(rows=1 << 62, hidden=1 << 20) == SHAPE
     # any width passes: rows that are not whole 16-byte vectors go to the
-    # element-wise kernel (which the forced one-wave shape cannot hold either)
+    # phased or element-wise kernel (which the forced one-wave shape cannot
+    # hold either)
     assert fp8(hidden=4100) == UNSUP
     assert fp8(hidden=4102, dt=rq.F32) == UNSUP
 
@@ -127,8 +128,9 @@ def test_fp8_unsupported_width():
     assert fp8(hidden=4 * 4096 + 4, dt=rq.F32) == UNSUP
     rq.set_tuning(0, 0, 0)  # automatic shapes: only the width limits remain
     try:
-        assert fp8(hidden=16384 + 2) == UNSUP               # beyond the element-wise kernel
-        assert fp8(hidden=16384 + 8, x=ctypes.c_void_p(BASE + 2)) == UNSUP  # off the vector path
+        assert fp8(hidden=32762) == UNSUP                   # contiguous: beyond the phased kernel
+        off = ctypes.c_void_p(BASE + 2)                     # x off out's phase: the element-wise kernel
+        assert fp8(hidden=16386, x=off) == UNSUP and fp8(hidden=16392, x=off) == UNSUP
     finally:
         rq.set_tuning(1, 1, 0)
 
@@ -261,7 +263,8 @@ def test_residual_fp4quant_errors():
     assert rfp4q(ro=P(0)) == UNSUP and rfp4q(ro=P(4)) == UNSUP
     L = rq.lib()
     q = lambda path: L.rmsq_query_shape(16384, 512, rq.BF16, path, None, None, None)  # fits the forced shape
-    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == OK and q(4) == VALUE
+    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == OK and q(5) == OK and q(6) == VALUE
+    assert q(4) == UNSUP  # the phased kernel's grid holds 65 vectors of a 512-element row: one more than forced
 
 
 def s8(x_stride=4096, r=None, r_stride=4096, ro=None, ro_stride=4096, out_stride=4096, dt=rq.BF16, x=None,
@@ -377,10 +380,12 @@ def test_tuning_and_query_shape():
         rq.set_tuning(1, 1, 0)
 
 
-@pytest.mark.parametrize("fp4", [False, True])
-def test_automatic_shape_fills_simds(fp4):
+@pytest.mark.parametrize("fp4,residual", [(False, False), (False, True), (True, False), (True, True)])
+def test_automatic_shape_fills_simds(fp4, residual):
     """Large batches get blocks of a multiple of 4 wavefronts whose lanes hold
-    the row, with the fewest idle lanes among such shapes."""
+    the row, with the fewest idle lanes among the allowed shapes (FP8 rows of
+    more than 256 vectors: at least 4 waves, and one vector per lane only at
+    4 waves)."""
     rq.set_tuning(0, 0, 0)
     try:
         for dt, epv in ((rq.torch.bfloat16, 8), (rq.torch.float16, 8), (rq.torch.float32, 4)):
@@ -388,19 +393,27 @@ def test_automatic_shape_fills_simds(fp4):
                 continue
             for hidden in range(64 * epv if not fp4 else 128, 4096 * epv + 1, 16 * epv):
                 nvec = hidden // epv
-                s = rq.query_shape(4096, hidden, dt, fp4)
+                s = rq.query_shape(4096, hidden, dt, fp4, residual)
                 w, v, r = s["waves_per_row"], s["vectors_per_lane"], s["rows_per_block"]
                 assert (w * r) % 4 == 0 and w * r <= 16, (hidden, s)
                 assert r == (1 if w >= 4 else 4 // w), (hidden, s)
                 idle = w * 64 * v - nvec
                 assert idle >= 0, (hidden, s)
-                best = min(ww * 64 * vv - nvec for ww in (1, 2, 4, 8, 12, 16) for vv in (1, 2, 4)
-                           if ww * 64 * vv >= nvec)
+                allowed = [(ww, vv) for ww in (1, 2, 4, 8, 12, 16) for vv in (1, 2, 4)
+                           if fp4 or nvec <= 256 or (ww >= 4 and (vv > 1 or ww == 4))]
+                best = min(ww * 64 * vv - nvec for ww, vv in allowed if ww * 64 * vv >= nvec)
                 assert idle == best, (hidden, s, best)
+                assert (w, v) in allowed, (hidden, s)
         # the measured preferences on ties
-        assert rq.query_shape(8192, 4096, rq.torch.bfloat16)["vectors_per_lane"] == 2
-        assert rq.query_shape(16384, 7168, rq.torch.bfloat16, True) == {
-            "waves_per_row": 4, "vectors_per_lane": 4, "rows_per_block": 1}
+        q = lambda rows, h, dt, fp4=False, res=False: rq.query_shape(rows, h, dt, fp4, res)
+        shape = lambda s: (s["waves_per_row"], s["vectors_per_lane"])
+        assert shape(q(8192, 4096, rq.torch.bfloat16)) == (4, 2)
+        assert shape(q(8192, 4096, rq.torch.bfloat16, res=True)) == (4, 2)
+        assert shape(q(16384, 8192, rq.torch.bfloat16)) == (4, 4)
+        assert shape(q(16384, 8192, rq.torch.bfloat16, res=True)) == (8, 2)
+        assert shape(q(16384, 16384, rq.torch.bfloat16)) == (8, 4)
+        assert shape(q(16384, 8192, rq.torch.float32, res=True)) == (16, 2)
+        assert shape(q(16384, 7168, rq.torch.bfloat16, True)) == (4, 4)
     finally:
         rq.set_tuning(1, 1, 0)
 
