@@ -284,25 +284,31 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
             // large batches: blocks of a multiple of 4 wavefronts, so the 4
             // SIMDs of a CU get equal work (odd counts measured 20-35% slower
             // on MI355X).  Among those shapes whose lanes hold the row, the one
-            // with the fewest idle lanes; ties go to 2 vectors per lane for
-            // residual FP8 and FP4 and to 4 for FP4 (the faster ones
-            // measured; residual FP4 holds two inputs per row and stays
-            // within its registers that way).  FP8 rows of more than 256
-            // vectors take at least 4 waves, one vector per lane only at 4
-            // waves, and without a residual prefer 4 vectors per lane
-            // (measured on MI355X, bf16: 12 x 1 runs 640- and 768-vector rows
-            // 1.1-1.5x slower than 8 x 2 / 4 x 4, 16 x 2 a 2048-vector row
-            // 1.3x slower than 8 x 4 without a residual).
-            const int order_2[3] = {2, 4, 1}, order_4[3] = {4, 2, 1};
-            const bool fp8 = path == kPathFp8 || path == kPathFp8Residual;
-            const int* order =
-                (path == kPathFp4 || (path == kPathFp8 && nvec > 256)) ? order_4 : order_2;
+            // with the fewest idle lanes; ties go to the vectors per lane
+            // measured fastest on MI355X (bf16, 2048-16384 elements):
+            //   rows of up to 256 vectors: 2, then 4, then 1 (FP4: 4, 2, 1);
+            //   longer rows take at least 4 waves, and
+            //     FP8 and FP4 without a residual: 4, 2, then 1 at 4 waves only
+            //     (12 x 1 ran 640- and 768-vector rows 1.3-1.5x slower than
+            //     4 x 4, 16 x 2 a 2048-vector row 1.3x slower than 8 x 4);
+            //     FP8 with a residual: 2, 4, then 1 at 4 waves only (12 x 1
+            //     ran 640- and 768-vector rows 1.13x slower than 8 x 2);
+            //     FP4 with a residual: 1, 2, 4 (it holds two inputs per row:
+            //     12 x 1 ran a 640-vector row 1.2x faster than 8 x 2, 16 x 1
+            //     an 896-vector row 1.1x faster).
+            const int order_2[3] = {2, 4, 1}, order_4[3] = {4, 2, 1}, order_1[3] = {1, 2, 4};
+            const bool wide = nvec > 256;
+            const int* order = !wide ? (path == kPathFp4 ? order_4 : order_2)
+                               : path == kPathFp4Residual ? order_1
+                               : (path == kPathFp4 || path == kPathFp8) ? order_4
+                                                                        : order_2;
+            const bool one_at_4 = wide && path != kPathFp4Residual;  // 1 vector per lane only at 4 waves
             int64_t best_idle = INT64_MAX;
             waves = 0;
             for (int i = 0; i < 3; ++i) {
                 const int v = order[i];
                 for (int w : {1, 2, 4, 8, 12, 16}) {
-                    if (fp8 && nvec > 256 && (w < 4 || (v == 1 && w > 4))) continue;
+                    if (wide && (w < 4 || (one_at_4 && v == 1 && w > 4))) continue;
                     const int64_t idle = (int64_t)w * 64 * v - nvec;
                     if (idle >= 0 && idle < best_idle) {
                         best_idle = idle;

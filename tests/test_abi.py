@@ -383,9 +383,9 @@ def test_tuning_and_query_shape():
 @pytest.mark.parametrize("fp4,residual", [(False, False), (False, True), (True, False), (True, True)])
 def test_automatic_shape_fills_simds(fp4, residual):
     """Large batches get blocks of a multiple of 4 wavefronts whose lanes hold
-    the row, with the fewest idle lanes among the allowed shapes (FP8 rows of
-    more than 256 vectors: at least 4 waves, and one vector per lane only at
-    4 waves)."""
+    the row, with the fewest idle lanes among the allowed shapes (rows of
+    more than 256 vectors: at least 4 waves, and, except for residual FP4,
+    one vector per lane only at 4 waves)."""
     rq.set_tuning(0, 0, 0)
     try:
         for dt, epv in ((rq.torch.bfloat16, 8), (rq.torch.float16, 8), (rq.torch.float32, 4)):
@@ -400,7 +400,7 @@ def test_automatic_shape_fills_simds(fp4, residual):
                 idle = w * 64 * v - nvec
                 assert idle >= 0, (hidden, s)
                 allowed = [(ww, vv) for ww in (1, 2, 4, 8, 12, 16) for vv in (1, 2, 4)
-                           if fp4 or nvec <= 256 or (ww >= 4 and (vv > 1 or ww == 4))]
+                           if nvec <= 256 or (ww >= 4 and (vv > 1 or ww == 4 or (fp4 and residual)))]
                 best = min(ww * 64 * vv - nvec for ww, vv in allowed if ww * 64 * vv >= nvec)
                 assert idle == best, (hidden, s, best)
                 assert (w, v) in allowed, (hidden, s)
@@ -414,6 +414,9 @@ def test_automatic_shape_fills_simds(fp4, residual):
         assert shape(q(16384, 16384, rq.torch.bfloat16)) == (8, 4)
         assert shape(q(16384, 8192, rq.torch.float32, res=True)) == (16, 2)
         assert shape(q(16384, 7168, rq.torch.bfloat16, True)) == (4, 4)
+        assert shape(q(16384, 7168, rq.torch.bfloat16, True, True)) == (16, 1)
+        assert shape(q(16384, 5120, rq.torch.bfloat16, True)) == (4, 4)
+        assert shape(q(16384, 16384, rq.torch.bfloat16, True, True)) == (16, 2)
     finally:
         rq.set_tuning(1, 1, 0)
 

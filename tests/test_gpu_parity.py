@@ -128,6 +128,26 @@ def test_fp4_ragged(dt, rows, hidden):
     check_fp4(w, inp, None, label=f"fp4 {dt} {rows}x{hidden} gs=None")
 
 
+@pytest.mark.parametrize("dt,hidden", [("bf16", 5120), ("bf16", 6144), ("bf16", 16384), ("f16", 3072),
+                                       ("f32", 3072), ("f32", 7168)])
+def test_automatic_large_batch_shapes(dt, hidden):
+    """Batches above 256 rows of widths whose automatic shapes differ by
+    path (4 x 4, 8 x 2, 8 x 4, 12 x 1, 16 x 1 ...), every element checked."""
+    rows = 260
+    for op in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "residual_rmsnorm_fp4"):
+        fp4, resid = op.endswith("fp4"), op.startswith("residual")
+        if fp4 and dt == "f32" and hidden > 8192:
+            continue
+        w = _wl(op, rows, hidden, dt)
+        inp = _rand_inputs(rows, hidden, dt, seed=hidden + len(op), resid=resid)
+        s = rq.query_shape(rows, hidden, workloads.TORCH_DTYPES[dt], fp4, resid)
+        say(f"[large batch] {op} {dt} {rows}x{hidden} shape {s}")
+        if fp4:
+            check_fp4(w, inp, fp4_gs_for(inp, w), label=f"{op} {dt} {hidden} {s}")
+        else:
+            check_fp8(w, inp, label=f"{op} {dt} {hidden} {s}")
+
+
 @pytest.mark.parametrize("dt,hidden", [("bf16", 32768), ("f16", 32768), ("f32", 16384)])
 def test_largest_hidden(dt, hidden):
     w = _wl("residual_rmsnorm_fp8", 5, hidden, dt)
