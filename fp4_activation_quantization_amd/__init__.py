@@ -348,13 +348,13 @@ def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, grid_blocks: i
 
 
 def query_shape(rows: int, hidden: int, dtype: torch.dtype, fp4: bool = False, residual: bool = False,
-                elementwise: bool = False, phased: bool = False) -> dict:
+                elementwise: bool = False) -> dict:
     """Launch shape of the FP8 (fp4=False) or FP4 path with or without a
-    residual; for FP8, phased selects the phased kernel and elementwise the
-    element-wise kernel (vectors_per_lane is then elements per lane; neither
-    depends on the residual)."""
+    residual; for FP8 (any hidden) the vector / phased kernels' shape, or with
+    elementwise the element-wise kernel's (vectors_per_lane is then elements
+    per lane; it does not depend on the residual)."""
     w, v, r = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    path = (2 if residual else 1) if fp4 else (3 if elementwise else 4 if phased else 5 if residual else 0)
+    path = (2 if residual else 1) if fp4 else (3 if elementwise else 5 if residual else 0)
     _check("rmsq_query_shape", lib().rmsq_query_shape(rows, hidden, _DT[dtype], path, ctypes.byref(w),
                                                       ctypes.byref(v), ctypes.byref(r)))
     return {"waves_per_row": w.value, "vectors_per_lane": v.value, "rows_per_block": r.value}

@@ -107,7 +107,7 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     auto same_phase = [&](const void* p, int64_t stride) {
         return reinterpret_cast<uintptr_t>(p) % 16 == xph && ((stride - x_stride) * esz) % 16 == 0;
     };
-    const int64_t phased_nvec = ceil_div(hidden + epv - 1, epv);  // the grid vectors a row can touch
+    const int64_t phased_nvec = ceil_div(hidden, epv);  // lanes as for a whole-vector row
     const bool phased = !vec && phased_nvec <= kMaxVec && aligned(gamma, 16) &&
                         (int64_t)(reinterpret_cast<uintptr_t>(out) % epv) == (int64_t)(xph / esz) % epv &&
                         (out_stride - x_stride) % epv == 0 &&
@@ -135,7 +135,7 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     }
 
     Shape shape;
-    const int path = !vec ? kPathFp8Phased : resid ? kPathFp8Residual : kPathFp8;
+    const int path = resid ? kPathFp8Residual : kPathFp8;
     if ((vec || phased) ? !choose_shape(rows, nvec, path, &shape)
                         : !choose_elem_shape(rows, hidden, &shape))
         return RMSQ_ERR_UNSUPPORTED;
@@ -266,20 +266,6 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
             // 8 x 2 on MI355X, 3.0 us as 16 x 1 and 2.8 us as 4 x 4)
             vpt = nvec <= 64 ? 1 : (nvec <= 16 * 64 * 2 ? 2 : 4);
             waves = (int)std::min<int64_t>(16, ceil_div(nvec, 64 * vpt));
-        } else if (path == kPathFp8Phased) {
-            // the phased kernel: the fewest waves that hold the row at up to
-            // 4 vectors per lane, then the fewest vectors per lane (measured
-            // on MI355X: a 513-vector row runs 1.2-1.3x faster as 4 x 4 than
-            // as 12 x 1, the shape with the fewest idle lanes)
-            waves = 0;
-            for (int w : {1, 2, 4, 8, 12, 16}) {
-                if ((int64_t)w * 64 * 4 >= nvec) {
-                    waves = w;
-                    break;
-                }
-            }
-            if (waves == 0) return false;
-            vpt = vpt_for(nvec, waves);
         } else {
             // large batches: blocks of a multiple of 4 wavefronts, so the 4
             // SIMDs of a CU get equal work (odd counts measured 20-35% slower
@@ -507,23 +493,15 @@ int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path, int* 
         if (rows_per_block) *rows_per_block = s.rpb;
         return RMSQ_OK;
     }
-    if (path == kPathFp8Phased) {
-        if (hidden <= 0) return RMSQ_ERR_SHAPE;
-        const int64_t epv = elems_per_vec(in_dtype), nv = ceil_div(hidden + epv - 1, epv);
-        if (nv > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
-        Shape s;
-        if (!choose_shape(rows, (int)nv, kPathFp8Phased, &s)) return RMSQ_ERR_UNSUPPORTED;
-        if (waves_per_row) *waves_per_row = s.waves;
-        if (vectors_per_lane) *vectors_per_lane = s.vpt;
-        if (rows_per_block) *rows_per_block = s.rpb;
-        return RMSQ_OK;
-    }
-    if (hidden <= 0 || hidden % elems_per_vec(in_dtype) != 0) return RMSQ_ERR_SHAPE;
-    const int64_t nvec = hidden / elems_per_vec(in_dtype);
-    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
-    Shape s;
     if (path != kPathFp8 && path != kPathFp4 && path != kPathFp4Residual && path != kPathFp8Residual)
         return RMSQ_ERR_VALUE;
+    // FP8 rows of any width (the vector and phased kernels hold a row in the
+    // lanes of ceil(hidden / vector width) vectors); FP4 rows whole vectors
+    const bool fp8 = path == kPathFp8 || path == kPathFp8Residual;
+    if (hidden <= 0 || (!fp8 && hidden % elems_per_vec(in_dtype) != 0)) return RMSQ_ERR_SHAPE;
+    const int64_t nvec = ceil_div(hidden, elems_per_vec(in_dtype));
+    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    Shape s;
     if (!choose_shape(rows, (int)nvec, path, &s)) return RMSQ_ERR_UNSUPPORTED;
     if (waves_per_row) *waves_per_row = s.waves;
     if (vectors_per_lane) *vectors_per_lane = s.vpt;

@@ -9,39 +9,41 @@
 // "allreduce_residual_rmsnorm_fp8".  Their input_fn is generic in its SIMD
 // width, so a row need not be a whole number of vectors.
 //
-// Work mapping: as the vector kernel, on the 16-byte grid rather than on the
-// row.  A row whose first element lies h elements past a 16-byte boundary
-// covers nv = ceil((h + hidden) / EPV) aligned vectors; lane l owns vectors
-// l, l + T, ... of them.  Interior vectors are whole; in the first and the
-// last, the bytes outside the row are zeroed after the load (the aligned
-// 16 bytes around an element of the row never leave its page, so these
-// loads cannot fault) and only the row's own elements are stored back, one
-// by one, so rows that share a vector never write each other's elements.
-// Codes and residual_out are stored 8 / 16 bytes at a time: the host takes
-// this kernel only when every tensor has x's phase (codes: the same offset
-// modulo the code bytes of a vector).  gamma' for the lane's vector is the
-// window h elements back across gamma's aligned vectors d - 1 and d (d held
-// by the lane, d - 1 by the previous lane), cut with byte funnel shifts
-// (v_alignbyte_b32) chosen by a switch on h, which is uniform over the
-// wavefronts of a row.
+// Work mapping: a row whose first element lies h elements past a 16-byte
+// boundary has a head of EPV - h elements (none for h = 0) before the next
+// boundary; the first lanes of the row group take one head element each
+// (element loads and stores).  From the boundary on, the row is the vector
+// kernel's: lane l owns the aligned vectors l, l + T, ..., all whole but the
+// last, whose bytes past the row are zeroed after the load (the aligned 16
+// bytes around an element of the row never leave its page, so the load
+// cannot fault) and whose own elements are stored one by one, so rows that
+// share a vector never write each other's elements.  A row thus needs the
+// lanes of a ceil(hidden / EPV)-vector row, like an aligned one.  Codes and
+// residual_out are stored 8 / 16 bytes at a time: the host takes this kernel
+// only when every tensor has x's phase (codes: the same offset modulo the
+// code bytes of a vector).  gamma' for a vector starts `head` elements into
+// gamma's aligned vector d and runs into d + 1 (held by the next lane, loaded
+// by the last lane of a wavefront); the window is cut with byte funnel
+// shifts (v_alignbyte_b32) chosen by a switch on the head, which is uniform
+// over the wavefronts of a row.
 #pragma once
 
 #include "rmsq_device.h"
+#include "rmsq_elem.h"
 #include "rmsq_internal.h"
 
 namespace rmsq {
 
-// Bytes [lo, hi) of a 16-byte vector kept, the others zeroed (dword w holds
-// bytes 4w .. 4w+3).
-__device__ __forceinline__ uint32_t dword_keep(int lo, int hi, int w) {
-    const int a = max(lo - 4 * w, 0), b = min(hi - 4 * w, 4);
-    return b > a ? (0xFFFFFFFFu >> (32 - 8 * (b - a))) << (8 * a) : 0u;
+// The low `hi` bytes of a 16-byte vector kept, the others zeroed.
+__device__ __forceinline__ uint32_t dword_keep_low(int hi, int w) {
+    const int b = min(max(hi - 4 * w, 0), 4);
+    return b == 4 ? 0xFFFFFFFFu : (1u << (8 * b)) - 1u;
 }
-__device__ __forceinline__ uint4 keep_bytes(uint4 v, int lo, int hi) {
-    v.x &= dword_keep(lo, hi, 0);
-    v.y &= dword_keep(lo, hi, 1);
-    v.z &= dword_keep(lo, hi, 2);
-    v.w &= dword_keep(lo, hi, 3);
+__device__ __forceinline__ uint4 keep_low_bytes(uint4 v, int hi) {
+    v.x &= dword_keep_low(hi, 0);
+    v.y &= dword_keep_low(hi, 1);
+    v.z &= dword_keep_low(hi, 2);
+    v.w &= dword_keep_low(hi, 3);
     return v;
 }
 
@@ -58,35 +60,34 @@ __device__ __forceinline__ uint4 window_at(const uint4& p, const uint4& c) {
     }
 }
 
-// Elements EPV - h .. 2 EPV - h - 1 of p | c (h elements of ESZ bytes back
-// from the start of c), 0 <= h < EPV.
+// Elements s .. s + EPV - 1 of p | c (elements of ESZ bytes), 0 <= s < EPV.
 template <int ESZ>
-__device__ __forceinline__ uint4 window_back(const uint4& p, const uint4& c, int h) {
+__device__ __forceinline__ uint4 window_from(const uint4& p, const uint4& c, int s) {
     if constexpr (ESZ == 2) {
-        switch (h) {
-        case 0: return c;
-        case 1: return window_at<14>(p, c);
-        case 2: return window_at<12>(p, c);
-        case 3: return window_at<10>(p, c);
+        switch (s) {
+        case 0: return p;
+        case 1: return window_at<2>(p, c);
+        case 2: return window_at<4>(p, c);
+        case 3: return window_at<6>(p, c);
         case 4: return window_at<8>(p, c);
-        case 5: return window_at<6>(p, c);
-        case 6: return window_at<4>(p, c);
-        default: return window_at<2>(p, c);
+        case 5: return window_at<10>(p, c);
+        case 6: return window_at<12>(p, c);
+        default: return window_at<14>(p, c);
         }
     } else {
-        switch (h) {
-        case 0: return c;
-        case 1: return window_at<12>(p, c);
+        switch (s) {
+        case 0: return p;
+        case 1: return window_at<4>(p, c);
         case 2: return window_at<8>(p, c);
-        default: return window_at<4>(p, c);
+        default: return window_at<12>(p, c);
         }
     }
 }
 
-// Lane (lane - 1)'s v within the wavefront (lane 0 gets its own), through
+// Lane (lane + 1)'s v within the wavefront (lane 63 gets its own), through
 // ds_bpermute.
-__device__ __forceinline__ uint4 from_prev_lane(const uint4& v, int lane) {
-    const int addr = (lane == 0 ? 0 : lane - 1) << 2;
+__device__ __forceinline__ uint4 from_next_lane(const uint4& v, int lane) {
+    const int addr = (lane == 63 ? 63 : lane + 1) << 2;
     return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x),
                       (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y),
                       (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z),
@@ -96,6 +97,8 @@ __device__ __forceinline__ uint4 from_prev_lane(const uint4& v, int lane) {
 template <typename InT, bool RESID, bool FNUZ, int VPT, bool ONE_ROW>
 __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
     using V = Vec<InT>;
+    using E = Elem<InT>;
+    using Bits = typename E::Bits;
     constexpr int EPV = V::EPV;    // elements per 16-byte vector
     constexpr int ESZ = V::BYTES;  // bytes per element
     constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
@@ -109,19 +112,9 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
     const int red = slot * waves + (lt >> 6);
     const int hidden = a.hidden;
     const int ngv = (hidden + EPV - 1) / EPV;  // gamma's vectors (gamma is 16-byte aligned)
-
-    // gamma's aligned vector d for each of this lane's vectors d (zero past
-    // gamma), raw, held for the block.  A row's window also needs vector
-    // d - 1: lane l - 1 holds it (same k), except for the first lane of each
-    // wavefront, which loads it (an L2 hit).
-    uint4 gc[VPT];
-    const uint4* gv = static_cast<const uint4*>(a.gamma);
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int d = lt + k * T;
-        gc[k] = d < ngv ? gv[d] : make_uint4(0, 0, 0, 0);
-    }
     const int lane = lt & 63;
+
+    const uint4* gv = static_cast<const uint4*>(a.gamma);
 
     __shared__ double red_sum[2][16];
     __shared__ int red_max[2][16];
@@ -131,61 +124,69 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
         const int64_t row = row0 + slot;
         const bool active = row < a.rows;
 
-        // the row's phase h and its vectors on the 16-byte grid: the first
-        // holds elements h .. EPV-1 of the row's first EPV - h, the last the
-        // first `tail` of its EPV
+        // the row's head (elements before its first 16-byte boundary) and
+        // the aligned vectors from there on: all whole but the last, which
+        // holds `tail` of the row's elements
         const char* xr = static_cast<const char*>(a.x) + row * a.x_stride;
         const int h = (int)((reinterpret_cast<uintptr_t>(xr) & 15) / ESZ);
-        const int nv = (h + hidden + EPV - 1) / EPV;
-        const int tail = h + hidden - (nv - 1) * EPV;
-        // bytes of vector d that belong to the row: [lo, hi)
-        auto lo_of = [&](int d) { return d == 0 ? h * ESZ : 0; };
-        auto hi_of = [&](int d) { return d == nv - 1 ? tail * ESZ : 16; };
-        auto whole = [&](int d) { return (d != 0 || h == 0) && (d != nv - 1 || tail == EPV); };
+        const int head = min(h != 0 ? EPV - h : 0, hidden);
+        const int nv = (hidden - head + EPV - 1) / EPV;
+        const int tail = hidden - head - (nv - 1) * EPV;
+        auto whole = [&](int d) { return d != nv - 1 || tail == EPV; };
 
         float t[VPT][EPV];  // s * g' (zero outside the row)
+        float ht = 0.0f;    // the head element's s * g' (lanes lt < head)
         double ssq = 0.0;
         float amax = 0.0f;
         if (active) {
-            const char* xb = xr - h * ESZ;  // 16-byte aligned
+            const char* xb = xr + head * ESZ;  // 16-byte aligned
             uint4 xv[VPT];
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int d = lt + k * T;
                 xv[k] = d < nv ? load_stream(xb, d) : make_uint4(0, 0, 0, 0);
             }
+            Bits hx = 0, hr = 0, hg = 0;
+            if (lt < head) {
+                hx = load_elem(reinterpret_cast<const Bits*>(xr) + lt);
+                hg = static_cast<const Bits*>(a.gamma)[lt];
+            }
             // all of the row's loads before any store (residual_out may be
             // x or residual itself)
             uint4 rv[RESID ? VPT : 1];
+            const char* rr = RESID ? static_cast<const char*>(a.residual) + row * a.residual_stride : nullptr;
             if constexpr (RESID) {
-                const char* rb = static_cast<const char*>(a.residual) + row * a.residual_stride - h * ESZ;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
                     const int d = lt + k * T;
-                    rv[k] = d < nv ? load_stream(rb, d) : make_uint4(0, 0, 0, 0);
+                    rv[k] = d < nv ? load_stream(rr + head * ESZ, d) : make_uint4(0, 0, 0, 0);
                 }
+                if (lt < head) hr = load_elem(reinterpret_cast<const Bits*>(rr) + lt);
             }
-            // gamma vectors d - 1 (only needed off the grid); every lane of
-            // the wavefront takes part in the lane exchange
-            uint4 gp[VPT];
-            if (h != 0) {
+            // gamma's aligned vector d for each of this lane's vectors (zero
+            // past gamma; L2 hits), loaded with the row so that its latency
+            // overlaps the row's.  A row with a head also needs vector d + 1,
+            // which the next lane holds; the last lane of a wavefront loads it.
+            uint4 gc[VPT], gn[VPT];
 #pragma unroll
-                for (int k = 0; k < VPT; ++k) {
-                    gp[k] = from_prev_lane(gc[k], lane);
-                    const int d = lt + k * T;
-                    if (lane == 0) gp[k] = (d >= 1 && d - 1 < ngv) ? gv[d - 1] : make_uint4(0, 0, 0, 0);
-                }
+            for (int k = 0; k < VPT; ++k) {
+                const int d = lt + k * T;
+                gc[k] = d < ngv ? gv[d] : make_uint4(0, 0, 0, 0);
+                gn[k] = make_uint4(0, 0, 0, 0);
+                if (head != 0 && lane == 63 && d + 1 < ngv) gn[k] = gv[d + 1];
             }
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int d = lt + k * T;
                 if (d < nv && !whole(d)) {
-                    xv[k] = keep_bytes(xv[k], lo_of(d), hi_of(d));
-                    if constexpr (RESID) rv[k] = keep_bytes(rv[k], lo_of(d), hi_of(d));
+                    xv[k] = keep_low_bytes(xv[k], tail * ESZ);
+                    if constexpr (RESID) rv[k] = keep_low_bytes(rv[k], tail * ESZ);
                 }
             }
+            float hs = E::widen(hx);
             if constexpr (RESID) {
-                char* rob = static_cast<char*>(a.residual_out) + row * a.residual_out_stride - h * ESZ;
+                char* ro = static_cast<char*>(a.residual_out) + row * a.residual_out_stride;
+                char* rob = ro + head * ESZ;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
                     const int d = lt + k * T;
@@ -195,17 +196,16 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) xf[e] += rf[e];
                     // one rounding of the fp32 sum to the element type
-                    // (bytes outside the row are zero and stay zero)
+                    // (bytes past the row are zero and stay zero)
                     xv[k] = V::pack(xf);
                     if (d < nv) {
                         if (whole(d)) {
                             store_stream(rob, d, xv[k]);
                         } else {
-                            const int lo = lo_of(d), hi = hi_of(d);
                             const uint32_t wd[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
 #pragma unroll
                             for (int e = 0; e < EPV; ++e) {
-                                if (e * ESZ < lo || e * ESZ >= hi) continue;
+                                if (e >= tail) continue;
                                 if constexpr (ESZ == 2)
                                     reinterpret_cast<uint16_t*>(rob)[d * EPV + e] =
                                         (uint16_t)(wd[e >> 1] >> (16 * (e & 1)));
@@ -215,16 +215,29 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
                         }
                     }
                 }
+                if (lt < head) {
+                    const Bits sb = E::round(hs + E::widen(hr));
+                    store_elem(reinterpret_cast<Bits*>(ro) + lt, sb);
+                    hs = E::widen(sb);
+                }
+            }
+            // every lane of the wavefront takes part in the lane exchange
+            if (head != 0) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const uint4 nx = from_next_lane(gc[k], lane);
+                    if (lane != 63) gn[k] = nx;
+                }
             }
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int d = lt + k * T;
                 if (d < nv) {
                     ssq += (double)V::sumsq(xv[k]);
-                    uint4 gw = h != 0 ? window_back<ESZ>(gp[k], gc[k], h) : gc[k];
-                    // gamma' past either end of the row is not gamma (or not
-                    // a number): zero, so that t = 0 there
-                    if (!whole(d)) gw = keep_bytes(gw, lo_of(d), hi_of(d));
+                    uint4 gw = head != 0 ? window_from<ESZ>(gc[k], gn[k], head) : gc[k];
+                    // gamma' past the row is not gamma (or not a number):
+                    // zero, so that t = 0 there
+                    if (!whole(d)) gw = keep_low_bytes(gw, tail * ESZ);
                     float s[EPV], gf[EPV];
                     V::unpack(xv[k], s);
                     V::unpack(gw, gf);
@@ -235,6 +248,11 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) t[k][e] = 0.0f;
                 }
+            }
+            if (lt < head) {
+                ssq += (double)hs * (double)hs;
+                ht = hs * (E::widen(hg) + a.weight_offset);
+                amax = fmaxf(amax, fabsf(ht));
             }
         }
 
@@ -266,9 +284,10 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
             const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
             const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
 
+            uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
             // codes of vector d start at ob + d * EPV (the host checked that
             // this is EPV-byte aligned on every row)
-            uint8_t* ob = static_cast<uint8_t*>(a.out) + row * a.out_stride - h;
+            uint8_t* ob = orow + head;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int d = lt + k * T;
@@ -283,12 +302,12 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
                     else
                         store_stream(ob, d, wd[0]);
                 } else {
-                    const int lo = lo_of(d) / ESZ, hi = hi_of(d) / ESZ;  // elements
 #pragma unroll
                     for (int e = 0; e < EPV; ++e)
-                        if (e >= lo && e < hi) ob[d * EPV + e] = (uint8_t)(wd[e >> 2] >> (8 * (e & 3)));
+                        if (e < tail) ob[d * EPV + e] = (uint8_t)(wd[e >> 2] >> (8 * (e & 3)));
                 }
             }
+            if (lt < head) orow[lt] = (uint8_t)fp8_x4<FNUZ>(ht * kq, 0.0f, 0.0f, 0.0f);
             if (lt == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
         }
     }

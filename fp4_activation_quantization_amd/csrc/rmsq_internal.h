@@ -56,7 +56,7 @@ struct Shape {
 };
 
 // Which fused path a shape is chosen for (the rmsq_query_shape `path` values).
-enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPathFp8Phased = 4, kPathFp8Residual = 5 };
+enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPathFp8Residual = 5 };
 
 // Pick the automatic shape for a row of nvec 16-byte vectors (or apply the
 // process-wide override).  Returns false if no supported shape holds the row.

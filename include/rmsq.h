@@ -85,8 +85,7 @@ enum {
  *                    offset and row stride modulo 8 for 16-bit, 4 for fp32
  *                    input; gamma 16-byte aligned), e.g. any hidden in
  *                    contiguous tensors: the phased kernel, at close to the
- *                    vector kernel's rate, hidden <= 32761 (16-bit) or
- *                    16381 (fp32);
+ *                    vector kernel's rate, up to the same widths;
  *                  - anything else element-aligned: the element-wise kernel
  *                    (several times slower), hidden <= 16384.
  *   in_dtype     : RMSQ_F32 / RMSQ_F16 / RMSQ_BF16, the type of x and gamma.
@@ -315,14 +314,13 @@ int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t wr
 int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks);
 
 /* Launch shape the next call with these arguments would use (for logs).
- * path: 0 for the FP8 entry points without a residual on the vector kernel,
- * 5 for those with a residual on the vector kernel, 1 for rmsnorm_fp4 /
- * rmsnorm_fp4quant, 2 for residual_rmsnorm_fp4quant, 3 for the FP8 entry
- * points on the element-wise kernel (vectors_per_lane then receives the
- * elements per lane; rmsq_set_tuning's wave count and grid apply to it, its
- * vectors per lane do not), 4 for the FP8 entry points on the phased kernel
- * (rows at a common offset from the 16-byte grid; see rmsnorm_fp8).
- * RMSQ_ERR_VALUE for another path. */
+ * path: 0 for the FP8 entry points without a residual and 5 for those with
+ * one, on the vector or phased kernel (any hidden; see rmsnorm_fp8), 1 for
+ * rmsnorm_fp4 / rmsnorm_fp4quant, 2 for residual_rmsnorm_fp4quant, 3 for
+ * the FP8 entry points on the element-wise kernel (vectors_per_lane then
+ * receives the elements per lane; rmsq_set_tuning's wave count and grid
+ * apply to it, its vectors per lane do not).  RMSQ_ERR_VALUE for another
+ * path. */
 int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path,
                      int* waves_per_row, int* vectors_per_lane, int* rows_per_block);
 

@@ -128,7 +128,7 @@ def test_fp8_unsupported_width():
     assert fp8(hidden=4 * 4096 + 4, dt=rq.F32) == UNSUP
     rq.set_tuning(0, 0, 0)  # automatic shapes: only the width limits remain
     try:
-        assert fp8(hidden=32762) == UNSUP                   # contiguous: beyond the phased kernel
+        assert fp8(hidden=32770) == UNSUP                   # contiguous: beyond the phased kernel
         off = ctypes.c_void_p(BASE + 2)                     # x off out's phase: the element-wise kernel
         assert fp8(hidden=16386, x=off) == UNSUP and fp8(hidden=16392, x=off) == UNSUP
     finally:
@@ -263,8 +263,11 @@ def test_residual_fp4quant_errors():
     assert rfp4q(ro=P(0)) == UNSUP and rfp4q(ro=P(4)) == UNSUP
     L = rq.lib()
     q = lambda path: L.rmsq_query_shape(16384, 512, rq.BF16, path, None, None, None)  # fits the forced shape
-    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == OK and q(5) == OK and q(6) == VALUE
-    assert q(4) == UNSUP  # the phased kernel's grid holds 65 vectors of a 512-element row: one more than forced
+    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == OK and q(5) == OK
+    assert q(4) == VALUE and q(6) == VALUE
+    # FP8 takes any width: 513 elements need 65 vectors' lanes, one more than forced
+    assert L.rmsq_query_shape(16384, 513, rq.BF16, 0, None, None, None) == UNSUP
+    assert L.rmsq_query_shape(16384, 513, rq.BF16, 1, None, None, None) == SHAPE
 
 
 def s8(x_stride=4096, r=None, r_stride=4096, ro=None, ro_stride=4096, out_stride=4096, dt=rq.BF16, x=None,

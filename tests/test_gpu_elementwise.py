@@ -171,7 +171,7 @@ def test_forced_shapes_and_row_strided_grid(waves, vpt, blocks):
     inp = _inputs(201, h, "f16", seed=29, resid=True)
     rq.set_tuning(waves, vpt, blocks)
     say(f"[shape] waves={waves} vpt={vpt} blocks={blocks}")
-    s = rq.query_shape(201, h, torch.float16, phased=True)
+    s = rq.query_shape(201, h, torch.float16, residual=True)
     assert s["waves_per_row"] == waves and (vpt == 0 or s["vectors_per_lane"] == vpt)
     check_fp8(w, inp, label=f"phased {waves}x{vpt} / {blocks} blocks")
     s = rq.query_shape(201, h, torch.float16, elementwise=True)
