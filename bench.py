@@ -299,10 +299,19 @@ def cpu_baseline(min_seconds: float) -> dict:
         if dt >= min_seconds:
             break
     per_pass = dt / passes
+    # one thread on the first rows, for the per-core rate
+    n1 = min(w.rows, 1024)
+    t1 = time.perf_counter()
+    oracle.rmsnorm_fp8(x[:n1], g, in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset, scale_ub=w.scale_ub,
+                       out_fmt=w.out_fmt, scales_dtype=w.scales_dtype, residual=r[:n1], threads=1, want_q=False)
+    d1 = time.perf_counter() - t1
+    row_bytes = algorithmic_bytes(w) / w.rows
     return {"value": round(algorithmic_bytes(w) / per_pass / 1e9, 6), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "rows_per_s": round(w.rows / per_pass, 1), "seconds": round(dt, 2),
             "sample": f"the whole {w.name} workload ({w.rows} rows), {passes} pass(es), float64 C oracle "
-                      f"split by rows over {threads} threads"}
+                      f"split by rows over {threads} threads",
+            "single_thread": {"value": round(row_bytes * n1 / d1 / 1e9, 6), "unit": "GB/s",
+                              "rows_per_s": round(n1 / d1, 1), "sample": f"the first {n1} rows, one thread"}}
 
 
 def copy_calibration(nbytes: int, steps: int) -> None:
