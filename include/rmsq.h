@@ -65,7 +65,7 @@ enum {
                                   (other than residual_out == x or == residual) */
     RMSQ_ERR_UNSUPPORTED = -7, /* hidden above the largest row the kernels hold
                                   (32768 for 16-bit inputs, 16384 for fp32; FP8 rows
-                                  off the vector path: 16384) */
+                                  on the element-wise kernel: 16384) */
     RMSQ_ERR_LAUNCH = -8       /* the kernel launch failed; see rmsq_last_hip_error() */
 };
 
@@ -84,8 +84,9 @@ enum {
  *                    out: address and row stride congruent to x's element
  *                    offset and row stride modulo 8 for 16-bit, 4 for fp32
  *                    input; gamma 16-byte aligned), e.g. any hidden in
- *                    contiguous tensors: the phased kernel, at close to the
- *                    vector kernel's rate, up to the same widths;
+ *                    contiguous tensors: the phased kernel (0.75-0.9 of the
+ *                    vector kernel's rate on the widths measured), up to the
+ *                    same widths;
  *                  - anything else element-aligned: the element-wise kernel
  *                    (several times slower), hidden <= 16384.
  *   in_dtype     : RMSQ_F32 / RMSQ_F16 / RMSQ_BF16, the type of x and gamma.
