@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
     L.oracle_rmsnorm_y.restype = I
     L.oracle_rmsnorm_absmax.argtypes = [I64, I64, I, P, P, D, D]
     L.oracle_rmsnorm_absmax.restype = D
+    L.oracle_sum_round.argtypes = [I, I, ctypes.POINTER(P), P, I64, P]
     L.oracle_encode_array.argtypes = [I, P, I64, P]
     L.oracle_decode_array.argtypes = [I, P, I64, P]
     L.oracle_round_array.argtypes = [I, P, I64, P]
@@ -132,6 +133,33 @@ def rmsnorm_fp8(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, sc
 
     _run(work, rows, threads)
     return {"codes": codes, "scales": scales, "residual_out": rout, "q": q, "sc": sc}
+
+
+def sum_round(inputs, residual, *, in_dtype: str) -> np.ndarray:
+    """round_to_in_dtype(residual + sum of inputs), the exact float64 sum
+    rounded once (bits of in_dtype, residual's shape)."""
+    res = _bits_array(residual, in_dtype)
+    ins = [_bits_array(t, in_dtype) for t in inputs]
+    assert ins and all(t.shape == res.shape for t in ins)
+    out = np.empty_like(res)
+    ptrs = (ctypes.c_void_p * len(ins))(*[t.ctypes.data for t in ins])
+    lib().oracle_sum_round(DTYPES[in_dtype], len(ins), ptrs, _ptr(res), res.size, _ptr(out))
+    return out
+
+
+def allreduce_residual_rmsnorm_fp8(inputs, residual, gamma, *, in_dtype: str, eps: float, weight_offset: float,
+                                   scale_ub: float, out_fmt: str, scales_dtype: str,
+                                   threads: int | None = None, want_q: bool = True) -> dict:
+    """Reference for the pre-norm sum over several input buffers: s =
+    round(residual + sum of inputs) (sum_round), then the FP8 path on s
+    (Mojo allreduce_residual_rmsnorm_fp8: residual_output is the pre-norm
+    sum, which is what is normalized).  Returns rmsnorm_fp8's dict with
+    residual_out = s."""
+    s = sum_round(inputs, residual, in_dtype=in_dtype)
+    ref = rmsnorm_fp8(s, gamma, in_dtype=in_dtype, eps=eps, weight_offset=weight_offset, scale_ub=scale_ub,
+                      out_fmt=out_fmt, scales_dtype=scales_dtype, threads=threads, want_q=want_q)
+    ref["residual_out"] = s
+    return ref
 
 
 def rmsnorm_fp4(x, gamma, *, in_dtype: str, eps: float, weight_offset: float, global_scale: float,

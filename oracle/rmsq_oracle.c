@@ -463,6 +463,20 @@ double oracle_rmsnorm_absmax(int64_t rows, int64_t hidden, int in_dt,
 }
 
 /* Array forms of the codecs, for tests. */
+/* The pre-norm sum of Mojo "allreduce_residual_rmsnorm_fp8" over several
+ * input buffers (Args: input_buffers, one per GPU; residual;
+ * residual_output): s_i = round_to_dt(residual_i + sum_g inputs[g]_i), the
+ * sum exact in float64 (in order: residual, then the inputs) and rounded
+ * once.  n elements of each buffer, all in dt.  ninputs >= 1. */
+void oracle_sum_round(int dt, int ninputs, const void* const* inputs, const void* residual, int64_t n,
+                      void* out) {
+    for (int64_t i = 0; i < n; i++) {
+        double s = load_elem(dt, residual, i);
+        for (int g = 0; g < ninputs; g++) s += load_elem(dt, inputs[g], i);
+        store_elem(dt, out, i, s);
+    }
+}
+
 void oracle_encode_array(int fmt, const double* v, int64_t n, uint8_t* out) {
     for (int64_t i = 0; i < n; i++) out[i] = (uint8_t)oracle_encode(fmt, v[i]);
 }
