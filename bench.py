@@ -68,7 +68,7 @@ def algorithmic_split(w: workloads.Workload) -> tuple[int, int]:
             writes += n * esz  # residual_out
         return reads, writes
     ssz = {"f32": 4, "bf16": 2, "f16": 2}[w.scales_dtype]
-    reads, writes = n * esz + w.hidden * esz, n + w.rows * ssz
+    reads, writes = w.ninputs * n * esz + w.hidden * esz, n + w.rows * ssz
     if w.residual:
         reads += n * esz   # residual
         writes += n * esz  # residual_out
@@ -97,6 +97,7 @@ class Case:
         dt = {"bf16": rq.BF16, "f16": rq.F16, "f32": rq.F32}[w.in_dtype]
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        ins0 = [t.to(dev) for t in inp["inputs"]] if w.ninputs > 1 else None
         for i in range(copies):
             x = x0 if i == 0 else x0.clone()
             if w.fp4:
@@ -125,7 +126,17 @@ class Case:
             sc = torch.empty((w.rows,), dtype=SC_T[w.scales_dtype], device=dev)
             fmt = {"e4m3fn": rq.E4M3FN, "e4m3fnuz": rq.E4M3FNUZ}[w.out_fmt]
             sdt = {"f32": rq.F32, "bf16": rq.BF16, "f16": rq.F16}[w.scales_dtype]
-            if w.residual:
+            if w.ninputs > 1:
+                ins = ins0 if i == 0 else [t.clone() for t in ins0]
+                r = r0 if i == 0 else r0.clone()
+                ro = torch.empty_like(r)
+                ptrs = (ctypes.c_void_p * len(ins))(*[P(t) for t in ins])
+                self.keep += ins + [r, ro, out, sc, ptrs]
+                self.outs += [ro, out, sc]
+                args = (w.rows, w.hidden, dt, len(ins), ptrs, P(r), P(ro), P(g), w.eps, w.weight_offset, w.scale_ub,
+                        fmt, P(out), sdt, P(sc), stream)
+                self.calls.append((L.allreduce_residual_rmsnorm_fp8, args))
+            elif w.residual:
                 r = r0 if i == 0 else r0.clone()
                 ro = torch.empty_like(x)
                 self.keep += [x, r, ro, out, sc]
@@ -367,7 +378,8 @@ def main() -> int:
         steps = args.steps if name == workloads.HEADLINE else max(10, args.steps // 2)
         res = time_case(case, steps, args.warmup)
         res["buffer_sets"] = k
-        res["launch"] = rq.query_shape(w.rows, w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.fp4, w.residual)
+        res["launch"] = rq.query_shape(w.rows, w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.fp4, w.residual,
+                                       summed=w.ninputs > 1)
         # latency-sized calls: also their GPU time inside a graph (decode steps run graphed)
         res.update(time_graph(case, 100, max(5, steps // 100)) if algorithmic_bytes(w) < STREAM_MIN_BYTES else {})
         results[name] = res

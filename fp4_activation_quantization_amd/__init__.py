@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
     L.rmsnorm_fp8.argtypes = [I64, I64, I, P, P, F, F, F, I, P, I, P, P]
     L.residual_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4.argtypes = [I64, I64, I, P, P, F, F, P, P, P, P]
+    L.allreduce_residual_rmsnorm_fp8.argtypes = [I64, I64, I, I, ctypes.POINTER(P), P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, F, F, P, I, I, I, I, P, P, P]
     L.rmsnorm_fp8_strided.argtypes = [I64, I64, I, P, I64, P, I64, P, I64, P, F, F, F, I, P, I64, I, P, P]
     L.rmsnorm_fp4quant_strided.argtypes = [I64, I64, I, P, I64, P, I64, P, I64, P, F, F, P, I, I, I, I, P, I64, P, P]
@@ -74,8 +75,8 @@ def lib() -> ctypes.CDLL:
     L.rmsq_query_shape.argtypes = [I64, I64, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)]
     L.rmsq_status_string.argtypes = [I]
     L.rmsq_status_string.restype = ctypes.c_char_p
-    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant",
-               "residual_rmsnorm_fp4quant", "rmsnorm_fp8_strided", "rmsnorm_fp4quant_strided", "rmsq_convert",
+    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "allreduce_residual_rmsnorm_fp8", "rmsnorm_fp4",
+               "rmsnorm_fp4quant", "residual_rmsnorm_fp4quant", "rmsnorm_fp8_strided", "rmsnorm_fp4quant_strided", "rmsq_convert",
                "rmsq_stream_probe",
                "rmsq_set_tuning",
                "rmsq_query_shape", "rmsq_abi_version", "rmsq_last_hip_error"):
@@ -143,6 +144,33 @@ def residual_rmsnorm_fp8(x, residual, gamma, eps=1e-6, weight_offset=0.0, scale_
            lib().residual_rmsnorm_fp8(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out),
                                       _ptr(gamma), eps, weight_offset, scale_ub, _FMT[out_fp8], _ptr(_u8(out)),
                                       _DT[scales.dtype], _ptr(scales), _stream(x, stream)))
+    return out, scales, residual_out
+
+
+def allreduce_residual_rmsnorm_fp8(inputs, residual, gamma, eps=1e-6, weight_offset=0.0, scale_ub=float("inf"),
+                                   out_fp8="e4m3fn", out=None, scales=None, residual_out=None,
+                                   scales_dtype=torch.float32, stream=None):
+    """residual_out = residual + sum(inputs) (the exact sum rounded once to
+    residual.dtype), then RMSNorm + per-row FP8 (C: allreduce_residual_rmsnorm_fp8;
+    the inputs are tensors this GPU can read, no communication).  Returns
+    (codes, scales, residual_out)."""
+    rows, hidden = _rows_hidden(residual)
+    inputs = list(inputs)
+    for t in inputs:
+        if t.dtype != residual.dtype or t.shape != residual.shape or not t.is_contiguous():
+            raise ValueError("every input must be contiguous with residual's shape and dtype")
+    if out is None:
+        out = torch.empty(residual.shape, dtype=torch.uint8, device=residual.device)
+    if scales is None:
+        scales = torch.empty(residual.shape[:-1], dtype=scales_dtype, device=residual.device)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    ptrs = (ctypes.c_void_p * max(1, len(inputs)))(*[_ptr(t) for t in inputs])
+    _check("allreduce_residual_rmsnorm_fp8",
+           lib().allreduce_residual_rmsnorm_fp8(rows, hidden, _DT[residual.dtype], len(inputs), ptrs, _ptr(residual),
+                                                _ptr(residual_out), _ptr(gamma), eps, weight_offset, scale_ub,
+                                                _FMT[out_fp8], _ptr(_u8(out)), _DT[scales.dtype], _ptr(scales),
+                                                _stream(residual, stream)))
     return out, scales, residual_out
 
 
@@ -348,13 +376,14 @@ def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, grid_blocks: i
 
 
 def query_shape(rows: int, hidden: int, dtype: torch.dtype, fp4: bool = False, residual: bool = False,
-                elementwise: bool = False) -> dict:
+                elementwise: bool = False, summed: bool = False) -> dict:
     """Launch shape of the FP8 (fp4=False) or FP4 path with or without a
-    residual; for FP8 (any hidden) the vector / phased kernels' shape, or with
+    residual; for FP8 (any hidden) the vector / phased kernels' shape, with
     elementwise the element-wise kernel's (vectors_per_lane is then elements
-    per lane; it does not depend on the residual)."""
+    per lane; it does not depend on the residual), with summed
+    allreduce_residual_rmsnorm_fp8's."""
     w, v, r = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    path = (2 if residual else 1) if fp4 else (3 if elementwise else 5 if residual else 0)
+    path = (2 if residual else 1) if fp4 else (6 if summed else 3 if elementwise else 5 if residual else 0)
     _check("rmsq_query_shape", lib().rmsq_query_shape(rows, hidden, _DT[dtype], path, ctypes.byref(w),
                                                       ctypes.byref(v), ctypes.byref(r)))
     return {"waves_per_row": w.value, "vectors_per_lane": v.value, "rows_per_block": r.value}

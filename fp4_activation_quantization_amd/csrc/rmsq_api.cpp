@@ -164,6 +164,67 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
                              : launch_fp8_elem(a, in_dtype, resid, out_fp8, shape, stream));
 }
 
+
+// Several input buffers summed in front of the residual FP8 path: whole,
+// 16-byte aligned vectors only (the vector mapping).
+int sum_common(int64_t rows, int64_t hidden, int in_dtype, int ninputs, const void* const* inputs,
+               const void* residual, void* residual_out, const void* gamma, float eps, float weight_offset,
+               float scale_ub, int out_fp8, void* out, int scales_dtype, void* scales, hipStream_t stream) {
+    if (!valid_dtype(in_dtype) || !valid_dtype(scales_dtype)) return RMSQ_ERR_DTYPE;
+    if (out_fp8 != RMSQ_E4M3FN && out_fp8 != RMSQ_E4M3FNUZ) return RMSQ_ERR_DTYPE;
+    if (ninputs < 1 || ninputs > kMaxSumInputs) return RMSQ_ERR_VALUE;
+    const int64_t esz = elem_size(in_dtype), epv = elems_per_vec(in_dtype);
+    if (rows < 0 || hidden <= 0 || hidden % epv != 0 || !size_ok(rows, hidden, esz)) return RMSQ_ERR_SHAPE;
+    if (int rc = check_scalars(eps, weight_offset, scale_ub, true)) return rc;
+    const int64_t nvec = hidden / epv;
+    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    if (rows == 0) return RMSQ_OK;
+    if (!inputs || !residual || !residual_out || !gamma || !out || !scales) return RMSQ_ERR_NULL;
+    for (int g = 0; g < ninputs; ++g)
+        if (!inputs[g]) return RMSQ_ERR_NULL;
+    const int64_t ssz = elem_size(scales_dtype);
+    if (!aligned(residual, 16) || !aligned(residual_out, 16) || !aligned(gamma, 16) || !aligned(out, 16) ||
+        !aligned(scales, (uintptr_t)ssz))
+        return RMSQ_ERR_ALIGN;
+    for (int g = 0; g < ninputs; ++g)
+        if (!aligned(inputs[g], 16)) return RMSQ_ERR_ALIGN;
+    const int64_t rb = rows * hidden * esz;
+    const Span sr(residual, rb), sro(residual_out, rb), sg(gamma, hidden * esz), so(out, rows * hidden),
+        ss(scales, rows * ssz);
+    // outputs never overlap an input, gamma or each other; residual_out may
+    // be exactly residual (in-place update); inputs may share memory (they
+    // are only read)
+    if (overlap(so, ss) || overlap(so, sro) || overlap(ss, sro)) return RMSQ_ERR_ALIAS;
+    for (const Span& o : {so, ss, sro}) {
+        if (overlap(o, sg)) return RMSQ_ERR_ALIAS;
+        for (int g = 0; g < ninputs; ++g)
+            if (overlap(o, Span(inputs[g], rb))) return RMSQ_ERR_ALIAS;
+    }
+    if (overlap(so, sr) || overlap(ss, sr)) return RMSQ_ERR_ALIAS;
+    if (residual_out != residual && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
+
+    Shape shape;
+    if (!choose_shape(rows, (int)nvec, kPathFp8Sum, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    SumArgs sa{};
+    FusedArgs& a = sa.a;
+    a.residual = residual;
+    a.residual_out = residual_out;
+    a.gamma = gamma;
+    a.out = out;
+    a.scales = scales;
+    a.rows = rows;
+    a.hidden = (int32_t)hidden;
+    a.inv_hidden = 1.0 / (double)hidden;
+    a.nvec = (int32_t)nvec;
+    a.eps = eps;
+    a.weight_offset = weight_offset;
+    a.scale_ub = scale_ub;
+    a.scales_dtype = scales_dtype;
+    for (int g = 0; g < ninputs; ++g) sa.inputs[g] = inputs[g];
+    sa.ninputs = ninputs;
+    return launched(launch_fp8_sum(sa, in_dtype, out_fp8, shape, stream));
+}
+
 }  // namespace
 
 namespace {
@@ -281,14 +342,16 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
             //     ran 640- and 768-vector rows 1.13x slower than 8 x 2);
             //     FP4 with a residual: 1, 2, 4 (it holds two inputs per row:
             //     12 x 1 ran a 640-vector row 1.2x faster than 8 x 2, 16 x 1
-            //     an 896-vector row 1.1x faster).
+            //     an 896-vector row 1.1x faster); the same for summed input
+            //     buffers (8 x 1 ran 8 inputs of 512 vectors 3% faster than
+            //     4 x 2).
             const int order_2[3] = {2, 4, 1}, order_4[3] = {4, 2, 1}, order_1[3] = {1, 2, 4};
             const bool wide = nvec > 256;
             const int* order = !wide ? (path == kPathFp4 ? order_4 : order_2)
-                               : path == kPathFp4Residual ? order_1
+                               : (path == kPathFp4Residual || path == kPathFp8Sum) ? order_1
                                : (path == kPathFp4 || path == kPathFp8) ? order_4
                                                                         : order_2;
-            const bool one_at_4 = wide && path != kPathFp4Residual;  // 1 vector per lane only at 4 waves
+            const bool one_at_4 = wide && path != kPathFp4Residual && path != kPathFp8Sum;  // 1 vector per lane only at 4 waves
             int64_t best_idle = INT64_MAX;
             waves = 0;
             for (int i = 0; i < 3; ++i) {
@@ -389,6 +452,14 @@ int residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, const void*
                          int out_fp8, void* out, int scales_dtype, void* scales, hipStream_t stream) {
     return fp8_common(rows, hidden, in_dtype, x, hidden, residual, hidden, residual_out, hidden, true, gamma, eps,
                       weight_offset, scale_ub, out_fp8, out, hidden, scales_dtype, scales, stream);
+}
+
+int allreduce_residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, int ninputs,
+                                   const void* const* input_buffers, const void* residual, void* residual_out,
+                                   const void* gamma, float eps, float weight_offset, float scale_ub, int out_fp8,
+                                   void* out, int scales_dtype, void* scales, hipStream_t stream) {
+    return sum_common(rows, hidden, in_dtype, ninputs, input_buffers, residual, residual_out, gamma, eps,
+                      weight_offset, scale_ub, out_fp8, out, scales_dtype, scales, stream);
 }
 
 int rmsnorm_fp8_strided(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_t x_stride,
@@ -493,10 +564,12 @@ int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path, int* 
         if (rows_per_block) *rows_per_block = s.rpb;
         return RMSQ_OK;
     }
-    if (path != kPathFp8 && path != kPathFp4 && path != kPathFp4Residual && path != kPathFp8Residual)
+    if (path != kPathFp8 && path != kPathFp4 && path != kPathFp4Residual && path != kPathFp8Residual &&
+        path != kPathFp8Sum)
         return RMSQ_ERR_VALUE;
     // FP8 rows of any width (the vector and phased kernels hold a row in the
-    // lanes of ceil(hidden / vector width) vectors); FP4 rows whole vectors
+    // lanes of ceil(hidden / vector width) vectors); FP4 and summed-input rows
+    // whole vectors
     const bool fp8 = path == kPathFp8 || path == kPathFp8Residual;
     if (hidden <= 0 || (!fp8 && hidden % elems_per_vec(in_dtype) != 0)) return RMSQ_ERR_SHAPE;
     const int64_t nvec = ceil_div(hidden, elems_per_vec(in_dtype));

@@ -1,0 +1,225 @@
+// Sum of several input buffers + residual, RMSNorm and per-row dynamic FP8
+// quantization, gfx950: the computation Mojo "allreduce_residual_rmsnorm_fp8"
+// performs on each GPU once the input buffers are visible to it (Args:
+// input_buffers, one per GPU; residual; residual_output = the pre-norm sum;
+// output and scale_output as "rms_norm_fused_fp8").  The buffers are plain
+// device pointers: local tensors, or peer memory the caller has mapped and
+// made ready; this kernel does no communication or signalling.
+//
+// s = round_to_in_dtype(residual + sum of inputs), the exact sum rounded once:
+// the terms are accumulated in fp64 (exact for realistic activations: the
+// terms' exponents would have to span more than 53 - p bits to round), and
+// the fp64 sum goes to the input type without double rounding (fp32: one
+// conversion; 16-bit types: rounded to odd at fp32 precision, then to nearest
+// even at 8 / 11 bits, which is exact because fp32 keeps more than two
+// extra bits).  s is stored to residual_out and normalized and quantized as
+// in the residual FP8 kernel (rmsq_fp8_kernel.h), with the same mapping:
+// `waves` wavefronts per row, lane l owns the 16-byte vectors l, l + T, ...
+// Rows are adjacent and whole vectors.
+#pragma once
+
+#include "rmsq_device.h"
+#include "rmsq_internal.h"
+
+namespace rmsq {
+
+// fp64 sum -> the 16-bit type's bits, one rounding: round to odd at fp32
+// precision (truncate toward zero, set the last bit if anything was cut),
+// then the hardware's round to nearest even to 8 / 11 significant bits.
+__device__ __forceinline__ float to_odd_f32(double d) {
+    float f = (float)d;
+    if ((double)f != d) {
+        uint32_t b = __float_as_uint(f);
+        if (fabs((double)f) > fabs(d)) b -= 1;  // rounded away from zero: one step back
+        f = __uint_as_float(b | 1u);
+    }
+    return f;
+}
+
+template <typename InT>
+__device__ __forceinline__ uint4 round_sum(const double (&acc)[Vec<InT>::EPV]) {
+    using V = Vec<InT>;
+    float f[V::EPV];
+#pragma unroll
+    for (int e = 0; e < V::EPV; ++e) {
+        if constexpr (V::BYTES == 4)
+            f[e] = (float)acc[e];
+        else
+            f[e] = to_odd_f32(acc[e]);
+    }
+    return V::pack(f);
+}
+
+template <typename InT, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW>
+__global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
+    const FusedArgs& a = sa.a;
+    using V = Vec<InT>;
+    constexpr int EPV = V::EPV;
+    constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
+
+    const int waves = a.waves;
+    const int T = waves * 64;
+    const int rpb = ONE_ROW ? 1 : blockDim.x / T;
+    const int tid = threadIdx.x;
+    const int slot = ONE_ROW ? 0 : tid / T;
+    const int lt = tid - slot * T;
+    const int red = slot * waves + (lt >> 6);
+    const int nvec = a.nvec;
+    const int nin = sa.ninputs;
+    constexpr int GRP = VPT > 2 ? 4 : 8;  // input vectors loaded together (measured: 8 is 4% faster at 2)
+    auto live = [&](int k) { return EXACT || lt + k * T < nvec; };
+    const int64_t row_bytes = (int64_t)a.hidden * V::BYTES;
+
+    __shared__ double red_sum[2][16];
+    __shared__ int red_max[2][16];
+
+    int parity = 0;
+    for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
+        const int64_t row = row0 + slot;
+        const bool active = row < a.rows;
+
+        float t[VPT][EPV];  // s * g'
+        double ssq = 0.0;
+        float amax = 0.0f;
+        if (active) {
+            const int64_t off = row * row_bytes;
+            // s, vector by vector: the residual's vector, then the inputs'
+            // GRP at a time (8 up to 2 vectors per lane, 4 at 4, which keeps
+            // the registers bounded), summed in fp64 and rounded once; every
+            // load of the row comes before any store (residual_out may be
+            // residual)
+            uint4 sv[VPT];
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                sv[k] = make_uint4(0, 0, 0, 0);
+                if (!live(k)) continue;
+                const int d = lt + k * T;
+                float f[EPV];
+                double acc[EPV];
+                V::unpack(load_stream(static_cast<const char*>(a.residual) + off, d), f);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[e] = (double)f[e];
+                for (int g0 = 0; g0 < nin; g0 += GRP) {
+                    uint4 iv[GRP];
+#pragma unroll
+                    for (int j = 0; j < GRP; ++j)
+                        if (g0 + j < nin) iv[j] = load_stream(static_cast<const char*>(sa.inputs[g0 + j]) + off, d);
+#pragma unroll
+                    for (int j = 0; j < GRP; ++j) {
+                        if (g0 + j < nin) {
+                            V::unpack(iv[j], f);
+#pragma unroll
+                            for (int e = 0; e < EPV; ++e) acc[e] += (double)f[e];
+                        }
+                    }
+                }
+                sv[k] = round_sum<InT>(acc);
+            }
+            char* ro = static_cast<char*>(a.residual_out) + off;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                if (live(k)) store_stream(ro, lt + k * T, sv[k]);
+                ssq += (double)V::sumsq(sv[k]);
+                // gamma + weight_offset with the row (L2 hits)
+                float s[EPV], g[EPV];
+                const uint4 gv = live(k) ? reinterpret_cast<const uint4*>(a.gamma)[lt + k * T] : make_uint4(0, 0, 0, 0);
+                V::unpack(gv, g);
+                V::unpack(sv[k], s);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) t[k][e] = live(k) ? s[e] * (g[e] + a.weight_offset) : 0.0f;
+                amax = abs_max<EPV>(amax, t[k]);
+            }
+        }
+
+        ssq = wave_sum(ssq);
+        amax = wave_max_nonneg(amax);
+        if (waves > 1) {  // uniform over the block
+            if ((lt & 63) == 0) {
+                red_sum[parity][red] = ssq;
+                red_max[parity][red] = __float_as_int(amax);
+            }
+            __syncthreads();
+            ssq = 0.0;
+            int m = 0;
+            for (int w = 0; w < waves; ++w) {
+                ssq += red_sum[parity][slot * waves + w];
+                m = max_bits(m, red_max[parity][slot * waves + w]);
+            }
+            amax = __int_as_float(m);
+            // the other parity's slots are rewritten only after the next
+            // barrier, which every wave reaches after finishing these reads
+            parity ^= 1;
+        }
+
+        if (active) {
+            const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
+            double sc = (double)amax * rstd * INV_FMAX;
+            if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
+            uint32_t sbits;
+            const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
+            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
+
+            uint8_t* orow = static_cast<uint8_t*>(a.out) + row * (int64_t)a.hidden;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                if (!live(k)) continue;
+                if constexpr (EPV == 8) {
+                    uint2 w;
+                    w.x = fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq);
+                    w.y = fp8_x4<FNUZ>(t[k][4] * kq, t[k][5] * kq, t[k][6] * kq, t[k][7] * kq);
+                    store_stream(orow, lt + k * T, w);
+                } else {
+                    store_stream(orow, lt + k * T, fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq));
+                }
+            }
+            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+        }
+    }
+}
+
+namespace fp8_sum_launch {
+
+template <typename InT, bool FNUZ, int VPT>
+hipError_t launch_vpt(SumArgs sa, Shape s, hipStream_t stream) {
+    FusedArgs& a = sa.a;
+    a.waves = s.waves;
+    const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
+    // default: one block per row group
+    int64_t grid = s.grid > 0 ? s.grid : groups;
+    if (grid > groups) grid = groups;
+    if (grid > INT32_MAX) grid = INT32_MAX;
+    if (grid < 1) grid = 1;
+    const dim3 gd((unsigned)grid), bd(s.waves * s.rpb * 64);
+    const bool exact = a.nvec == VPT * s.waves * 64;
+    if (s.rpb == 1) {
+        if (exact)
+            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, true, true>), gd, bd, 0, stream, sa);
+        else
+            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, false, true>), gd, bd, 0, stream, sa);
+    } else {
+        if (exact)
+            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, true, false>), gd, bd, 0, stream, sa);
+        else
+            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, false, false>), gd, bd, 0, stream, sa);
+    }
+    return hipGetLastError();
+}
+
+template <typename InT, bool FNUZ>
+hipError_t by_vpt(const SumArgs& sa, Shape s, hipStream_t st) {
+    switch (s.vpt) {
+    case 1: return launch_vpt<InT, FNUZ, 1>(sa, s, st);
+    case 2: return launch_vpt<InT, FNUZ, 2>(sa, s, st);
+    default: return launch_vpt<InT, FNUZ, 4>(sa, s, st);
+    }
+}
+
+}  // namespace fp8_sum_launch
+
+// All variants for one input type (one translation unit each).
+template <typename InT>
+hipError_t launch_fp8_sum_typed(const SumArgs& sa, bool fnuz, Shape s, hipStream_t stream) {
+    return fnuz ? fp8_sum_launch::by_vpt<InT, true>(sa, s, stream) : fp8_sum_launch::by_vpt<InT, false>(sa, s, stream);
+}
+
+}  // namespace rmsq

@@ -38,6 +38,16 @@ struct FusedArgs {
     int64_t out_stride;
 };
 
+// Several input buffers summed in front of the residual FP8 path (at most
+// 8, the page's signal array size): `a` as for the residual FP8 kernel
+// (a.x unused), inputs[0 .. ninputs-1] the buffers.
+constexpr int kMaxSumInputs = 8;
+struct SumArgs {
+    FusedArgs a;
+    const void* inputs[kMaxSumInputs];
+    int32_t ninputs;
+};
+
 // FP4 variant: elements per block scale and the scale format.
 struct Fp4Format {
     int block;   // 16 or 32
@@ -56,7 +66,7 @@ struct Shape {
 };
 
 // Which fused path a shape is chosen for (the rmsq_query_shape `path` values).
-enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPathFp8Residual = 5 };
+enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPathFp8Residual = 5, kPathFp8Sum = 6 };
 
 // Pick the automatic shape for a row of nvec 16-byte vectors (or apply the
 // process-wide override).  Returns false if no supported shape holds the row.
@@ -79,6 +89,7 @@ hipError_t launch_fp8_phased(const FusedArgs& a, int in_dtype, bool residual, in
                              hipStream_t stream);
 hipError_t launch_fp8_elem(const FusedArgs& a, int in_dtype, bool residual, int out_fp8, Shape shape,
                            hipStream_t stream);
+hipError_t launch_fp8_sum(const SumArgs& sa, int in_dtype, int out_fp8, Shape shape, hipStream_t stream);
 hipError_t launch_fp4(const FusedArgs& a, int in_dtype, bool residual, Fp4Format fmt, Shape shape,
                       hipStream_t stream);
 hipError_t launch_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);

@@ -129,6 +129,37 @@ int residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype,
                          hipStream_t stream);
 
 /*
+ * allreduce_residual_rmsnorm_fp8 -- the sum of several input buffers plus the
+ * residual, then RMSNorm + per-row FP8 quantization: what Mojo docs
+ * "allreduce_residual_rmsnorm_fp8" computes on each GPU (Args: input_buffers,
+ * one per GPU; residual; residual_output = the pre-norm sum; output;
+ * scale_output), for input buffers this GPU can already read.  It performs
+ * no communication or synchronization: the buffers are device pointers to
+ * local memory, or to peer memory the caller has mapped and made ready.
+ *   ninputs       : 1..8 (the page's signal array holds 8 GPUs).
+ *   input_buffers : HOST array of ninputs DEVICE pointers, each [rows, hidden]
+ *                   in in_dtype, 16-byte aligned; they may share memory with
+ *                   each other or with residual (they are only read).
+ *   residual      : [rows, hidden] in in_dtype, 16-byte aligned.
+ *   residual_out  : [rows, hidden]; receives s = round_to_in_dtype(residual +
+ *                   sum of the inputs), the exact sum rounded once (RNE;
+ *                   summed in fp64 on the GPU, exact unless the terms'
+ *                   exponents span more than 53 - p bits).  May be exactly
+ *                   residual (in-place update); any other overlap with an
+ *                   input, gamma or an output is RMSQ_ERR_ALIAS.
+ *   other arguments as for residual_rmsnorm_fp8; rows are contiguous whole
+ *   16-byte vectors (hidden a multiple of 8 for 16-bit, 4 for fp32 input,
+ *   else RMSQ_ERR_SHAPE).  ninputs outside 1..8 is RMSQ_ERR_VALUE.
+ * With ninputs = 1 this equals residual_rmsnorm_fp8(x = input_buffers[0]).
+ */
+int allreduce_residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, int ninputs,
+                                   const void* const* input_buffers, const void* residual,
+                                   void* residual_out, const void* gamma,
+                                   float eps, float weight_offset, float scale_ub,
+                                   int out_fp8, void* out, int scales_dtype, void* scales,
+                                   hipStream_t stream);
+
+/*
  * rmsnorm_fp4 -- RMSNorm + block-scaled FP4 (NVFP4-style) quantization:
  * FlashInfer "rmsnorm_fp4quant.py" (rmsnorm_fp4quant, block_size 16, E4M3
  * scale factors, row-major scale layout).
@@ -320,8 +351,8 @@ int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks);
  * rmsnorm_fp4 / rmsnorm_fp4quant, 2 for residual_rmsnorm_fp4quant, 3 for
  * the FP8 entry points on the element-wise kernel (vectors_per_lane then
  * receives the elements per lane; rmsq_set_tuning's wave count and grid
- * apply to it, its vectors per lane do not).  RMSQ_ERR_VALUE for another
- * path. */
+ * apply to it, its vectors per lane do not), 6 for
+ * allreduce_residual_rmsnorm_fp8.  RMSQ_ERR_VALUE for another path. */
 int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path,
                      int* waves_per_row, int* vectors_per_lane, int* rows_per_block);
 

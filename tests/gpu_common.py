@@ -34,7 +34,12 @@ def run_fp8(w, inp, *, rows_idx=None, ub=None, out_fmt=None, scales_dtype=None, 
     off = w.weight_offset if weight_offset is None else weight_offset
     x, g = to_dev(inp["x"]), to_dev(inp["gamma"])
     sc_t = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[sdt]
-    if inp.get("residual") is not None:
+    if w.ninputs > 1:
+        r = to_dev(inp["residual"])
+        codes, scales, rout = rq.allreduce_residual_rmsnorm_fp8(
+            [to_dev(t) for t in inp["inputs"]], r, g, eps=w.eps, weight_offset=off, scale_ub=ub, out_fp8=out_fmt,
+            scales_dtype=sc_t, residual_out=r if in_place == "residual" else None, stream=stream)
+    elif inp.get("residual") is not None:
         r = to_dev(inp["residual"])
         ro = None
         if in_place == "x":
@@ -64,8 +69,16 @@ def oracle_fp8(w, inp, *, rows_idx=None, ub=None, out_fmt=None, scales_dtype=Non
         r = r[rows_idx] if r is not None else None
     g = workloads.bits(inp["gamma"])
     kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset if weight_offset is None else weight_offset)
-    ref = oracle.rmsnorm_fp8(x, g, scale_ub=w.scale_ub if ub is None else ub, out_fmt=out_fmt or w.out_fmt,
-                             scales_dtype=scales_dtype or w.scales_dtype, residual=r, **kw)
+    q = dict(scale_ub=w.scale_ub if ub is None else ub, out_fmt=out_fmt or w.out_fmt,
+             scales_dtype=scales_dtype or w.scales_dtype)
+    if w.ninputs > 1:
+        ins = [workloads.bits(t) for t in inp["inputs"]]
+        if rows_idx is not None:
+            ins = [t[rows_idx] for t in ins]
+        ref = oracle.allreduce_residual_rmsnorm_fp8(ins, r, g, **q, **kw)
+        y = oracle.rmsnorm_y(ref["residual_out"], g, **kw)["y"]
+        return ref, y
+    ref = oracle.rmsnorm_fp8(x, g, residual=r, **q, **kw)
     y = oracle.rmsnorm_y(x, g, residual=r, round_product=w.fp4_round_product, **kw)["y"]
     return ref, y
 

@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "residual_rmsnorm_fp4quant",
+    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "allreduce_residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "residual_rmsnorm_fp4quant",
               "rmsnorm_fp8_strided", "rmsnorm_fp4quant_strided", "rmsq_fp4_scale_bytes",
               "rmsq_convert", "rmsq_stream_probe",
               "rmsq_set_tuning", "rmsq_query_shape", "rmsq_status_string", "rmsq_abi_version",
@@ -263,8 +263,8 @@ def test_residual_fp4quant_errors():
     assert rfp4q(ro=P(0)) == UNSUP and rfp4q(ro=P(4)) == UNSUP
     L = rq.lib()
     q = lambda path: L.rmsq_query_shape(16384, 512, rq.BF16, path, None, None, None)  # fits the forced shape
-    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == OK and q(5) == OK
-    assert q(4) == VALUE and q(6) == VALUE
+    assert q(0) == OK and q(1) == OK and q(2) == OK and q(3) == OK and q(5) == OK and q(6) == OK
+    assert q(4) == VALUE and q(7) == VALUE
     # FP8 takes any width: 513 elements need 65 vectors' lanes, one more than forced
     assert L.rmsq_query_shape(16384, 513, rq.BF16, 0, None, None, None) == UNSUP
     assert L.rmsq_query_shape(16384, 513, rq.BF16, 1, None, None, None) == SHAPE
@@ -304,6 +304,34 @@ def test_strided_argument_checks():
     assert s8(r=P(4), ro=P(0)) == UNSUP
     assert s8(r=P(4), ro=P(0), ro_stride=8192) == ALIAS
     assert s4(r=P(4), ro=P(4)) == UNSUP and s4(r=P(4), ro=P(4), r_stride=8192) == ALIAS
+
+
+def ar8(n=2, inputs=None, rows=4, hidden=4096, dt=rq.BF16, r=None, ro=None, g=None, out=None, sc=None):
+    ins = [P(6 + i) for i in range(n)] if inputs is None else inputs
+    arr = (ctypes.c_void_p * max(1, len(ins)))(*ins)
+    r = P(4) if r is None else r
+    ro = P(5) if ro is None else ro
+    g = P(1) if g is None else g
+    out = P(2) if out is None else out
+    sc = P(3) if sc is None else sc
+    return rq.lib().allreduce_residual_rmsnorm_fp8(rows, hidden, dt, n, arr, r, ro, g, 1e-6, 0.0, 1200.0,
+                                                  rq.E4M3FN, out, rq.F32, sc, None)
+
+
+def test_allreduce_argument_checks():
+    z = ctypes.c_void_p(0)
+    assert ar8() == UNSUP and ar8(n=1) == UNSUP and ar8(n=8) == UNSUP   # every check passed
+    assert ar8(n=0) == VALUE and ar8(n=9, inputs=[P(6 + i) for i in range(9)]) == VALUE
+    assert ar8(inputs=[P(6), z]) == NULL and ar8(r=z) == NULL and ar8(ro=z) == NULL
+    assert ar8(hidden=4100) == SHAPE and ar8(rows=-1) == SHAPE
+    assert ar8(inputs=[P(6), ctypes.c_void_p(BASE + 7 * MB + 2)]) == ALIGN
+    assert ar8(ro=P(4)) == UNSUP                       # in place over residual
+    assert ar8(inputs=[P(6), P(6)]) == UNSUP           # inputs may share memory
+    assert ar8(inputs=[P(6), P(4)]) == UNSUP           # and may be the residual (read only)
+    assert ar8(ro=P(6)) == ALIAS                       # residual_out over an input
+    assert ar8(out=P(7)) == ALIAS                      # codes over an input
+    assert ar8(ro=ctypes.c_void_p(BASE + 4 * MB + 64)) == ALIAS   # partial overlap with residual
+    assert ar8(rows=0, inputs=[z, z], r=z, ro=z) == OK
 
 
 def test_fp4_scale_bytes():

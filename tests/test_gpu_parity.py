@@ -28,6 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 W = workloads.WORKLOADS
 FP8_NAMES = [n for n, w in W.items() if not w.fp4]
 SMALL_ROWS = {"rmsnorm_fp8_bf16_16x512": 16, "residual_rmsnorm_fp8_bf16_8192x4096": 301,
+              "allreduce_residual_rmsnorm_fp8_bf16_8x8192x4096": 97,
               "rmsnorm_fp8_f16_decode_1x8192": 1, "rmsnorm_fp8_f16_decode_8x8192": 8,
               "rmsnorm_fp8_f16_decode_64x8192": 64, "residual_rmsnorm_fp8_bf16_32768x8192": 203,
               "residual_rmsnorm_fp8_f32_32768x8192": 203, "rmsnorm_fp4_bf16_16384x7168": 157,

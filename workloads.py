@@ -55,10 +55,11 @@ class Workload:
     fp4_scale: str = "e4m3"          # FP4 only: "e4m3" or "ue8m0" block scales
     fp4_swizzled: bool = False       # FP4 only: 128 x 4-tile scale layout
     fp4_round_product: bool = False  # FP4 only: the page's 16-bit x * w numerics
+    ninputs: int = 1                 # FP8 summed inputs (allreduce op): input buffers summed with the residual
 
     @property
     def residual(self) -> bool:
-        return self.op.startswith("residual_")
+        return self.op.startswith("residual_") or self.op.startswith("allreduce_residual_")
 
     @property
     def fp4(self) -> bool:
@@ -99,6 +100,10 @@ WORKLOADS = {w.name: w for w in [
     # a residual stream in front of the FP4 quantizer (x and residual drawn alike)
     Workload("residual_rmsnorm_fp4_bf16_16384x7168", "residual_rmsnorm_fp4", 16384, 7168, "bf16", 5, eps=1e-6,
              gamma_lo=0.8, gamma_hi=1.2, heavy_channel_frac=0.01),
+    # the headline's rows as 8 per-GPU partial buffers summed with the residual
+    # (each buffer drawn like the headline's x, same outlier channels)
+    Workload("allreduce_residual_rmsnorm_fp8_bf16_8x8192x4096", "allreduce_residual_rmsnorm_fp8", 8192, 4096, "bf16",
+             6, eps=1e-5, gamma_lo=0.8, gamma_hi=1.2, outlier_channels=8, outlier_scale=50.0, ninputs=8),
 ]}
 
 # The workload the headline throughput is quoted on.
@@ -164,13 +169,18 @@ def make(w: Workload | str, seed: int = 0, rows: int | None = None) -> dict:
     rx, rr, rg, rs = _streams(w, seed)
     sel = _selection(rs, w)
     x = _to(_draw_activations(rx, w, sel), w.in_dtype)
+    # further input buffers continue x's stream
+    inputs = [x] + [_to(_draw_activations(rx, w, sel), w.in_dtype) for _ in range(w.ninputs - 1)]
     res = _to(_draw_activations(rr, w, sel), w.in_dtype) if w.residual else None
     if w.gamma_dist == "normal":
         g = rg.normal(0.0, w.gamma_std, size=w.hidden)
     else:
         g = rg.uniform(w.gamma_lo, w.gamma_hi, size=w.hidden)
     gamma = _to(g.astype(np.float32), w.in_dtype)
-    return {"x": x, "residual": res, "gamma": gamma, "workload": w, "selection": sel}
+    out = {"x": x, "residual": res, "gamma": gamma, "workload": w, "selection": sel}
+    if w.ninputs > 1:
+        out["inputs"] = inputs
+    return out
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
