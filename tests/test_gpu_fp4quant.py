@@ -86,6 +86,31 @@ def test_swizzled_tile_slots_widest_row(fmt):
     check_fp4(w, inp, _gs(inp, w), label=f"widest swizzled {fmt}")
 
 
+# Swizzled scales over many 256-row runs of the row map that keeps each
+# 32-row group (the rows whose scales share 128-byte lines) on one XCD:
+# ragged last 128-row tiles (partial and empty groups), ragged 4-column tiles,
+# each input type, the residual variant, and forced shapes and grids.
+MANY_RUNS = [  # dt, block, fmt, rows, hidden, resid, (waves, vpt, blocks)
+    ("bf16", 16, "e4m3", 8229, 112, False, (0, 0, 0)),     # 7 scale columns, 37-row last tile
+    ("bf16", 16, "e4m3", 8192, 7168, False, (0, 0, 0)),    # the 16384 x 7168 workload's row
+    ("f16", 32, "ue8m0", 8292, 1056, True, (0, 0, 0)),     # 33 columns, residual, 100-row last tile
+    ("f32", 16, "e4m3", 8200, 256, False, (0, 0, 0)),      # 8-row last tile: 3 empty groups
+    ("bf16", 32, "e4m3", 8229, 2048, False, (1, 4, 0)),    # one wave per row
+    ("bf16", 16, "ue8m0", 8229, 2048, True, (4, 1, 7)),    # 7 blocks: not a multiple of 8
+    ("f16", 16, "e4m3", 8300, 4096, False, (16, 1, 0)),    # 16 waves per row: one row per block
+]
+
+
+@pytest.mark.parametrize("case", MANY_RUNS, ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}-{c[3]}x{c[4]}-r{int(c[5])}-{c[6]}")
+def test_swizzled_many_row_runs(case):
+    dt, block, fmt, rows, hidden, resid, tune = case
+    w = _wl(rows, hidden, dt, block, fmt, True, resid=resid)
+    inp = _inputs(rows, hidden, dt, seed=rows + hidden, resid=resid)
+    rq.set_tuning(*tune)
+    say(f"[fp4quant swizzled row runs] {case}")
+    check_fp4(w, inp, _gs(inp, w), label=f"swizzled row runs {case}")
+
+
 @pytest.mark.parametrize("row", GOLDEN["fp4_block_rows"], ids=lambda r: r["id"])
 def test_hand_rows_byte_exact(row):
     dt = row["in_dtype"]
