@@ -215,3 +215,25 @@ def test_value_of_round_trip():
         # +/-0 and every finite value map back to themselves
         assert np.array_equal(back, bits[finite])
     del rng
+
+
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e4m3fnuz", "e2m1"])
+def test_encoder_every_pattern_in_the_rounding_band(fmt):
+    """The oracle's encoder over every fp32 pattern whose magnitude lies where
+    the format rounds (all 2^23 mantissas of each exponent there, both signs),
+    checked through the defining properties of saturating RNE on the decoded
+    magnitudes (tests/codec_props.py); past the band, values saturate or round
+    to zero, which test_saturation and test_signed_zero pin."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from codec_props import BANDS, band_values, check_codes
+
+    def one(es):
+        e, sign = es
+        v = band_values(e, sign)
+        return check_codes(fmt, v, oracle.encode(fmt, v.astype(np.float64)))
+
+    jobs = [(e, s) for e in BANDS[fmt][2] for s in (0, 1)]
+    with ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        ties = sum(ex.map(one, jobs))
+    assert ties > 0  # the band holds exact midpoints; they were met and went to even
