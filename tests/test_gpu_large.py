@@ -153,6 +153,34 @@ def test_phased_fp8_past_4gib():
     free()
 
 
+def test_elementwise_fp8_past_4gib():
+    # gamma one element off the 16-byte grid: the element-wise kernel
+    hidden = 8192
+    rows = rows_past_4gib(hidden, 2, 555)
+    x = Tiled(rows, hidden, "bf16", 40, tag_cols=(3, 6000))
+    r = Tiled(rows, hidden, "bf16", 41, tag_cols=(4, 6001))
+    g = torch.from_numpy(np.random.default_rng(42).uniform(0.5, 1.5, hidden)).to(torch.bfloat16)
+    gbuf = torch.empty(hidden + 8, dtype=torch.bfloat16, device=DEV)
+    dg = gbuf[1:1 + hidden]
+    dg.copy_(g.to(DEV))
+    assert dg.data_ptr() % 16 == 2
+    say(f"[large] residual FP8 bf16 element-wise {rows}x{hidden}")
+    codes, scales, ro = rq.residual_rmsnorm_fp8(x.dev, r.dev, dg, eps=1e-6, scale_ub=1200.0, out_fp8="e4m3fnuz",
+                                                scales_dtype=torch.float16)
+    torch.cuda.synchronize()
+    idx = boundary_rows(rows, [hidden * 2, hidden], seed=43)
+    sel = torch.as_tensor(idx, device=DEV)
+    hx, hr = workloads.bits(x.host_rows(idx)), workloads.bits(r.host_rows(idx))
+    ref = oracle.rmsnorm_fp8(hx, workloads.bits(g), residual=hr, in_dtype="bf16", eps=1e-6, weight_offset=0.0,
+                             scale_ub=1200.0, out_fmt="e4m3fnuz", scales_dtype="f16")
+    y = oracle.rmsnorm_y(hx, workloads.bits(g), residual=hr, in_dtype="bf16", eps=1e-6, weight_offset=0.0)["y"]
+    rep = compare_fp8(codes[sel].cpu().numpy(), workloads.bits(scales[sel].cpu()), ref, y, out_fmt="e4m3fnuz",
+                      scales_dtype="f16", gpu_residual_out=workloads.bits(ro[sel].cpu()))
+    say(f"  parity rows {idx.tolist()}: {rep}")
+    del x, r, codes, scales, ro
+    free()
+
+
 @pytest.mark.parametrize("swizzled,resid,block,fmt", [(True, False, 16, "e4m3"), (False, True, 32, "ue8m0")],
                          ids=["swizzled-e4m3-16", "residual-ue8m0-32"])
 def test_fp4_past_4gib(swizzled, resid, block, fmt):
