@@ -78,8 +78,8 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     if (!valid_dtype(in_dtype) || !valid_dtype(scales_dtype)) return RMSQ_ERR_DTYPE;
     if (out_fp8 != RMSQ_E4M3FN && out_fp8 != RMSQ_E4M3FNUZ) return RMSQ_ERR_DTYPE;
     const int64_t esz = elem_size(in_dtype), epv = elems_per_vec(in_dtype);
-    // any row width and any element-aligned rows: the vector kernel takes
-    // rows of whole, 16-byte aligned vectors, the element kernel the rest
+    // any row width and any element-aligned rows (the kernel is chosen from
+    // the layout below)
     if (rows < 0 || hidden <= 0) return RMSQ_ERR_SHAPE;
     if (!stride_ok(x_stride, hidden, esz, esz) || !stride_ok(out_stride, hidden, 1, 1)) return RMSQ_ERR_SHAPE;
     if (resid && (!stride_ok(r_stride, hidden, esz, esz) || !stride_ok(ro_stride, hidden, esz, esz)))
@@ -321,7 +321,7 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
     int waves = g_tune_waves.load(std::memory_order_relaxed);
     int vpt = g_tune_vpt.load(std::memory_order_relaxed);
     if (waves == 0 && vpt == 0) {
-        if (rows <= 256) {
+        if (rows <= kLatencyRows) {
             // small batches are latency bound: spread the row over up to 16
             // waves with 2 vectors per lane (a 16 KB row takes 2.4 us as
             // 8 x 2 on MI355X, 3.0 us as 16 x 1 and 2.8 us as 4 x 4)

@@ -68,6 +68,10 @@ struct Shape {
 // Which fused path a shape is chosen for (the rmsq_query_shape `path` values).
 enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPathFp8Residual = 5, kPathFp8Sum = 6 };
 
+// Batches of up to this many rows are latency bound (shapes and kernel
+// variants are chosen for the time of one call); larger ones stream.
+constexpr int64_t kLatencyRows = 256;
+
 // Pick the automatic shape for a row of nvec 16-byte vectors (or apply the
 // process-wide override).  Returns false if no supported shape holds the row.
 bool choose_shape(int64_t rows, int nvec, int path, Shape* s);
