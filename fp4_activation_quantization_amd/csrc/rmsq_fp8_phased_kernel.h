@@ -22,10 +22,10 @@
 // residual_out are stored 8 / 16 bytes at a time: the host takes this kernel
 // only when every tensor has x's phase (codes: the same offset modulo the
 // code bytes of a vector).  gamma' for a vector starts `head` elements into
-// gamma's aligned vector d and runs into d + 1 (held by the next lane, loaded
-// by the last lane of a wavefront); the window is cut with byte funnel
-// shifts (v_alignbyte_b32) chosen by a switch on the head, which is uniform
-// over the wavefronts of a row.
+// gamma's aligned vector d and runs into d + 1 (both L2 hits; taking d + 1
+// from the next lane through ds_bpermute instead measured 2-4% slower); the
+// window is cut with byte funnel shifts (v_alignbyte_b32) chosen by a switch
+// on the head, which is uniform over the wavefronts of a row.
 #pragma once
 
 #include "rmsq_device.h"
@@ -84,16 +84,6 @@ __device__ __forceinline__ uint4 window_from(const uint4& p, const uint4& c, int
     }
 }
 
-// Lane (lane + 1)'s v within the wavefront (lane 63 gets its own), through
-// ds_bpermute.
-__device__ __forceinline__ uint4 from_next_lane(const uint4& v, int lane) {
-    const int addr = (lane == 63 ? 63 : lane + 1) << 2;
-    return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x),
-                      (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y),
-                      (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z),
-                      (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w));
-}
-
 template <typename InT, bool RESID, bool FNUZ, int VPT, bool ONE_ROW>
 __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
     using V = Vec<InT>;
@@ -112,7 +102,6 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
     const int red = slot * waves + (lt >> 6);
     const int hidden = a.hidden;
     const int ngv = (hidden + EPV - 1) / EPV;  // gamma's vectors (gamma is 16-byte aligned)
-    const int lane = lt & 63;
 
     const uint4* gv = static_cast<const uint4*>(a.gamma);
 
@@ -165,15 +154,13 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
             }
             // gamma's aligned vector d for each of this lane's vectors (zero
             // past gamma; L2 hits), loaded with the row so that its latency
-            // overlaps the row's.  A row with a head also needs vector d + 1,
-            // which the next lane holds; the last lane of a wavefront loads it.
+            // overlaps the row's; a row with a head also needs vector d + 1.
             uint4 gc[VPT], gn[VPT];
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int d = lt + k * T;
                 gc[k] = d < ngv ? gv[d] : make_uint4(0, 0, 0, 0);
-                gn[k] = make_uint4(0, 0, 0, 0);
-                if (head != 0 && lane == 63 && d + 1 < ngv) gn[k] = gv[d + 1];
+                gn[k] = head != 0 && d + 1 < ngv ? gv[d + 1] : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
@@ -219,14 +206,6 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
                     const Bits sb = E::round(hs + E::widen(hr));
                     store_elem(reinterpret_cast<Bits*>(ro) + lt, sb);
                     hs = E::widen(sb);
-                }
-            }
-            // every lane of the wavefront takes part in the lane exchange
-            if (head != 0) {
-#pragma unroll
-                for (int k = 0; k < VPT; ++k) {
-                    const uint4 nx = from_next_lane(gc[k], lane);
-                    if (lane != 63) gn[k] = nx;
                 }
             }
 #pragma unroll
