@@ -11,10 +11,14 @@ Functions mirror the C entry points:
   rmsnorm_fp4(x, gamma, ...)                   -> (packed_codes, block_scales)
   convert(kind, src, dst)
 Tensors may have any number of leading dimensions; the last one is hidden.
-Outputs are allocated (uint8 / scale dtype) when not given.
+Outputs are allocated (uint8 / scale dtype) when not given.  Every tensor
+must live on x's GPU, and given buffers must have the sizes the kernels
+write (checked here, since the C ABI receives bare pointers); the call runs
+with x's GPU current.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -100,6 +104,47 @@ def _stream(t: torch.Tensor, stream):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+# one-byte element types accepted for code outputs (written as raw bytes)
+_BYTE = tuple(t for t in (torch.uint8, torch.int8, getattr(torch, "float8_e4m3fn", None),
+                          getattr(torch, "float8_e4m3fnuz", None)) if t is not None)
+
+
+def _gpu(name: str, t, dev: torch.device) -> None:
+    """t (if given) must live on GPU `dev`: the kernels receive raw device
+    pointers, and a host pointer, or another GPU's, would fault there."""
+    if t is not None and (not t.is_cuda or t.device != dev):
+        raise ValueError(f"{name} must be a tensor on {dev if dev.type == 'cuda' else 'a GPU'}, got {t.device}")
+
+
+def _buf(name: str, t, dev: torch.device, numel: int, dtypes) -> None:
+    """An output or input buffer the kernel walks as numel dense elements."""
+    _gpu(name, t, dev)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not one of {dtypes}")
+    if t.numel() != numel or not t.is_contiguous():
+        raise ValueError(f"{name}: expected {numel} contiguous elements, got {t.numel()} "
+                         f"({'contiguous' if t.is_contiguous() else 'not contiguous'})")
+
+
+def _device(x: torch.Tensor):
+    """x's GPU made current for the call (a no-op when it already is)."""
+    _gpu("x", x, x.device)
+    if x.device.index is None or x.device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(x.device)
+
+
+def _check_gamma(gamma, x: torch.Tensor, hidden: int) -> None:
+    _buf("gamma", gamma, x.device, hidden, (x.dtype,))
+
+
+def _check_global_scale(global_scale, dev: torch.device) -> None:
+    if global_scale is not None:
+        _gpu("global_scale", global_scale, dev)
+        if global_scale.dtype != torch.float32 or global_scale.numel() != 1:
+            raise ValueError("global_scale must be a one-element float32 tensor")
+
+
 def _rows_hidden(x: torch.Tensor):
     if not x.is_contiguous():
         raise ValueError("x must be contiguous")
@@ -120,9 +165,14 @@ def rmsnorm_fp8(x, gamma, eps=1e-6, weight_offset=0.0, scale_ub=float("inf"), ou
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(x.shape[:-1], dtype=scales_dtype, device=x.device)
-    _check("rmsnorm_fp8", lib().rmsnorm_fp8(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset,
-                                            scale_ub, _FMT[out_fp8], _ptr(_u8(out)), _DT[scales.dtype],
-                                            _ptr(scales), _stream(x, stream)))
+    ctx = _device(x)
+    _check_gamma(gamma, x, hidden)
+    _buf("out", out, x.device, rows * hidden, _BYTE)
+    _buf("scales", scales, x.device, rows, tuple(_DT))
+    with ctx:
+        _check("rmsnorm_fp8", lib().rmsnorm_fp8(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset,
+                                                scale_ub, _FMT[out_fp8], _ptr(_u8(out)), _DT[scales.dtype],
+                                                _ptr(scales), _stream(x, stream)))
     return out, scales
 
 
@@ -140,10 +190,17 @@ def residual_rmsnorm_fp8(x, residual, gamma, eps=1e-6, weight_offset=0.0, scale_
         scales = torch.empty(x.shape[:-1], dtype=scales_dtype, device=x.device)
     if residual_out is None:
         residual_out = torch.empty_like(x)
-    _check("residual_rmsnorm_fp8",
-           lib().residual_rmsnorm_fp8(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out),
-                                      _ptr(gamma), eps, weight_offset, scale_ub, _FMT[out_fp8], _ptr(_u8(out)),
-                                      _DT[scales.dtype], _ptr(scales), _stream(x, stream)))
+    ctx = _device(x)
+    _check_gamma(gamma, x, hidden)
+    _buf("residual", residual, x.device, rows * hidden, (x.dtype,))
+    _buf("residual_out", residual_out, x.device, rows * hidden, (x.dtype,))
+    _buf("out", out, x.device, rows * hidden, _BYTE)
+    _buf("scales", scales, x.device, rows, tuple(_DT))
+    with ctx:
+        _check("residual_rmsnorm_fp8",
+               lib().residual_rmsnorm_fp8(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out),
+                                          _ptr(gamma), eps, weight_offset, scale_ub, _FMT[out_fp8], _ptr(_u8(out)),
+                                          _DT[scales.dtype], _ptr(scales), _stream(x, stream)))
     return out, scales, residual_out
 
 
@@ -165,12 +222,20 @@ def allreduce_residual_rmsnorm_fp8(inputs, residual, gamma, eps=1e-6, weight_off
         scales = torch.empty(residual.shape[:-1], dtype=scales_dtype, device=residual.device)
     if residual_out is None:
         residual_out = torch.empty_like(residual)
+    ctx = _device(residual)
+    for k, t in enumerate(inputs):
+        _gpu(f"inputs[{k}]", t, residual.device)
+    _check_gamma(gamma, residual, hidden)
+    _buf("residual_out", residual_out, residual.device, rows * hidden, (residual.dtype,))
+    _buf("out", out, residual.device, rows * hidden, _BYTE)
+    _buf("scales", scales, residual.device, rows, tuple(_DT))
     ptrs = (ctypes.c_void_p * max(1, len(inputs)))(*[_ptr(t) for t in inputs])
-    _check("allreduce_residual_rmsnorm_fp8",
-           lib().allreduce_residual_rmsnorm_fp8(rows, hidden, _DT[residual.dtype], len(inputs), ptrs, _ptr(residual),
-                                                _ptr(residual_out), _ptr(gamma), eps, weight_offset, scale_ub,
-                                                _FMT[out_fp8], _ptr(_u8(out)), _DT[scales.dtype], _ptr(scales),
-                                                _stream(residual, stream)))
+    with ctx:
+        _check("allreduce_residual_rmsnorm_fp8",
+               lib().allreduce_residual_rmsnorm_fp8(rows, hidden, _DT[residual.dtype], len(inputs), ptrs,
+                                                    _ptr(residual), _ptr(residual_out), _ptr(gamma), eps,
+                                                    weight_offset, scale_ub, _FMT[out_fp8], _ptr(_u8(out)),
+                                                    _DT[scales.dtype], _ptr(scales), _stream(residual, stream)))
     return out, scales, residual_out
 
 
@@ -186,11 +251,15 @@ def rmsnorm_fp4(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, out=No
         out = torch.empty((*x.shape[:-1], hidden // 2), dtype=torch.uint8, device=x.device)
     if block_scales is None:
         block_scales = torch.empty((*x.shape[:-1], hidden // 16), dtype=torch.uint8, device=x.device)
-    if global_scale is not None and (global_scale.dtype != torch.float32 or global_scale.numel() != 1):
-        raise ValueError("global_scale must be a one-element float32 tensor")
-    _check("rmsnorm_fp4", lib().rmsnorm_fp4(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset,
-                                            _ptr(global_scale), _ptr(_u8(out)), _ptr(_u8(block_scales)),
-                                            _stream(x, stream)))
+    ctx = _device(x)
+    _check_global_scale(global_scale, x.device)
+    _check_gamma(gamma, x, hidden)
+    _buf("out", out, x.device, rows * (hidden // 2), _BYTE)
+    _buf("block_scales", block_scales, x.device, rows * (hidden // 16), _BYTE)
+    with ctx:
+        _check("rmsnorm_fp4", lib().rmsnorm_fp4(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset,
+                                                _ptr(global_scale), _ptr(_u8(out)), _ptr(_u8(block_scales)),
+                                                _stream(x, stream)))
     return out, block_scales
 
 
@@ -200,6 +269,22 @@ def fp4_scale_bytes(rows: int, hidden: int, block_size: int = 16, swizzled: bool
     if n < 0:
         _check("rmsq_fp4_scale_bytes", int(n))
     return int(n)
+
+
+def _check_fp4_outputs(x, rows, hidden, block_size, swizzled, out, block_scales, global_scale) -> None:
+    """Packed codes: rows * hidden/2 dense bytes; block scales: a dense
+    buffer of at least rows * hidden/block bytes (row-major) or
+    fp4_scale_bytes() bytes (swizzled)."""
+    _buf("out", out, x.device, rows * (hidden // 2), _BYTE)
+    _gpu("block_scales", block_scales, x.device)
+    if block_scales.dtype not in _BYTE or not block_scales.is_contiguous():
+        raise ValueError("block_scales must be a contiguous one-byte tensor")
+    if swizzled:
+        if block_scales.numel() < fp4_scale_bytes(rows, hidden, block_size, True):
+            raise ValueError("block_scales is smaller than fp4_scale_bytes()")
+    elif block_scales.numel() < rows * (hidden // block_size):
+        raise ValueError(f"block_scales: {block_scales.numel()} bytes, fewer than rows * hidden / block_size")
+    _check_global_scale(global_scale, x.device)
 
 
 def rmsnorm_fp4quant(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, block_size=16,
@@ -229,14 +314,14 @@ def rmsnorm_fp4quant(x, gamma, eps=1e-6, weight_offset=0.0, global_scale=None, b
                                        device=x.device)
         else:
             block_scales = torch.empty((*x.shape[:-1], hidden // block_size), dtype=torch.uint8, device=x.device)
-    elif block_scales.numel() * block_scales.element_size() < fp4_scale_bytes(rows, hidden, block_size, swizzled):
-        raise ValueError("block_scales is smaller than fp4_scale_bytes()")
-    if global_scale is not None and (global_scale.dtype != torch.float32 or global_scale.numel() != 1):
-        raise ValueError("global_scale must be a one-element float32 tensor")
-    _check("rmsnorm_fp4quant", lib().rmsnorm_fp4quant(
-        rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset, _ptr(global_scale), block_size, sfmt,
-        SF_SWIZZLED if swizzled else SF_ROW_MAJOR, FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)),
-        _ptr(_u8(block_scales)), _stream(x, stream)))
+    ctx = _device(x)
+    _check_fp4_outputs(x, rows, hidden, block_size, swizzled, out, block_scales, global_scale)
+    _check_gamma(gamma, x, hidden)
+    with ctx:
+        _check("rmsnorm_fp4quant", lib().rmsnorm_fp4quant(
+            rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset, _ptr(global_scale), block_size,
+            sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR, FP4_ROUND_PRODUCT if round_product else 0,
+            _ptr(_u8(out)), _ptr(_u8(block_scales)), _stream(x, stream)))
     return out, block_scales
 
 
@@ -263,14 +348,17 @@ def residual_rmsnorm_fp4quant(x, residual, gamma, eps=1e-6, weight_offset=0.0, g
                                        device=x.device)
         else:
             block_scales = torch.empty((*x.shape[:-1], hidden // block_size), dtype=torch.uint8, device=x.device)
-    elif block_scales.numel() * block_scales.element_size() < fp4_scale_bytes(rows, hidden, block_size, swizzled):
-        raise ValueError("block_scales is smaller than fp4_scale_bytes()")
-    if global_scale is not None and (global_scale.dtype != torch.float32 or global_scale.numel() != 1):
-        raise ValueError("global_scale must be a one-element float32 tensor")
-    _check("residual_rmsnorm_fp4quant", lib().residual_rmsnorm_fp4quant(
-        rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), eps, weight_offset,
-        _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR,
-        FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)), _ptr(_u8(block_scales)), _stream(x, stream)))
+    ctx = _device(x)
+    _check_fp4_outputs(x, rows, hidden, block_size, swizzled, out, block_scales, global_scale)
+    _check_gamma(gamma, x, hidden)
+    _buf("residual", residual, x.device, rows * hidden, (x.dtype,))
+    _buf("residual_out", residual_out, x.device, rows * hidden, (x.dtype,))
+    with ctx:
+        _check("residual_rmsnorm_fp4quant", lib().residual_rmsnorm_fp4quant(
+            rows, hidden, _DT[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), eps,
+            weight_offset, _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR,
+            FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)), _ptr(_u8(block_scales)),
+            _stream(x, stream)))
     return out, block_scales, residual_out
 
 
@@ -284,6 +372,20 @@ def _row_view(t: torch.Tensor, name: str):
     except RuntimeError as e:
         raise ValueError(f"{name}: leading dimensions must collapse to one row stride") from e
     return v.shape[0], (v.stride(0) if v.shape[0] > 1 else t.shape[-1])
+
+
+def _check_views(x, *, residual, residual_out, out, out_width=None) -> None:
+    """Row views of the strided entry points: on x's GPU, x's row count, the
+    row width the kernel writes (codes: hidden, or hidden/2 packed FP4)."""
+    lead = tuple(x.shape[:-1])
+    for name, t, width, dtypes in (("residual", residual, x.shape[-1], (x.dtype,)),
+                                   ("residual_out", residual_out, x.shape[-1], (x.dtype,)),
+                                   ("out", out, x.shape[-1] if out_width is None else out_width, _BYTE)):
+        if t is None:
+            continue
+        _gpu(name, t, x.device)
+        if t.dtype not in dtypes or tuple(t.shape) != lead + (width,):
+            raise ValueError(f"{name}: expected shape {lead + (width,)} of {dtypes}, got {tuple(t.shape)} {t.dtype}")
 
 
 def rmsnorm_fp8_strided(x, gamma, residual=None, eps=1e-6, weight_offset=0.0, scale_ub=float("inf"),
@@ -309,10 +411,15 @@ def rmsnorm_fp8_strided(x, gamma, residual=None, eps=1e-6, weight_offset=0.0, sc
         _, rs = _row_view(residual, "residual")
         _, ros = _row_view(residual_out, "residual_out")
     _, os_ = _row_view(_u8(out), "out")
-    _check("rmsnorm_fp8_strided", lib().rmsnorm_fp8_strided(
-        rows, hidden, _DT[x.dtype], _ptr(x), xs, _ptr(residual), rs, _ptr(residual_out), ros, _ptr(gamma), eps,
-        weight_offset, scale_ub, _FMT[out_fp8], _ptr(_u8(out)), os_, _DT[scales.dtype], _ptr(scales),
-        _stream(x, stream)))
+    ctx = _device(x)
+    _check_views(x, residual=residual, residual_out=residual_out, out=out)
+    _check_gamma(gamma, x, hidden)
+    _buf("scales", scales, x.device, rows, tuple(_DT))
+    with ctx:
+        _check("rmsnorm_fp8_strided", lib().rmsnorm_fp8_strided(
+            rows, hidden, _DT[x.dtype], _ptr(x), xs, _ptr(residual), rs, _ptr(residual_out), ros, _ptr(gamma), eps,
+            weight_offset, scale_ub, _FMT[out_fp8], _ptr(_u8(out)), os_, _DT[scales.dtype], _ptr(scales),
+            _stream(x, stream)))
     return out, scales, residual_out
 
 
@@ -336,8 +443,6 @@ def rmsnorm_fp4quant_strided(x, gamma, residual=None, eps=1e-6, weight_offset=0.
     elif not block_scales.is_contiguous() or \
             block_scales.numel() * block_scales.element_size() < fp4_scale_bytes(rows, hidden, block_size, swizzled):
         raise ValueError("block_scales must be contiguous and hold fp4_scale_bytes() bytes")
-    if global_scale is not None and (global_scale.dtype != torch.float32 or global_scale.numel() != 1):
-        raise ValueError("global_scale must be a one-element float32 tensor")
     rs = ros = hidden
     if residual is not None:
         if residual.dtype != x.dtype or residual.shape != x.shape:
@@ -347,17 +452,33 @@ def rmsnorm_fp4quant_strided(x, gamma, residual=None, eps=1e-6, weight_offset=0.
         _, rs = _row_view(residual, "residual")
         _, ros = _row_view(residual_out, "residual_out")
     _, os_ = _row_view(_u8(out), "out")
-    _check("rmsnorm_fp4quant_strided", lib().rmsnorm_fp4quant_strided(
-        rows, hidden, _DT[x.dtype], _ptr(x), xs, _ptr(residual), rs, _ptr(residual_out), ros, _ptr(gamma), eps,
-        weight_offset, _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR,
-        FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)), os_, _ptr(_u8(block_scales)),
-        _stream(x, stream)))
+    ctx = _device(x)
+    _check_views(x, residual=residual, residual_out=residual_out, out=out, out_width=hidden // 2)
+    _check_gamma(gamma, x, hidden)
+    _gpu("block_scales", block_scales, x.device)
+    _check_global_scale(global_scale, x.device)
+    with ctx:
+        _check("rmsnorm_fp4quant_strided", lib().rmsnorm_fp4quant_strided(
+            rows, hidden, _DT[x.dtype], _ptr(x), xs, _ptr(residual), rs, _ptr(residual_out), ros, _ptr(gamma), eps,
+            weight_offset, _ptr(global_scale), block_size, sfmt, SF_SWIZZLED if swizzled else SF_ROW_MAJOR,
+            FP4_ROUND_PRODUCT if round_product else 0, _ptr(_u8(out)), os_, _ptr(_u8(block_scales)),
+            _stream(x, stream)))
     return out, block_scales, residual_out
 
 
 def convert(kind: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
     """Elementwise device conversion (C: rmsq_convert); n = src.numel()."""
-    _check("rmsq_convert", lib().rmsq_convert(kind, _ptr(src), _ptr(dst), src.numel(), _stream(src, stream)))
+    n = src.numel()
+    need = {CVT_F32_TO_E4M3FN: n, CVT_F32_TO_E4M3FNUZ: n, CVT_F32_TO_E2M1: (n + 1) // 2, CVT_F32_TO_BF16: 2 * n,
+            CVT_F32_TO_F16: 2 * n, CVT_E4M3FN_TO_F32: 4 * n}.get(kind)
+    src_esz = 1 if kind == CVT_E4M3FN_TO_F32 else 4
+    ctx = _device(src)
+    _gpu("dst", dst, src.device)
+    if need is not None and (src.element_size() != src_esz or not src.is_contiguous() or not dst.is_contiguous()
+                             or dst.numel() * dst.element_size() < need):
+        raise ValueError("convert: src must be dense with the kind's input width, dst dense and large enough")
+    with ctx:
+        _check("rmsq_convert", lib().rmsq_convert(kind, _ptr(src), _ptr(dst), n, _stream(src, stream)))
     return dst
 
 
@@ -366,8 +487,11 @@ def stream_probe(src: torch.Tensor, read_bytes: int, dst: torch.Tensor, write_by
     src and writes write_bytes of dst, in that proportion, computing nothing."""
     if src.numel() * src.element_size() < read_bytes or dst.numel() * dst.element_size() < write_bytes:
         raise ValueError("stream_probe: buffer smaller than the byte count")
-    _check("rmsq_stream_probe", lib().rmsq_stream_probe(_ptr(src), read_bytes, _ptr(dst), write_bytes,
-                                                        _stream(src, stream)))
+    ctx = _device(src)
+    _gpu("dst", dst, src.device)
+    with ctx:
+        _check("rmsq_stream_probe", lib().rmsq_stream_probe(_ptr(src), read_bytes, _ptr(dst), write_bytes,
+                                                            _stream(src, stream)))
 
 
 def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, grid_blocks: int = 0) -> None:

@@ -458,3 +458,21 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(rq, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         rq.lib()
+
+
+def test_binding_rejects_host_tensors():
+    """The kernels get raw device pointers: the binding refuses tensors that
+    are not on a GPU before anything reaches the library."""
+    import torch
+
+    x = torch.zeros(4, 1024, dtype=torch.bfloat16)
+    g = torch.ones(1024, dtype=torch.bfloat16)
+    for call in (lambda: rq.rmsnorm_fp8(x, g), lambda: rq.residual_rmsnorm_fp8(x, x.clone(), g),
+                 lambda: rq.rmsnorm_fp4(x, g), lambda: rq.rmsnorm_fp4quant(x, g, block_size=32),
+                 lambda: rq.residual_rmsnorm_fp4quant(x, x.clone(), g),
+                 lambda: rq.allreduce_residual_rmsnorm_fp8([x.clone()], x, g),
+                 lambda: rq.rmsnorm_fp8_strided(x, g), lambda: rq.rmsnorm_fp4quant_strided(x, g),
+                 lambda: rq.convert(rq.CVT_F32_TO_E4M3FN, x.float(), torch.empty(4096, dtype=torch.uint8)),
+                 lambda: rq.stream_probe(x, 16, x.clone(), 16)):
+        with pytest.raises(ValueError, match="GPU"):
+            call()
