@@ -218,15 +218,19 @@ def time_graph(case: Case, calls: int, replays: int) -> dict:
         for t, e in zip(case.outputs(), eager):
             if not torch.equal(t, e):
                 raise RuntimeError(f"{case.w.name}: graph replay differs from the eager run")
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(replays):
+    # one event per replay boundary: the mean over all replays, and the median
+    # of the replays' per-call times (p50)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    ev[0].record()
+    for k in range(replays):
         g.replay()
-    t1.record()
+        ev[k + 1].record()
     torch.cuda.synchronize()
-    per_us = t0.elapsed_time(t1) * 1e3 / (replays * calls)
+    per_us = ev[0].elapsed_time(ev[-1]) * 1e3 / (replays * calls)
+    each = sorted(ev[k].elapsed_time(ev[k + 1]) * 1e3 / calls for k in range(replays))
     del g
-    return {"graph_us": per_us, "graph_calls": calls, "graph_replays": replays}
+    return {"graph_us": per_us, "graph_us_p50": each[len(each) // 2], "graph_calls": calls,
+            "graph_replays": replays}
 
 
 def stream_ceiling(w: workloads.Workload, copies: int, steps: int, warmup: int) -> float:
@@ -390,7 +394,7 @@ def main() -> int:
                               if algorithmic_bytes(w) >= STREAM_MIN_BYTES and not args.no_stream_ceiling else None)
         ceil = f", streaming reference {res['stream_gbps']:.0f} GB/s" if res["stream_gbps"] else ""
         if "graph_us" in res:
-            ceil += f", {res['graph_us']:.2f} us per call in a graph"
+            ceil += f", {res['graph_us']:.2f} us per call in a graph (p50 over replays {res['graph_us_p50']:.2f})"
         print(f"# {name}: {res['launch_us']:.2f} us/launch, {res['gbps']:.0f} GB/s{ceil}, {k} buffer set(s), "
               f"launch {res['launch']}", file=sys.stderr, flush=True)
 
@@ -423,6 +427,7 @@ def main() -> int:
                           "frac_hbm": round(r["gbps"] / HBM_PEAK_GBS, 4), "rows_per_s": round(r["rows_per_s"], 1),
                           "bytes": r["bytes"], "buffer_sets": r["buffer_sets"], "launch": r["launch"],
                           "graph_us": round(r["graph_us"], 3) if "graph_us" in r else None,
+                          "graph_us_p50": round(r["graph_us_p50"], 3) if "graph_us_p50" in r else None,
                           "stream_reference_gbps": round(r["stream_gbps"], 1) if r["stream_gbps"] else None,
                           "frac_of_stream_reference": round(r["gbps"] / r["stream_gbps"], 4)
                           if r["stream_gbps"] else None}
