@@ -8,6 +8,7 @@
 #include <atomic>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "../../include/rmsq.h"
@@ -87,22 +88,25 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     const int64_t widest = std::max({x_stride, out_stride / esz + 1, resid ? std::max(r_stride, ro_stride) : 0});
     if (!size_ok(rows, widest, esz)) return RMSQ_ERR_SHAPE;
     if (int rc = check_scalars(eps, weight_offset, scale_ub, true)) return rc;
-    if (hidden > std::max(kMaxVec * epv, kMaxElemHidden)) return RMSQ_ERR_UNSUPPORTED;
+    if (hidden > std::max(kMaxWideVec * epv, kMaxElemHidden)) return RMSQ_ERR_UNSUPPORTED;
     if (rows == 0) return RMSQ_OK;
     if (!x || !gamma || !out || !scales) return RMSQ_ERR_NULL;
     if (resid && (!residual || !residual_out)) return RMSQ_ERR_NULL;
     const int64_t ssz = elem_size(scales_dtype);
     if (!aligned(x, esz) || !aligned(gamma, esz) || !aligned(scales, (uintptr_t)ssz)) return RMSQ_ERR_ALIGN;
     if (resid && (!aligned(residual, esz) || !aligned(residual_out, esz))) return RMSQ_ERR_ALIGN;
-    // Three kernels: rows of whole, 16-byte aligned vectors (the vector
-    // kernel); rows at a common offset from the 16-byte grid (the phased
+    // Four kernels: rows of whole, 16-byte aligned vectors (the vector
+    // kernel, or above 4096 vectors the wide-row kernel, the row staged in
+    // LDS); rows at a common offset from the 16-byte grid (the phased
     // kernel: residual and residual_out at x's offset on every row, codes at
     // the same offset modulo epv, gamma aligned); anything else (the
     // element-wise kernel)
-    const bool vec = hidden % epv == 0 && hidden / epv <= kMaxVec && aligned(x, 16) && aligned(gamma, 16) &&
-                     aligned(out, 16) && (x_stride * esz) % 16 == 0 && out_stride % epv == 0 &&
-                     (!resid || (aligned(residual, 16) && aligned(residual_out, 16) && (r_stride * esz) % 16 == 0 &&
-                                 (ro_stride * esz) % 16 == 0));
+    const bool whole = hidden % epv == 0 && aligned(x, 16) && aligned(gamma, 16) && aligned(out, 16) &&
+                       (x_stride * esz) % 16 == 0 && out_stride % epv == 0 &&
+                       (!resid || (aligned(residual, 16) && aligned(residual_out, 16) &&
+                                   (r_stride * esz) % 16 == 0 && (ro_stride * esz) % 16 == 0));
+    const bool vec = whole && hidden / epv <= kMaxVec;
+    const bool wide = whole && !vec && hidden / epv <= kMaxWideVec;
     const uintptr_t xph = reinterpret_cast<uintptr_t>(x) % 16;  // bytes past the 16-byte grid
     auto same_phase = [&](const void* p, int64_t stride) {
         return reinterpret_cast<uintptr_t>(p) % 16 == xph && ((stride - x_stride) * esz) % 16 == 0;
@@ -112,8 +116,8 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
                         (int64_t)(reinterpret_cast<uintptr_t>(out) % epv) == (int64_t)(xph / esz) % epv &&
                         (out_stride - x_stride) % epv == 0 &&
                         (!resid || (same_phase(residual, r_stride) && same_phase(residual_out, ro_stride)));
-    if (!vec && !phased && hidden > kMaxElemHidden) return RMSQ_ERR_UNSUPPORTED;
-    const int nvec = vec ? (int)(hidden / epv) : phased ? (int)phased_nvec : 0;
+    if (!vec && !wide && !phased && hidden > kMaxElemHidden) return RMSQ_ERR_UNSUPPORTED;
+    const int nvec = (vec || wide) ? (int)(hidden / epv) : phased ? (int)phased_nvec : 0;
 
     // spans cover every row; strided tensors are compared by their extents
     const int64_t rb = hidden * esz;
@@ -136,8 +140,8 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
 
     Shape shape;
     const int path = resid ? kPathFp8Residual : kPathFp8;
-    if ((vec || phased) ? !choose_shape(rows, nvec, path, &shape)
-                        : !choose_elem_shape(rows, hidden, &shape))
+    if (wide ? !choose_wide_shape(nvec, &shape)
+             : (vec || phased) ? !choose_shape(rows, nvec, path, &shape) : !choose_elem_shape(rows, hidden, &shape))
         return RMSQ_ERR_UNSUPPORTED;
     FusedArgs a{};
     a.x = x;
@@ -159,6 +163,9 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     a.residual_stride = r_stride * esz;
     a.residual_out_stride = ro_stride * esz;
     a.out_stride = out_stride;
+    if (wide)
+        return launched(launch_wide(a, in_dtype, resid, out_fp8 == RMSQ_E4M3FNUZ ? kWideFp8Fnuz : kWideFp8,
+                                    Fp4Format{16, false}, shape.grid, stream));
     return launched(vec      ? launch_fp8(a, in_dtype, resid, out_fp8, shape, stream)
                     : phased ? launch_fp8_phased(a, in_dtype, resid, out_fp8, shape, stream)
                              : launch_fp8_elem(a, in_dtype, resid, out_fp8, shape, stream));
@@ -255,8 +262,10 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     const int64_t widest = std::max({x_stride, out_stride / esz + 1, resid ? std::max(r_stride, ro_stride) : 0});
     if (!size_ok(rows, widest, esz)) return RMSQ_ERR_SHAPE;
     if (int rc = check_scalars(eps, weight_offset, 1.0f, false)) return rc;
-    const int nvec = (int)(hidden / elems_per_vec(in_dtype));
-    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    const int64_t nvec64 = hidden / elems_per_vec(in_dtype);
+    if (nvec64 > kMaxWideVec) return RMSQ_ERR_UNSUPPORTED;
+    const int nvec = (int)nvec64;
+    const bool wide = nvec > kMaxVec;  // the row staged in LDS
     if (rows == 0) return RMSQ_OK;
     if (!x || !gamma || !out || !block_scales) return RMSQ_ERR_NULL;
     if (resid && (!residual || !residual_out)) return RMSQ_ERR_NULL;
@@ -289,7 +298,8 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
         if (!on_r && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
     }
     Shape shape;
-    if (!choose_shape(rows, nvec, resid ? kPathFp4Residual : kPathFp4, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    if (wide ? !choose_wide_shape(nvec, &shape) : !choose_shape(rows, nvec, resid ? kPathFp4Residual : kPathFp4, &shape))
+        return RMSQ_ERR_UNSUPPORTED;
     FusedArgs a{};
     a.x = x;
     a.residual = residual;
@@ -312,6 +322,7 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     a.residual_out_stride = ro_stride * esz;
     a.out_stride = out_stride;
     const Fp4Format fmt{block_size, scale_format == RMSQ_SF_UE8M0};
+    if (wide) return launched(launch_wide(a, in_dtype, resid, kWideFp4, fmt, shape.grid, stream));
     return launched(launch_fp4(a, in_dtype, resid, fmt, shape, stream));
 }
 
@@ -380,6 +391,19 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
     return true;
 }
 
+bool choose_wide_shape(int nvec, Shape* s) {
+    // the wide-row kernel always runs 16 waves and stages the row in LDS; a
+    // forced wave count or vectors per lane cannot be honoured
+    const int waves = g_tune_waves.load(std::memory_order_relaxed);
+    const int vpt = g_tune_vpt.load(std::memory_order_relaxed);
+    if ((waves != 0 && waves != 16) || vpt != 0 || nvec > kMaxWideVec) return false;
+    s->waves = 16;
+    s->vpt = (int)ceil_div(nvec, 16 * 64);
+    s->rpb = 1;
+    s->grid = g_tune_blocks.load(std::memory_order_relaxed);
+    return true;
+}
+
 bool choose_elem_shape(int64_t rows, int64_t hidden, Shape* s) {
     (void)rows;
     // elements per lane for w waves: the smallest compiled count that holds
@@ -416,18 +440,18 @@ bool choose_elem_shape(int64_t rows, int64_t hidden, Shape* s) {
     return true;
 }
 
-int persistent_blocks(const void* kernel, int block_threads) {
+int persistent_blocks(const void* kernel, int block_threads, size_t dyn_lds) {
     static std::mutex mu;
-    static std::map<std::pair<std::pair<int, int>, const void*>, int> cache;
+    static std::map<std::tuple<int, int, size_t, const void*>, int> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     std::lock_guard<std::mutex> lock(mu);
-    auto key = std::make_pair(std::make_pair(dev, block_threads), kernel);
+    const auto key = std::make_tuple(dev, block_threads, dyn_lds, kernel);
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block_threads, 0) != hipSuccess || per < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block_threads, dyn_lds) != hipSuccess || per < 1)
         per = 1;
     const int blocks = cus * per;
     cache[key] = blocks;
@@ -569,13 +593,19 @@ int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path, int* 
         return RMSQ_ERR_VALUE;
     // FP8 rows of any width (the vector and phased kernels hold a row in the
     // lanes of ceil(hidden / vector width) vectors); FP4 and summed-input rows
-    // whole vectors
+    // whole vectors.  Above 4096 vectors, rows of whole vectors (not summed
+    // inputs) take the wide-row kernel.
     const bool fp8 = path == kPathFp8 || path == kPathFp8Residual;
     if (hidden <= 0 || (!fp8 && hidden % elems_per_vec(in_dtype) != 0)) return RMSQ_ERR_SHAPE;
     const int64_t nvec = ceil_div(hidden, elems_per_vec(in_dtype));
-    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
     Shape s;
-    if (!choose_shape(rows, (int)nvec, path, &s)) return RMSQ_ERR_UNSUPPORTED;
+    if (nvec > kMaxVec) {
+        if (path == kPathFp8Sum || hidden % elems_per_vec(in_dtype) != 0 || nvec > kMaxWideVec ||
+            !choose_wide_shape((int)nvec, &s))
+            return RMSQ_ERR_UNSUPPORTED;
+    } else if (!choose_shape(rows, (int)nvec, path, &s)) {
+        return RMSQ_ERR_UNSUPPORTED;
+    }
     if (waves_per_row) *waves_per_row = s.waves;
     if (vectors_per_lane) *vectors_per_lane = s.vpt;
     if (rows_per_block) *rows_per_block = s.rpb;

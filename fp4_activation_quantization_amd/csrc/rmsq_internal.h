@@ -76,6 +76,11 @@ constexpr int64_t kLatencyRows = 256;
 // process-wide override).  Returns false if no supported shape holds the row.
 bool choose_shape(int64_t rows, int nvec, int path, Shape* s);
 
+// Shape of the wide-row kernel (16 waves, the row in LDS; vpt reports the
+// vectors per lane it walks): false if a forced wave count other than 16 or
+// a forced vectors per lane is set, or the row exceeds kMaxWideVec.
+bool choose_wide_shape(int nvec, Shape* s);
+
 // Elements per lane the FP8 element kernel is compiled for, and the widest
 // row it holds (16 waves x 64 lanes x 16 elements; more per lane would spill
 // the 128 VGPRs a 1024-thread block allows).
@@ -97,9 +102,22 @@ hipError_t launch_fp8_sum(const SumArgs& sa, int in_dtype, int out_fp8, Shape sh
 hipError_t launch_fp4(const FusedArgs& a, int in_dtype, bool residual, Fp4Format fmt, Shape shape,
                       hipStream_t stream);
 hipError_t launch_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
+
+// Rows wider than the register-resident kernels hold (more than 4096
+// vectors) are staged in LDS: up to this many 16-byte vectors per row
+// (158 KiB of gfx950's 160 KiB per workgroup; 80896 16-bit or 40448 fp32
+// elements), whole vectors and 16-byte aligned tensors only.
+constexpr int kMaxWideVec = 158 * 1024 / 16;
+// Output of the wide-row kernel: FP8 e4m3fn or e4m3fnuz codes with a per-row
+// scale, or FP4 (the format from Fp4Format).
+enum { kWideFp8 = 0, kWideFp8Fnuz = 1, kWideFp4 = 2 };
+// grid_blocks: 0 = one block per resident slot (the row count at most).
+hipError_t launch_wide(const FusedArgs& a, int in_dtype, bool residual, int out, Fp4Format fmt, int grid_blocks,
+                       hipStream_t stream);
 hipError_t launch_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, hipStream_t stream);
 
-// Occupancy-based persistent grid size for a kernel (cached per kernel).
-int persistent_blocks(const void* kernel, int block_threads);
+// Occupancy-based persistent grid size for a kernel with that block size and
+// dynamic LDS per block (cached per device, kernel and launch parameters).
+int persistent_blocks(const void* kernel, int block_threads, size_t dyn_lds = 0);
 
 }  // namespace rmsq

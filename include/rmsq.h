@@ -63,9 +63,13 @@ enum {
                                   weight_offset non-finite */
     RMSQ_ERR_ALIAS = -6,       /* an output overlaps an input or another output
                                   (other than residual_out == x or == residual) */
-    RMSQ_ERR_UNSUPPORTED = -7, /* hidden above the largest row the kernels hold
-                                  (32768 for 16-bit inputs, 16384 for fp32; FP8 rows
-                                  on the element-wise kernel: 16384) */
+    RMSQ_ERR_UNSUPPORTED = -7, /* hidden above the largest row the kernels hold:
+                                  80896 for 16-bit inputs, 40448 for fp32 (rows of
+                                  whole, 16-byte aligned vectors; above 32768 / 16384
+                                  the row is staged in LDS); other FP8 layouts 32768 /
+                                  16384 (phased) or 16384 (element-wise);
+                                  allreduce_residual_rmsnorm_fp8 32768 / 16384; or a
+                                  forced launch shape that cannot hold the row */
     RMSQ_ERR_LAUNCH = -8       /* the kernel launch failed; see rmsq_last_hip_error() */
 };
 
@@ -74,10 +78,14 @@ enum {
  * (Mojo docs "rms_norm_fused_fp8", Args).
  *   rows, hidden : tensor shape; normalization runs over the last dimension.
  *                  Any hidden >= 1 (the page's input_fn is generic in its SIMD
- *                  width).  Three kernels compute the same results:
+ *                  width).  Four kernels compute the same results:
  *                  - rows of whole 16-byte vectors (hidden a multiple of 8
  *                    for 16-bit, 4 for fp32 input; x, gamma, out, residual,
- *                    residual_out 16-byte aligned): the vector kernel;
+ *                    residual_out 16-byte aligned): the vector kernel, the
+ *                    row held in registers, up to 32768 16-bit / 16384 fp32
+ *                    elements; wider rows up to 80896 / 40448 elements on the
+ *                    wide-row kernel, the row staged in LDS (one 1024-thread
+ *                    block per row, the same results);
  *                  - otherwise, rows that all sit at x's offset from the
  *                    16-byte grid (residual, residual_out: the same address
  *                    modulo 16 and row strides congruent modulo 16 bytes;
@@ -341,7 +349,10 @@ int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t wr
  * group and rmsnorm_fp4 launches max(min(groups, resident blocks),
  * ceil(groups / 4)) blocks.  0 for any field keeps the automatic choice.
  * Returns RMSQ_ERR_VALUE for an unsupported value.  A call whose hidden does
- * not fit the forced shape returns RMSQ_ERR_UNSUPPORTED.
+ * not fit the forced shape returns RMSQ_ERR_UNSUPPORTED.  Wide rows (staged
+ * in LDS) always run 16 waves per row: a forced wave count other than 16,
+ * or any forced vectors per lane, does not fit them; their grid defaults
+ * to one block per resident slot and takes grid_blocks.
  */
 int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks);
 
@@ -352,7 +363,10 @@ int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks);
  * the FP8 entry points on the element-wise kernel (vectors_per_lane then
  * receives the elements per lane; rmsq_set_tuning's wave count and grid
  * apply to it, its vectors per lane do not), 6 for
- * allreduce_residual_rmsnorm_fp8.  RMSQ_ERR_VALUE for another path. */
+ * allreduce_residual_rmsnorm_fp8.  For a wide row (whole vectors above 4096
+ * of them) paths 0, 5, 1 and 2 report the wide-row kernel: 16 waves, the
+ * vectors per lane it walks (ceil(vectors / 1024)), one row per block.
+ * RMSQ_ERR_VALUE for another path. */
 int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path,
                      int* waves_per_row, int* vectors_per_lane, int* rows_per_block);
 

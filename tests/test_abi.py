@@ -476,3 +476,35 @@ def test_binding_rejects_host_tensors():
                  lambda: rq.stream_probe(x, 16, x.clone(), 16)):
         with pytest.raises(ValueError, match="GPU"):
             call()
+
+
+def test_wide_rows_limits_and_shapes():
+    """Rows of whole vectors above 4096 of them take the wide-row kernel (16
+    waves, the row staged in LDS) up to 10112 vectors; a forced shape other
+    than 16 waves cannot hold them, and wider rows are refused before any
+    launch."""
+    bf, f32 = rq.torch.bfloat16, rq.torch.float32
+    wide16, wide32 = 8 * 10112, 4 * 10112
+    # the module's forced shape (1 wave x 1 vector) does not fit a wide row
+    assert fp8(hidden=65536) == UNSUP and rfp8(hidden=65536) == UNSUP and fp4(hidden=65536) == UNSUP
+    rq.set_tuning(0, 0, 0)
+    try:
+        assert fp8(hidden=wide16 + 8) == UNSUP and rfp8(hidden=wide16 + 8) == UNSUP
+        assert fp8(hidden=wide32 + 4, dt=rq.F32) == UNSUP
+        assert fp4(hidden=wide16 + 16) == UNSUP
+        assert rq.query_shape(3, 65536, bf) == {"waves_per_row": 16, "vectors_per_lane": 8, "rows_per_block": 1}
+        assert rq.query_shape(3, wide16, bf, fp4=True) == {"waves_per_row": 16, "vectors_per_lane": 10,
+                                                            "rows_per_block": 1}
+        assert rq.query_shape(3, wide32, f32, residual=True) == {"waves_per_row": 16, "vectors_per_lane": 10,
+                                                                  "rows_per_block": 1}
+        for kw in (dict(hidden=wide16 + 8), dict(hidden=65537), dict(hidden=65536, summed=True)):
+            with pytest.raises(rq.RmsqError):
+                rq.query_shape(3, kw.pop("hidden"), bf, **kw)
+        rq.set_tuning(16, 0, 5)
+        assert rq.query_shape(3, 65536, bf)["waves_per_row"] == 16
+        for waves, vpt in ((8, 0), (0, 2)):
+            rq.set_tuning(waves, vpt, 0)
+            with pytest.raises(rq.RmsqError):
+                rq.query_shape(3, 65536, bf)
+    finally:
+        rq.set_tuning(1, 1, 0)

@@ -1,0 +1,113 @@
+"""GPU: rows wider than the register-resident kernels hold (more than 4096
+16-byte vectors: 32768 16-bit or 16384 fp32 elements) run the wide-row
+kernel, which stages the row in LDS, up to 10112 vectors (80896 16-bit or
+40448 fp32 elements).  Against the oracle: FP8 (both formats, every scale
+type, with and without the residual, in place), FP4 (every block size,
+scale format and layout, with and without the residual), row strides, and a
+forced grid smaller than the row count (blocks loop over rows)."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_activation_quantization_amd as rq
+import oracle
+import workloads
+from gpu_common import DEV, check_fp4, check_fp8, say
+from parity import compare_fp8
+
+pytestmark = pytest.mark.gpu
+TD = workloads.TORCH_DTYPES
+MAX16, MAX32 = 8 * 10112, 4 * 10112
+
+
+@pytest.fixture(autouse=True)
+def automatic_shapes():
+    rq.set_tuning(0, 0, 0)
+    yield
+    rq.set_tuning(0, 0, 0)
+
+
+def _inputs(rows, hidden, dt, seed, resid):
+    rng = np.random.default_rng(seed)
+    mag = np.exp2(rng.integers(-6, 6, (rows, 1)))
+    x = torch.from_numpy(rng.standard_normal((rows, hidden)) * mag).to(TD[dt])
+    r = torch.from_numpy(rng.standard_normal((rows, hidden)) * mag).to(TD[dt]) if resid else None
+    return {"x": x, "residual": r, "gamma": torch.from_numpy(rng.uniform(0.5, 1.5, hidden)).to(TD[dt])}
+
+
+def _gs(inp, w):
+    amax = oracle.absmax(workloads.bits(inp["x"]), workloads.bits(inp["gamma"]), in_dtype=w.in_dtype, eps=w.eps,
+                         weight_offset=w.weight_offset)
+    return float(np.float32(448 * 6 / amax))
+
+
+@pytest.mark.parametrize("dt,hidden", [("bf16", 32776), ("bf16", 65536), ("bf16", MAX16), ("f16", 40000),
+                                       ("f32", 16388), ("f32", MAX32)])
+@pytest.mark.parametrize("resid", [False, True])
+def test_fp8_wide_rows(dt, hidden, resid):
+    rows = 37
+    assert rq.query_shape(rows, hidden, TD[dt], residual=resid)["waves_per_row"] == 16
+    for fmt, sdt, off in (("e4m3fn", "f32", 0.0), ("e4m3fnuz", "bf16", 1.0)):
+        op = "residual_rmsnorm_fp8" if resid else "rmsnorm_fp8"
+        w = workloads.Workload("wide", op, rows, hidden, dt, 95, eps=1e-6, weight_offset=off, out_fmt=fmt,
+                               scales_dtype=sdt)
+        inp = _inputs(rows, hidden, dt, seed=hidden + rows, resid=resid)
+        say(f"[wide fp8] {op} {dt} {rows}x{hidden} {fmt} {sdt}")
+        check_fp8(w, inp, label=f"wide {op} {dt} {rows}x{hidden} {fmt}")
+
+
+def test_fp8_wide_in_place_and_forced_grid():
+    rows, hidden = 37, 49152
+    w = workloads.Workload("wide", "residual_rmsnorm_fp8", rows, hidden, "bf16", 95, eps=1e-6)
+    inp = _inputs(rows, hidden, "bf16", seed=5, resid=True)
+    say("[wide fp8] residual_out over x, then over residual")
+    check_fp8(w, inp, in_place="x", label="wide in place over x")
+    check_fp8(w, inp, in_place="residual", label="wide in place over residual")
+    rq.set_tuning(0, 0, 3)  # 3 blocks: each loops over its rows
+    say("[wide fp8] 3 blocks for 37 rows")
+    check_fp8(w, inp, label="wide 3 blocks")
+
+
+@pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0"), (32, "e4m3"), (16, "ue8m0")])
+@pytest.mark.parametrize("swz", [False, True], ids=["rowmajor", "swizzled"])
+@pytest.mark.parametrize("resid", [False, True])
+def test_fp4_wide_rows(block, fmt, swz, resid):
+    for dt, rows, hidden in (("bf16", 37, 65536), ("f32", 5, 20480), ("f16", 3, MAX16)):
+        op = "residual_rmsnorm_fp4" if resid else "rmsnorm_fp4"
+        w = workloads.Workload("wide", op, rows, hidden, dt, 95, eps=1e-6, fp4_block=block, fp4_scale=fmt,
+                               fp4_swizzled=swz)
+        inp = _inputs(rows, hidden, dt, seed=hidden + block, resid=resid)
+        say(f"[wide fp4] {op} {dt} {rows}x{hidden} block={block} {fmt} swizzled={swz}")
+        check_fp4(w, inp, _gs(inp, w), label=f"wide {op} {dt} {rows}x{hidden} {block} {fmt} swz={swz}")
+
+
+def test_fp8_wide_strided_rows():
+    rows, hidden, stride = 21, 40000, 40960
+    inp = _inputs(rows, hidden, "bf16", seed=9, resid=True)
+    buf = torch.zeros((rows, stride), dtype=torch.bfloat16, device=DEV)
+    rbuf = torch.zeros_like(buf)
+    obuf = torch.full((rows, stride), 0xA5, dtype=torch.uint8, device=DEV)
+    x, r, out = buf[:, :hidden], rbuf[:, :hidden], obuf[:, :hidden]
+    x.copy_(inp["x"].to(DEV))
+    r.copy_(inp["residual"].to(DEV))
+    say("[wide fp8] strided rows")
+    codes, scales, ro = rq.rmsnorm_fp8_strided(x, inp["gamma"].to(DEV), residual=r, scale_ub=1200.0, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:, hidden:] == 0xA5), "codes written outside the row views"
+    w = workloads.Workload("wide", "residual_rmsnorm_fp8", rows, hidden, "bf16", 95, eps=1e-6)
+    xb, rb, gb = (workloads.bits(inp[k]) for k in ("x", "residual", "gamma"))
+    ref = oracle.rmsnorm_fp8(xb, gb, residual=rb, in_dtype="bf16", eps=1e-6, weight_offset=0.0, scale_ub=1200.0,
+                             out_fmt="e4m3fn", scales_dtype="f32")
+    y = oracle.rmsnorm_y(xb, gb, residual=rb, in_dtype="bf16", eps=1e-6, weight_offset=0.0)["y"]
+    rep = compare_fp8(codes.cpu().numpy(), workloads.bits(scales.cpu()), ref, y, out_fmt="e4m3fn",
+                      scales_dtype="f32", gpu_residual_out=workloads.bits(ro.cpu()))
+    say(f"  parity {w.op} strided: {rep}")
+
+
+def test_beyond_the_widest_row_is_refused():
+    x = torch.zeros((2, MAX16 + 16), dtype=torch.bfloat16, device=DEV)  # one FP4 block past the widest row
+    g = torch.ones(MAX16 + 16, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(rq.RmsqError, match="UNSUPPORTED"):
+        rq.rmsnorm_fp8(x, g)
+    with pytest.raises(rq.RmsqError, match="UNSUPPORTED"):
+        rq.rmsnorm_fp4quant(x, g)
