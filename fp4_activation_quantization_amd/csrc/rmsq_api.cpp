@@ -440,9 +440,16 @@ bool choose_elem_shape(int64_t rows, int64_t hidden, Shape* s) {
     return true;
 }
 
-int persistent_blocks(const void* kernel, int block_threads, size_t dyn_lds) {
+namespace {
+
+struct Occupancy {
+    int cus;     // compute units of the device
+    int per_cu;  // resident blocks per CU
+};
+
+Occupancy occupancy(const void* kernel, int block_threads, size_t dyn_lds) {
     static std::mutex mu;
-    static std::map<std::tuple<int, int, size_t, const void*>, int> cache;
+    static std::map<std::tuple<int, int, size_t, const void*>, Occupancy> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     std::lock_guard<std::mutex> lock(mu);
@@ -453,9 +460,20 @@ int persistent_blocks(const void* kernel, int block_threads, size_t dyn_lds) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block_threads, dyn_lds) != hipSuccess || per < 1)
         per = 1;
-    const int blocks = cus * per;
-    cache[key] = blocks;
-    return blocks;
+    const Occupancy o{cus, per};
+    cache[key] = o;
+    return o;
+}
+
+}  // namespace
+
+int persistent_blocks(const void* kernel, int block_threads, size_t dyn_lds) {
+    const Occupancy o = occupancy(kernel, block_threads, dyn_lds);
+    return o.cus * o.per_cu;
+}
+
+int blocks_per_cu(const void* kernel, int block_threads, size_t dyn_lds) {
+    return occupancy(kernel, block_threads, dyn_lds).per_cu;
 }
 
 }  // namespace rmsq

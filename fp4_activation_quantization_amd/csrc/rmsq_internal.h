@@ -119,5 +119,8 @@ hipError_t launch_stream(const void* src, int64_t read_bytes, void* dst, int64_t
 // Occupancy-based persistent grid size for a kernel with that block size and
 // dynamic LDS per block (cached per device, kernel and launch parameters).
 int persistent_blocks(const void* kernel, int block_threads, size_t dyn_lds = 0);
+// Blocks of that kernel one CU holds at once (the occupancy API's figure,
+// at least 1; same cache).
+int blocks_per_cu(const void* kernel, int block_threads, size_t dyn_lds = 0);
 
 }  // namespace rmsq

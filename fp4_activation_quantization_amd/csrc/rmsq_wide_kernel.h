@@ -1,8 +1,7 @@
 // Fused (residual +) RMSNorm + FP8 / FP4 quantization for rows wider than
 // the register-resident kernels hold (more than 16 waves x 64 lanes x 4
 // vectors = 4096 16-byte vectors: 32768 16-bit or 16384 fp32 elements),
-// gfx950: the row is staged in LDS (160 KB per CU) between the reduction and
-// the quantization.
+// gfx950.
 //
 // Operation: that of rmsq_fp8_kernel.h (Mojo docs "rms_norm_fused_fp8",
 // per-row scale; the residual form of "allreduce_residual_rmsnorm_fp8") and
@@ -11,16 +10,29 @@
 // page's 16-bit x * w product), with or without the residual, computed with
 // the same fp32 / fp64 steps as those kernels.
 //
-// Work mapping: one 1024-thread block per row (blocks stride over rows).
-// Pass 1: lane l takes the 16-byte vectors l, l + 1024, ..., U of them in
-// flight at a time; it forms s (x, or x + residual rounded once to the input
-// type and stored to residual_out), keeps s in LDS and accumulates sum(s^2)
-// and, for FP8, max |s * g'| (g' = gamma + weight_offset, read from L2).
-// The block reduces both through LDS.  Pass 2: every lane takes its vectors
-// back from LDS, forms t = s * g' again (the same fp32 products) and
-// quantizes: FP8 with the row's scale, FP4 per block, whose lanes are
-// adjacent as in the FP4 kernel.  HBM traffic is that of the register
-// kernels: every input element read once, every output written once.
+// Work mapping: one 1024-thread block per row (blocks stride over rows);
+// lane l owns the 16-byte vectors l, l + 1024, ...  Pass 1 forms s (x, or
+// x + residual rounded once to the input type and stored to residual_out)
+// and accumulates sum(s^2) and, for FP8, max |s * g'| (g' = gamma +
+// weight_offset, read from L2); the block reduces both.  Pass 2 forms
+// t = s * g' again (the same fp32 products) and quantizes: FP8 with the
+// row's scale, FP4 per block, whose lanes are adjacent as in the FP4 kernel.
+// HBM traffic is that of the register kernels: every input element read
+// once, every output written once.
+//
+// Between the passes s is kept in one of two places:
+//  - LDS (wide_kernel): the row's vectors in dynamic shared memory, up to
+//    158 KiB, read in chunks of U vectors per lane;
+//  - registers (wide_reg_kernel): NV packed vectors per lane, the raw
+//    16-byte words at 4 VGPRs each (NV = 10, 40 VGPRs, at the widest row),
+//    every load of the row in flight at once.
+// Measured on MI355X (A/B in one process, outputs identical): without a
+// residual the register form is 11-27% faster whenever the LDS form leaves
+// room for only one block per CU (rows above ~80 KiB), and 8% slower on
+// rows that let two LDS blocks share a CU; with a residual the LDS form is
+// faster (2-26%: the second input's loads push the register form to spill).
+// The launch takes the register form for rows without a residual on which
+// the occupancy API reports one resident LDS block per CU.
 #pragma once
 
 #include "rmsq_device.h"
@@ -30,10 +42,179 @@ namespace rmsq {
 
 constexpr int kWideThreads = 1024;
 
-template <typename InT, bool RESID, int OUT, int BLOCK, bool UE8M0>
-__global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
+namespace wide_detail {
+
+// g' = gamma + weight_offset for vector d
+template <typename InT>
+__device__ __forceinline__ void gamma_of(const FusedArgs& a, int d, float (&g)[Vec<InT>::EPV]) {
+    Vec<InT>::unpack(static_cast<const uint4*>(a.gamma)[d], g);
+#pragma unroll
+    for (int e = 0; e < Vec<InT>::EPV; ++e) g[e] += a.weight_offset;
+}
+
+// t = s * g' for vector d of a row
+template <typename InT>
+__device__ __forceinline__ void product(const FusedArgs& a, int d, const uint4& s, float (&t)[Vec<InT>::EPV]) {
+    float g[Vec<InT>::EPV];
+    Vec<InT>::unpack(s, t);
+    gamma_of<InT>(a, d, g);
+#pragma unroll
+    for (int e = 0; e < Vec<InT>::EPV; ++e) t[e] *= g[e];
+}
+
+// Sum of squares and amax over the block (16 waves).  The slots are read
+// after the barrier; the caller keeps a later row from rewriting them before
+// every wave has read them.
+__device__ __forceinline__ void block_reduce(double& ssq, float& amax, bool with_max, double* red_sum,
+                                             int* red_max) {
+    const int tid = threadIdx.x;
+    ssq = wave_sum(ssq);
+    if (with_max) amax = wave_max_nonneg(amax);
+    if ((tid & 63) == 0) {
+        red_sum[tid >> 6] = ssq;
+        red_max[tid >> 6] = __float_as_int(amax);
+    }
+    __syncthreads();
+    ssq = 0.0;
+    int m = 0;
+    for (int w = 0; w < kWideThreads / 64; ++w) {
+        ssq += red_sum[w];
+        m = max_bits(m, red_max[w]);
+    }
+    amax = __int_as_float(m);
+}
+
+// FP8: the row's scale min(amax * rstd / FMAX, scale_ub), rounded to the
+// stored scale type (bits into *sbits); returns the element factor
+// rstd / stored scale (0 for an all-zero row)
+template <bool FNUZ>
+__device__ __forceinline__ float fp8_row_factor(const FusedArgs& a, float amax, double rstd, uint32_t* sbits) {
+    constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
+    double sc = (double)amax * rstd * INV_FMAX;
+    if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
+    const float sc_st = round_scale((float)sc, a.scales_dtype, sbits);
+    return sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
+}
+
+// FP8 codes of vector d (s packed) into the row's output
+template <typename InT, bool FNUZ>
+__device__ __forceinline__ void fp8_store(const FusedArgs& a, uint8_t* orow, int d, const uint4& s, float kq) {
+    float t[Vec<InT>::EPV];
+    product<InT>(a, d, s, t);
+    if constexpr (Vec<InT>::EPV == 8) {
+        uint2 w;
+        w.x = fp8_x4<FNUZ>(t[0] * kq, t[1] * kq, t[2] * kq, t[3] * kq);
+        w.y = fp8_x4<FNUZ>(t[4] * kq, t[5] * kq, t[6] * kq, t[7] * kq);
+        store_stream(orow, d, w);
+    } else {
+        store_stream(orow, d, fp8_x4<FNUZ>(t[0] * kq, t[1] * kq, t[2] * kq, t[3] * kq));
+    }
+}
+
+// FP4: the row's constants and output places
+struct Fp4Row {
+    float c_scale;  // E4M3: block scale = bmax * c_scale (gs * rstd / 6)
+    float c_elem;   // element factor numerator (gs * rstd)
+    uint8_t* orow;  // E2M1 codes
+    uint8_t* srow;  // the row's first scale byte
+    bool swz;
+};
+
+template <int BLOCK>
+__device__ __forceinline__ Fp4Row fp4_row(const FusedArgs& a, int64_t row, double rstd) {
+    // E4M3: block scale gs * (amax_t * rstd) / 6, element factor
+    // gs * rstd / d; UE8M0 (gs = 1): code from amax_t * rstd / 6,
+    // element factor rstd * 2^(127 - code)
+    const double gs = a.global_scale ? (double)*a.global_scale : 1.0;
+    Fp4Row r;
+    r.c_scale = (float)(gs * rstd * (1.0 / 6.0));
+    r.c_elem = (float)(gs * rstd);
+    r.swz = a.sf_swizzled != 0;
+    r.orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
+    // this row's scale bytes: row-major, or the row's place in its 128 x 4
+    // tiles ((row/128) * K * 512 + (row%32) * 16 + ((row%128)/32) * 4)
+    r.srow = static_cast<uint8_t*>(a.scales) +
+             (r.swz ? (row >> 7) * ((int64_t)a.sf_k_tiles * 512) + (row & 31) * 16 + ((row & 127) >> 5) * 4
+                    : row * (int64_t)(a.hidden / BLOCK));
+    return r;
+}
+
+// FP4 codes of vector d and, from the block's first lane, its scale byte.
+// Every lane of the block calls it (the block maximum is a lane swap): a
+// block's lanes are all inside the row or all past it (nvec and the lane
+// count are multiples of the lanes per block), and past it (live false)
+// t = 0 and nothing is stored.
+template <typename InT, int BLOCK, bool UE8M0>
+__device__ __forceinline__ void fp4_store(const FusedArgs& a, const Fp4Row& r, int d, bool live, const uint4& s) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
+    constexpr int LPB = BLOCK / EPV;  // lanes (vectors) per block
+    float t[EPV];
+    if (live) {
+        product<InT>(a, d, s, t);
+        if (a.round_product) V::unpack(V::pack(t), t);
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) t[e] = 0.0f;
+    }
+    const float bmax = block_max_nonneg<LPB>(abs_max<EPV>(0.0f, t));
+    uint32_t code;
+    float kq;
+    if constexpr (UE8M0) {
+        code = ue8m0_code(bmax * r.c_scale);
+        kq = ue8m0_factor(r.c_elem, code);
+    } else {
+        code = e4m3fn_scale_code(bmax * r.c_scale);
+        const float dv = e4m3fn_decode(code);
+        kq = dv > 0.0f ? r.c_elem * __builtin_amdgcn_rcpf(dv) : 0.0f;
+    }
+    if (live) {
+        float q[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) q[e] = t[e] * kq;
+        if constexpr (EPV == 8)
+            store_stream(r.orow, d, e2m1_x8(q));            // 4 bytes per lane
+        else
+            store_stream(r.orow, d, (uint16_t)e2m1_x4(q));  // 2 bytes per lane
+        if ((d & (LPB - 1)) == 0) {
+            const int j = d / LPB;  // block index in the row
+            r.srow[r.swz ? (j >> 2) * 512 + (j & 3) : j] = (uint8_t)code;
+        }
+    }
+}
+
+// Pass 1's per-vector step: s of vector d (x, or x + residual rounded once
+// and stored to residual_out), its sum of squares and, for FP8, its amax
+template <typename InT, bool RESID, bool FP8>
+__device__ __forceinline__ uint4 form_s(const FusedArgs& a, char* ro, int d, const uint4& xv, const uint4& rv,
+                                        double& ssq, float& amax) {
+    using V = Vec<InT>;
+    constexpr int EPV = V::EPV;
+    uint4 s = xv;
+    if constexpr (RESID) {
+        float xf[EPV], rf[EPV];
+        V::unpack(xv, xf);
+        V::unpack(rv, rf);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) xf[e] += rf[e];
+        s = V::pack(xf);  // one rounding of the fp32 sum
+        store_stream(ro, d, s);
+    }
+    ssq += (double)V::sumsq(s);
+    if constexpr (FP8) {
+        float t[EPV];
+        product<InT>(a, d, s, t);
+        amax = abs_max<EPV>(amax, t);
+    }
+    return s;
+}
+
+}  // namespace wide_detail
+
+// s staged in LDS between the passes (any row up to kMaxWideVec vectors).
+template <typename InT, bool RESID, int OUT, int BLOCK, bool UE8M0>
+__global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
+    using namespace wide_detail;
     // vectors per lane loaded together in pass 1: 8 with a residual, 4
     // without (measured: 8 is 9-13% faster with a residual; without one the
     // extra registers cost a second resident block on rows that leave LDS
@@ -41,8 +222,6 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
     constexpr int T = kWideThreads, U = RESID ? 8 : 4;
     constexpr bool FP4 = OUT == kWideFp4;
     constexpr bool FNUZ = OUT == kWideFp8Fnuz;
-    constexpr int LPB = BLOCK / EPV;  // FP4: lanes (vectors) per block
-    constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
 
     extern __shared__ uint4 row_s[];  // s of the current row: nvec vectors
     __shared__ double red_sum[16];
@@ -51,171 +230,60 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
     const int tid = threadIdx.x;
     const int nvec = a.nvec;
     const int steps = (nvec + U * T - 1) / (U * T);  // uniform over the block
-    const uint4* gv = static_cast<const uint4*>(a.gamma);
-    auto gamma_of = [&](int d, float (&g)[EPV]) {
-        V::unpack(gv[d], g);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) g[e] += a.weight_offset;
-    };
-
-    // chunk i of a row: this lane's vectors tid + (i * U + u) * T, u < U.
-    // Every load of a chunk comes before any of its stores (residual_out may
-    // be x or residual itself; the lane that reads a vector writes it).
-    auto fetch = [&](int64_t row, int i, uint4 (&xv)[U], uint4 (&rv)[U]) {
-        const char* xr = static_cast<const char*>(a.x) + row * a.x_stride;
-        const char* rr = RESID ? static_cast<const char*>(a.residual) + row * a.residual_stride : nullptr;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int d = tid + (i * U + u) * T;
-            if (d < nvec) {
-                xv[u] = load_stream(xr, d);
-                if constexpr (RESID) rv[u] = load_stream(rr, d);
-            }
-        }
-    };
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         // ---- pass 1: s into LDS, sum of squares (and FP8's amax) ----
+        const char* xr = static_cast<const char*>(a.x) + row * a.x_stride;
+        const char* rr = RESID ? static_cast<const char*>(a.residual) + row * a.residual_stride : nullptr;
         char* ro = RESID ? static_cast<char*>(a.residual_out) + row * a.residual_out_stride : nullptr;
         double ssq = 0.0;
         float amax = 0.0f;
         for (int i = 0; i < steps; ++i) {
+            // chunk i: this lane's vectors tid + (i * U + u) * T.  Every load
+            // of a chunk comes before any of its stores (residual_out may be
+            // x or residual itself; the lane that reads a vector writes it).
             uint4 xv[U], rv[U];
-            fetch(row, i, xv, rv);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int d = tid + (i * U + u) * T;
-                if (d >= nvec) continue;
-                uint4 s = xv[u];
-                if constexpr (RESID) {
-                    float xf[EPV], rf[EPV];
-                    V::unpack(xv[u], xf);
-                    V::unpack(rv[u], rf);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) xf[e] += rf[e];
-                    s = V::pack(xf);  // one rounding of the fp32 sum
-                    store_stream(ro, d, s);
+                if (d < nvec) {
+                    xv[u] = load_stream(xr, d);
+                    if constexpr (RESID) rv[u] = load_stream(rr, d);
                 }
-                row_s[d] = s;
-                ssq += (double)V::sumsq(s);
-                if constexpr (!FP4) {
-                    float sf[EPV], g[EPV], t[EPV];
-                    V::unpack(s, sf);
-                    gamma_of(d, g);
+            }
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) t[e] = sf[e] * g[e];
-                    amax = abs_max<EPV>(amax, t);
-                }
+            for (int u = 0; u < U; ++u) {
+                const int d = tid + (i * U + u) * T;
+                if (d < nvec) row_s[d] = form_s<InT, RESID, !FP4>(a, ro, d, xv[u], rv[u], ssq, amax);
             }
         }
 
-        // ---- the row's sums over the block (the barrier also orders the
-        // row's LDS writes before pass 2 reads them) ----
-        ssq = wave_sum(ssq);
-        if constexpr (!FP4) amax = wave_max_nonneg(amax);
-        if ((tid & 63) == 0) {
-            red_sum[tid >> 6] = ssq;
-            red_max[tid >> 6] = __float_as_int(amax);
-        }
-        __syncthreads();
-        ssq = 0.0;
-        int m = 0;
-        for (int w = 0; w < T / 64; ++w) {
-            ssq += red_sum[w];
-            m = max_bits(m, red_max[w]);
-        }
-        amax = __int_as_float(m);
+        // ---- the row's sums (the barrier also orders the row's LDS writes
+        // before pass 2 reads them) ----
+        block_reduce(ssq, amax, !FP4, red_sum, red_max);
         const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
 
         // ---- pass 2: quantize from LDS ----
         if constexpr (!FP4) {
-            double sc = (double)amax * rstd * INV_FMAX;
-            if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
             uint32_t sbits;
-            const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
-            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
+            const float kq = fp8_row_factor<FNUZ>(a, amax, rstd, &sbits);
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
             for (int i = 0; i < steps; ++i) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int d = tid + (i * U + u) * T;
-                    if (d >= nvec) continue;
-                    float sf[EPV], g[EPV], t[EPV];
-                    V::unpack(row_s[d], sf);
-                    gamma_of(d, g);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) t[e] = sf[e] * g[e];
-                    if constexpr (EPV == 8) {
-                        uint2 w;
-                        w.x = fp8_x4<FNUZ>(t[0] * kq, t[1] * kq, t[2] * kq, t[3] * kq);
-                        w.y = fp8_x4<FNUZ>(t[4] * kq, t[5] * kq, t[6] * kq, t[7] * kq);
-                        store_stream(orow, d, w);
-                    } else {
-                        store_stream(orow, d, fp8_x4<FNUZ>(t[0] * kq, t[1] * kq, t[2] * kq, t[3] * kq));
-                    }
+                    if (d < nvec) fp8_store<InT, FNUZ>(a, orow, d, row_s[d], kq);
                 }
             }
             if (tid == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
         } else {
-            // E4M3: block scale gs * (amax_t * rstd) / 6, element factor
-            // gs * rstd / d; UE8M0 (gs = 1): code from amax_t * rstd / 6,
-            // element factor rstd * 2^(127 - code)
-            const double gs = a.global_scale ? (double)*a.global_scale : 1.0;
-            const float c_scale = (float)(gs * rstd * (1.0 / 6.0));
-            const float c_elem = (float)(gs * rstd);
-            const bool swz = a.sf_swizzled != 0;
-            const int nblk = a.hidden / BLOCK;
-            uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
-            // this row's scale bytes: row-major, or the row's place in its
-            // 128 x 4 tiles ((row/128) * K * 512 + (row%32) * 16 + ((row%128)/32) * 4)
-            uint8_t* srow = static_cast<uint8_t*>(a.scales) +
-                            (swz ? (row >> 7) * ((int64_t)a.sf_k_tiles * 512) + (row & 31) * 16 +
-                                       ((row & 127) >> 5) * 4
-                                 : row * (int64_t)nblk);
+            const Fp4Row r = fp4_row<BLOCK>(a, row, rstd);
             for (int i = 0; i < steps; ++i) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    // every lane takes part in the block's lane swaps: a
-                    // block's lanes are all inside the row or all past it
-                    // (nvec and T are multiples of LPB), and past it t = 0
                     const int d = tid + (i * U + u) * T;
                     const bool live = d < nvec;
-                    float t[EPV];
-                    if (live) {
-                        float g[EPV];
-                        V::unpack(row_s[d], t);
-                        gamma_of(d, g);
-#pragma unroll
-                        for (int e = 0; e < EPV; ++e) t[e] *= g[e];
-                        if (a.round_product) V::unpack(V::pack(t), t);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < EPV; ++e) t[e] = 0.0f;
-                    }
-                    const float bmax = block_max_nonneg<LPB>(abs_max<EPV>(0.0f, t));
-                    uint32_t code;
-                    float kq;
-                    if constexpr (UE8M0) {
-                        code = ue8m0_code(bmax * c_scale);
-                        kq = ue8m0_factor(c_elem, code);
-                    } else {
-                        code = e4m3fn_scale_code(bmax * c_scale);
-                        const float dv = e4m3fn_decode(code);
-                        kq = dv > 0.0f ? c_elem * __builtin_amdgcn_rcpf(dv) : 0.0f;
-                    }
-                    if (live) {
-                        float q[EPV];
-#pragma unroll
-                        for (int e = 0; e < EPV; ++e) q[e] = t[e] * kq;
-                        if constexpr (EPV == 8)
-                            store_stream(orow, d, e2m1_x8(q));            // 4 bytes per lane
-                        else
-                            store_stream(orow, d, (uint16_t)e2m1_x4(q));  // 2 bytes per lane
-                        if ((d & (LPB - 1)) == 0) {
-                            const int j = d / LPB;  // block index in the row
-                            srow[swz ? (j >> 2) * 512 + (j & 3) : j] = (uint8_t)code;
-                        }
-                    }
+                    fp4_store<InT, BLOCK, UE8M0>(a, r, d, live, live ? row_s[d] : make_uint4(0, 0, 0, 0));
                 }
             }
         }
@@ -224,24 +292,106 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
     }
 }
 
+// s held in registers between the passes: NV vectors per lane (nvec <=
+// NV * 1024), rows without a residual.
+template <typename InT, int OUT, int BLOCK, bool UE8M0, int NV>
+__global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
+    using namespace wide_detail;
+    constexpr int T = kWideThreads;
+    constexpr bool FP4 = OUT == kWideFp4;
+    constexpr bool FNUZ = OUT == kWideFp8Fnuz;
+
+    // two sets of reduction slots, alternating by row: a wave that reaches
+    // the next row's barrier has passed this row's, so no wave can still be
+    // reading the set it writes; one barrier per row
+    __shared__ double red_sum[2][16];
+    __shared__ int red_max[2][16];
+
+    const int tid = threadIdx.x;
+    const int nvec = a.nvec;
+    int set = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, set ^= 1) {
+        // ---- pass 1: the whole row's loads, then s's sums ----
+        const char* xr = static_cast<const char*>(a.x) + row * a.x_stride;
+        uint4 sv[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int d = tid + k * T;
+            sv[k] = d < nvec ? load_stream(xr, d) : make_uint4(0, 0, 0, 0);
+        }
+        double ssq = 0.0;
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int d = tid + k * T;
+            if (d < nvec) form_s<InT, false, !FP4>(a, nullptr, d, sv[k], sv[k], ssq, amax);
+        }
+        block_reduce(ssq, amax, !FP4, red_sum[set], red_max[set]);
+        const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
+
+        // ---- pass 2: quantize from registers ----
+        if constexpr (!FP4) {
+            uint32_t sbits;
+            const float kq = fp8_row_factor<FNUZ>(a, amax, rstd, &sbits);
+            uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int d = tid + k * T;
+                if (d < nvec) fp8_store<InT, FNUZ>(a, orow, d, sv[k], kq);
+            }
+            if (tid == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+        } else {
+            const Fp4Row r = fp4_row<BLOCK>(a, row, rstd);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int d = tid + k * T;
+                fp4_store<InT, BLOCK, UE8M0>(a, r, d, d < nvec, sv[k]);
+            }
+        }
+    }
+}
+
 namespace wide_launch {
 
-// The row's LDS exceeds the default dynamic-LDS limit of a launch: the
-// kernel's limit is raised to it first (on the current device, every call).
-template <typename InT, bool RESID, int OUT, int BLOCK, bool UE8M0>
-hipError_t launch(const FusedArgs& a, int grid_blocks, hipStream_t stream) {
-    auto kern = wide_kernel<InT, RESID, OUT, BLOCK, UE8M0>;
-    const size_t lds = (size_t)a.nvec * 16;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+inline hipError_t launch_grid(const void* kern, const FusedArgs& a, int grid_blocks, size_t lds,
+                              hipStream_t stream) {
     int64_t grid = grid_blocks;
-    if (grid <= 0) grid = persistent_blocks(reinterpret_cast<const void*>(kern), kWideThreads, lds);
+    if (grid <= 0) grid = persistent_blocks(kern, kWideThreads, lds);
     if (grid > a.rows) grid = a.rows;
     if (grid > INT32_MAX) grid = INT32_MAX;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWideThreads), lds, stream, a);
-    return hipGetLastError();
+    void* args[] = {const_cast<FusedArgs*>(&a)};
+    return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kWideThreads), args, lds, stream);
+}
+
+template <typename InT, int OUT, int BLOCK, bool UE8M0>
+hipError_t launch_reg(const FusedArgs& a, int grid_blocks, hipStream_t stream) {
+    // NV = the vectors per lane the row needs (rows here exceed 4096
+    // vectors, so 5 or more), each compiled: rounding NV up costs the
+    // registers of the idle slots (measured: 9000-vector rows 13% slower at
+    // NV = 10 than at 9)
+    const int nv = (a.nvec + kWideThreads - 1) / kWideThreads;
+    const void* kern = nv <= 5   ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 5>)
+                       : nv <= 6 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 6>)
+                       : nv <= 7 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 7>)
+                       : nv <= 8 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 8>)
+                       : nv <= 9 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 9>)
+                                 : reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 10>);
+    return launch_grid(kern, a, grid_blocks, 0, stream);
+}
+
+// The LDS row exceeds the default dynamic-LDS limit of a launch: the LDS
+// kernel's limit is raised to it first (on the current device, every call).
+template <typename InT, bool RESID, int OUT, int BLOCK, bool UE8M0>
+hipError_t launch(const FusedArgs& a, int grid_blocks, hipStream_t stream) {
+    const void* kern = reinterpret_cast<const void*>(wide_kernel<InT, RESID, OUT, BLOCK, UE8M0>);
+    const size_t lds = (size_t)a.nvec * 16;
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    if constexpr (!RESID) {
+        if (blocks_per_cu(kern, kWideThreads, lds) < 2) return launch_reg<InT, OUT, BLOCK, UE8M0>(a, grid_blocks, stream);
+    }
+    return launch_grid(kern, a, grid_blocks, lds, stream);
 }
 
 template <typename InT, bool RESID>

@@ -66,7 +66,7 @@ enum {
     RMSQ_ERR_UNSUPPORTED = -7, /* hidden above the largest row the kernels hold:
                                   80896 for 16-bit inputs, 40448 for fp32 (rows of
                                   whole, 16-byte aligned vectors; above 32768 / 16384
-                                  the row is staged in LDS); other FP8 layouts 32768 /
+                                  the wide-row kernels); other FP8 layouts 32768 /
                                   16384 (phased) or 16384 (element-wise);
                                   allreduce_residual_rmsnorm_fp8 32768 / 16384; or a
                                   forced launch shape that cannot hold the row */
@@ -84,8 +84,10 @@ enum {
  *                    residual_out 16-byte aligned): the vector kernel, the
  *                    row held in registers, up to 32768 16-bit / 16384 fp32
  *                    elements; wider rows up to 80896 / 40448 elements on the
- *                    wide-row kernel, the row staged in LDS (one 1024-thread
- *                    block per row, the same results);
+ *                    wide-row kernels (one 1024-thread block per row, the
+ *                    row staged in LDS, or held in registers for rows
+ *                    without a residual that leave LDS room for only one
+ *                    block per CU; the same results);
  *                  - otherwise, rows that all sit at x's offset from the
  *                    16-byte grid (residual, residual_out: the same address
  *                    modulo 16 and row strides congruent modulo 16 bytes;
@@ -349,8 +351,8 @@ int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t wr
  * group and rmsnorm_fp4 launches max(min(groups, resident blocks),
  * ceil(groups / 4)) blocks.  0 for any field keeps the automatic choice.
  * Returns RMSQ_ERR_VALUE for an unsupported value.  A call whose hidden does
- * not fit the forced shape returns RMSQ_ERR_UNSUPPORTED.  Wide rows (staged
- * in LDS) always run 16 waves per row: a forced wave count other than 16,
+ * not fit the forced shape returns RMSQ_ERR_UNSUPPORTED.  Wide rows (above
+ * 4096 vectors) always run 16 waves per row: a forced wave count other than 16,
  * or any forced vectors per lane, does not fit them; their grid defaults
  * to one block per resident slot and takes grid_blocks.
  */

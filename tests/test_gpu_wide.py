@@ -1,10 +1,13 @@
 """GPU: rows wider than the register-resident kernels hold (more than 4096
 16-byte vectors: 32768 16-bit or 16384 fp32 elements) run the wide-row
-kernel, which stages the row in LDS, up to 10112 vectors (80896 16-bit or
-40448 fp32 elements).  Against the oracle: FP8 (both formats, every scale
-type, with and without the residual, in place), FP4 (every block size,
-scale format and layout, with and without the residual), row strides, and a
-forced grid smaller than the row count (blocks loop over rows)."""
+kernels, up to 10112 vectors (80896 16-bit or 40448 fp32 elements): rows
+with a residual, and rows of up to ~80 KiB, stage the row in LDS; wider rows
+without a residual hold it in registers (5 to 10 vectors per lane).
+Against the oracle: FP8 (both formats, every scale type, with and without
+the residual, in place), FP4 (every block size, scale format and layout,
+with and without the residual), row strides, each register width with a
+partly filled last vector slot, and forced grids smaller than the row count
+(blocks loop over rows)."""
 import numpy as np
 import pytest
 import torch
@@ -81,6 +84,39 @@ def test_fp4_wide_rows(block, fmt, swz, resid):
         check_fp4(w, inp, _gs(inp, w), label=f"wide {op} {dt} {rows}x{hidden} {block} {fmt} swz={swz}")
 
 
+# rows without a residual past one LDS block per CU: held in registers, the
+# last of NV vector slots partly filled (NV = 6, 6, 7, 8, 9; NV = 5 and 10
+# are the fp32 20480 and 16-bit 80896 rows above)
+REG_ROWS = [("f32", 20484, 5121), ("bf16", 45056, 5632), ("bf16", 56000, 7000), ("bf16", 60000, 7500),
+            ("f16", 72000, 9000)]
+
+
+@pytest.mark.parametrize("dt,hidden,nvec", REG_ROWS, ids=[f"{d}-{h}" for d, h, _ in REG_ROWS])
+def test_fp8_rows_held_in_registers(dt, hidden, nvec):
+    assert hidden * {"bf16": 2, "f16": 2, "f32": 4}[dt] == nvec * 16
+    for rows, grid in ((37, 0), (600, 0), (37, 3)):
+        rq.set_tuning(0, 0, grid)  # 600 rows or 3 blocks: blocks loop over rows
+        for fmt, sdt in (("e4m3fn", "f32"), ("e4m3fnuz", "f16")):
+            w = workloads.Workload("wide", "rmsnorm_fp8", rows, hidden, dt, 95, eps=1e-6, out_fmt=fmt,
+                                   scales_dtype=sdt)
+            inp = _inputs(rows, hidden, dt, seed=hidden + rows + grid, resid=False)
+            say(f"[wide fp8 registers] {dt} {rows}x{hidden} {fmt} grid={grid or 'auto'}")
+            check_fp8(w, inp, label=f"wide registers {dt} {rows}x{hidden} {fmt} grid={grid}")
+
+
+@pytest.mark.parametrize("block,fmt,swz", [(16, "e4m3", False), (32, "ue8m0", True), (16, "ue8m0", True),
+                                           (32, "e4m3", False)])
+def test_fp4_rows_held_in_registers(block, fmt, swz):
+    for dt, rows, hidden, grid in (("bf16", 300, 45056, 0), ("bf16", 37, 60000, 3), ("f32", 37, 28672, 0),
+                                   ("f16", 260, 72000, 0)):
+        rq.set_tuning(0, 0, grid)
+        w = workloads.Workload("wide", "rmsnorm_fp4", rows, hidden, dt, 95, eps=1e-6, fp4_block=block,
+                               fp4_scale=fmt, fp4_swizzled=swz)
+        inp = _inputs(rows, hidden, dt, seed=hidden + block + rows, resid=False)
+        say(f"[wide fp4 registers] {dt} {rows}x{hidden} block={block} {fmt} swizzled={swz} grid={grid or 'auto'}")
+        check_fp4(w, inp, _gs(inp, w), label=f"wide registers {dt} {rows}x{hidden} {block} {fmt} swz={swz}")
+
+
 def test_fp8_wide_strided_rows():
     rows, hidden, stride = 21, 40000, 40960
     inp = _inputs(rows, hidden, "bf16", seed=9, resid=True)
@@ -102,6 +138,26 @@ def test_fp8_wide_strided_rows():
     rep = compare_fp8(codes.cpu().numpy(), workloads.bits(scales.cpu()), ref, y, out_fmt="e4m3fn",
                       scales_dtype="f32", gpu_residual_out=workloads.bits(ro.cpu()))
     say(f"  parity {w.op} strided: {rep}")
+
+
+def test_fp8_strided_rows_held_in_registers():
+    rows, hidden, stride = 21, 65536, 66560
+    inp = _inputs(rows, hidden, "bf16", seed=10, resid=False)
+    buf = torch.zeros((rows, stride), dtype=torch.bfloat16, device=DEV)
+    obuf = torch.full((rows, stride), 0xA5, dtype=torch.uint8, device=DEV)
+    x, out = buf[:, :hidden], obuf[:, :hidden]
+    x.copy_(inp["x"].to(DEV))
+    say("[wide fp8 registers] strided rows")
+    codes, scales, _ = rq.rmsnorm_fp8_strided(x, inp["gamma"].to(DEV), scale_ub=1200.0, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:, hidden:] == 0xA5), "codes written outside the row views"
+    xb, gb = workloads.bits(inp["x"]), workloads.bits(inp["gamma"])
+    ref = oracle.rmsnorm_fp8(xb, gb, in_dtype="bf16", eps=1e-6, weight_offset=0.0, scale_ub=1200.0,
+                             out_fmt="e4m3fn", scales_dtype="f32")
+    y = oracle.rmsnorm_y(xb, gb, in_dtype="bf16", eps=1e-6, weight_offset=0.0)["y"]
+    rep = compare_fp8(codes.cpu().numpy(), workloads.bits(scales.cpu()), ref, y, out_fmt="e4m3fn",
+                      scales_dtype="f32")
+    say(f"  parity rmsnorm_fp8 strided (registers): {rep}")
 
 
 def test_beyond_the_widest_row_is_refused():
