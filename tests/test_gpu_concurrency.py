@@ -22,11 +22,14 @@ def _rand(shape, dt, seed):
 def _jobs():
     """(name, run(stream) -> outputs) for a mix of entry points and shapes."""
     jobs = []
-    for i, (rows, hidden) in enumerate([(512, 4096), (64, 8192), (300, 4095), (1024, 7168)]):
+    # (96, 65536): wide rows, staged in LDS with a residual, in registers without
+    for i, (rows, hidden) in enumerate([(512, 4096), (64, 8192), (300, 4095), (1024, 7168), (96, 65536)]):
         x, r = _rand((rows, hidden), torch.bfloat16, 10 * i), _rand((rows, hidden), torch.bfloat16, 10 * i + 1)
         g = _rand((hidden,), torch.bfloat16, 10 * i + 2)
         jobs.append((f"residual_fp8 {rows}x{hidden}",
                      lambda s, x=x, r=r, g=g: rq.residual_rmsnorm_fp8(x, r, g, scale_ub=1200.0, stream=s)))
+        if hidden > 32768:
+            jobs.append((f"fp8 {rows}x{hidden}", lambda s, x=x, g=g: rq.rmsnorm_fp8(x, g, scale_ub=1200.0, stream=s)))
         if hidden % 16 == 0:
             gs = torch.tensor([64.0], device=DEV)
             nbs = rq.fp4_scale_bytes(rows, hidden, 16, True)

@@ -131,6 +131,42 @@ def test_residual_fp4_and_summed_inputs():
                    run_sum, outs8)
 
 
+@pytest.mark.parametrize("resid", [False, True], ids=["registers", "lds"])
+def test_wide_rows(resid):
+    """Rows above 4096 vectors: without a residual the row is held in
+    registers, with one it is staged in LDS (the launch raises the kernel's
+    dynamic-LDS limit and queries occupancy, host calls made during capture)."""
+    rows, hidden = 40, 65536
+    x = _rand((rows, hidden), torch.bfloat16, 13)
+    r = _rand((rows, hidden), torch.bfloat16, 14) if resid else None
+    g = _rand((hidden,), torch.bfloat16, 15)
+    outs8 = [torch.empty((rows, hidden), dtype=torch.uint8, device=DEV),
+             torch.empty((rows,), dtype=torch.float32, device=DEV)] + ([torch.empty_like(x)] if resid else [])
+    gs = torch.tensor([30.0], dtype=torch.float32, device=DEV)
+    outs4 = [torch.empty((rows, hidden // 2), dtype=torch.uint8, device=DEV),
+             torch.empty((rows, hidden // 16), dtype=torch.uint8, device=DEV)] + ([torch.empty_like(x)] if resid else [])
+
+    def run8(o):
+        if resid:
+            rq.residual_rmsnorm_fp8(x, r, g, scale_ub=1200.0, out=o[0], scales=o[1], residual_out=o[2])
+        else:
+            rq.rmsnorm_fp8(x, g, scale_ub=1200.0, out=o[0], scales=o[1])
+
+    def run4(o):
+        if resid:
+            rq.residual_rmsnorm_fp4quant(x, r, g, global_scale=gs, out=o[0], block_scales=o[1], residual_out=o[2])
+        else:
+            rq.rmsnorm_fp4quant(x, g, global_scale=gs, out=o[0], block_scales=o[1])
+
+    ins = [x] + ([r] if resid else [])
+
+    def inputs(i):
+        return [_rand((rows, hidden), torch.bfloat16, 90 + 10 * i + k) for k in range(len(ins))]
+
+    _check_replays(f"wide rmsnorm_fp8 resid={resid}", ins, inputs, run8, outs8)
+    _check_replays(f"wide rmsnorm_fp4quant resid={resid}", ins, inputs, run4, outs4)
+
+
 def test_replays_follow_the_global_scale():
     """The stored E4M3 block scales of a replay track the device global scale
     written after capture: doubling gs doubles every unsaturated stored scale
