@@ -265,7 +265,7 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     const int64_t nvec64 = hidden / elems_per_vec(in_dtype);
     if (nvec64 > kMaxWideVec) return RMSQ_ERR_UNSUPPORTED;
     const int nvec = (int)nvec64;
-    const bool wide = nvec > kMaxVec;  // the row staged in LDS
+    const bool wide = nvec > kMaxVec;  // the wide-row kernels
     if (rows == 0) return RMSQ_OK;
     if (!x || !gamma || !out || !block_scales) return RMSQ_ERR_NULL;
     if (resid && (!residual || !residual_out)) return RMSQ_ERR_NULL;
@@ -392,8 +392,8 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
 }
 
 bool choose_wide_shape(int nvec, Shape* s) {
-    // the wide-row kernel always runs 16 waves and stages the row in LDS; a
-    // forced wave count or vectors per lane cannot be honoured
+    // the wide-row kernels always run 16 waves (the row in LDS or in
+    // registers); a forced wave count or vectors per lane cannot be honoured
     const int waves = g_tune_waves.load(std::memory_order_relaxed);
     const int vpt = g_tune_vpt.load(std::memory_order_relaxed);
     if ((waves != 0 && waves != 16) || vpt != 0 || nvec > kMaxWideVec) return false;

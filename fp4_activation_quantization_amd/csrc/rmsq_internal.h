@@ -76,8 +76,8 @@ constexpr int64_t kLatencyRows = 256;
 // process-wide override).  Returns false if no supported shape holds the row.
 bool choose_shape(int64_t rows, int nvec, int path, Shape* s);
 
-// Shape of the wide-row kernel (16 waves, the row in LDS; vpt reports the
-// vectors per lane it walks): false if a forced wave count other than 16 or
+// Shape of the wide-row kernels (16 waves, the row in LDS or registers; vpt
+// reports the vectors per lane they walk): false if a forced wave count other than 16 or
 // a forced vectors per lane is set, or the row exceeds kMaxWideVec.
 bool choose_wide_shape(int nvec, Shape* s);
 
@@ -104,9 +104,10 @@ hipError_t launch_fp4(const FusedArgs& a, int in_dtype, bool residual, Fp4Format
 hipError_t launch_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
 
 // Rows wider than the register-resident kernels hold (more than 4096
-// vectors) are staged in LDS: up to this many 16-byte vectors per row
-// (158 KiB of gfx950's 160 KiB per workgroup; 80896 16-bit or 40448 fp32
-// elements), whole vectors and 16-byte aligned tensors only.
+// vectors) run the wide-row kernels (the row staged in LDS, or held in
+// registers without a residual): up to this many 16-byte vectors per row
+// (158 KiB of gfx950's 160 KiB of LDS per workgroup; 80896 16-bit or 40448
+// fp32 elements), whole vectors and 16-byte aligned tensors only.
 constexpr int kMaxWideVec = 158 * 1024 / 16;
 // Output of the wide-row kernel: FP8 e4m3fn or e4m3fnuz codes with a per-row
 // scale, or FP4 (the format from Fp4Format).

@@ -479,8 +479,8 @@ def test_binding_rejects_host_tensors():
 
 
 def test_wide_rows_limits_and_shapes():
-    """Rows of whole vectors above 4096 of them take the wide-row kernel (16
-    waves, the row staged in LDS) up to 10112 vectors; a forced shape other
+    """Rows of whole vectors above 4096 of them take the wide-row kernels (16
+    waves, the row in LDS or registers) up to 10112 vectors; a forced shape other
     than 16 waves cannot hold them, and wider rows are refused before any
     launch."""
     bf, f32 = rq.torch.bfloat16, rq.torch.float32
