@@ -354,7 +354,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard across GPUs "
+        print("bench.py measures one GPU: this library has no multi-GPU path (rows shard across GPUs "
               "without communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
