@@ -117,6 +117,23 @@ def test_fp4_rows_held_in_registers(block, fmt, swz):
         check_fp4(w, inp, _gs(inp, w), label=f"wide registers {dt} {rows}x{hidden} {block} {fmt} swz={swz}")
 
 
+@pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0")])
+def test_fp4_wide_round_product_and_offset(block, fmt):
+    """The FlashInfer page's 16-bit x * w product (round_product) and a
+    weight offset on wide rows: registers (no residual, 65536), LDS (with a
+    residual, and f16 36000 without one: two LDS blocks fit a CU)."""
+    for dt, rows, hidden, resid, off in (("bf16", 37, 65536, False, 0.0), ("bf16", 37, 65536, True, 1.0),
+                                         ("f16", 21, 36000, False, 1.0)):
+        op = "residual_rmsnorm_fp4" if resid else "rmsnorm_fp4"
+        w = workloads.Workload("wide", op, rows, hidden, dt, 95, eps=1e-6, weight_offset=off, fp4_block=block,
+                               fp4_scale=fmt, fp4_round_product=True)
+        inp = _inputs(rows, hidden, dt, seed=hidden + block + 7, resid=resid)
+        if off:
+            inp["gamma"] = (inp["gamma"].double() - 1.0).to(TD[dt])  # g' = gamma + 1 stays near 1
+        say(f"[wide fp4 round_product] {op} {dt} {rows}x{hidden} block={block} {fmt} offset={off}")
+        check_fp4(w, inp, _gs(inp, w), label=f"wide round_product {op} {dt} {rows}x{hidden} {block} {fmt}")
+
+
 def test_fp8_wide_strided_rows():
     rows, hidden, stride = 21, 40000, 40960
     inp = _inputs(rows, hidden, "bf16", seed=9, resid=True)
