@@ -29,6 +29,12 @@
  *    non-finite inputs, or eps == 0 on an all-zero row, give unspecified codes.
  *  - Calls are reentrant; concurrent calls on different streams are safe as
  *    long as their output buffers do not overlap.
+ *  - Kernels run on the current HIP device, which must own the pointers and
+ *    `stream`.  Host-side state: occupancy figures cached per device, kernel
+ *    and launch size (mutex-guarded); before a wide-row launch the kernel's
+ *    dynamic-LDS limit is raised on the current device (hipFuncSetAttribute,
+ *    not a stream operation, so calls may be captured in a HIP graph); the
+ *    launch-shape override of rmsq_set_tuning is process-wide.
  */
 #ifndef RMSQ_H
 #define RMSQ_H
