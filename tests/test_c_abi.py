@@ -31,13 +31,26 @@ def test_c_program_builds_and_argument_errors(tmp_path):
 
 
 @pytest.mark.gpu
-def test_c_program_outputs_match_the_oracle(tmp_path):
+@pytest.mark.parametrize("shape", ["headline", "wide"])
+def test_c_program_outputs_match_the_oracle(tmp_path, shape):
+    """headline: 37 rows of the headline workload; wide: 9 x 65536 bf16 rows
+    (the residual call stages them in LDS, the other two hold them in
+    registers), from a process that uses the HIP runtime alone."""
+    import torch
     from gpu_common import say
 
     assert os.path.exists(c_build.EXE), "tests/c_abi/rmsq_c_check is missing: run __graft_entry__.build()"
-    w = workloads.WORKLOADS[workloads.HEADLINE]
-    rows, hidden, gs = 37, w.hidden, 40.0
-    inp = workloads.make(w, rows=rows)
+    gs = 40.0
+    if shape == "headline":
+        w = workloads.WORKLOADS[workloads.HEADLINE]
+        rows, hidden = 37, w.hidden
+        inp = workloads.make(w, rows=rows)
+    else:
+        rows, hidden = 9, 65536
+        rng = np.random.default_rng(65536)
+        inp = {"x": torch.from_numpy(rng.standard_normal((rows, hidden))).to(torch.bfloat16),
+               "residual": torch.from_numpy(rng.standard_normal((rows, hidden))).to(torch.bfloat16),
+               "gamma": torch.from_numpy(rng.uniform(0.5, 1.5, hidden)).to(torch.bfloat16)}
     x, r, g = (workloads.bits(inp[k]) for k in ("x", "residual", "gamma"))
     fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
     with open(fin, "wb") as f:
