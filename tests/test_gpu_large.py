@@ -105,6 +105,59 @@ def test_residual_fp8_past_4gib():
     free()
 
 
+@pytest.mark.parametrize("resid", [False, True], ids=["registers", "lds"])
+def test_wide_fp8_past_4gib(resid):
+    """65536-wide rows (128 KiB each): held in registers without a residual,
+    staged in LDS with one."""
+    hidden = 65536
+    rows = rows_past_4gib(hidden, 2, 37)
+    x = Tiled(rows, hidden, "bf16", 40, tag_cols=(3, 50000))
+    r = Tiled(rows, hidden, "bf16", 41, tag_cols=(hidden - 1, 1234)) if resid else None
+    g = torch.from_numpy(np.random.default_rng(42).uniform(0.5, 1.5, hidden)).to(torch.bfloat16)
+    say(f"[large] wide FP8 bf16 {rows}x{hidden} residual={resid} ({rows * hidden * 2 / 2**30:.2f} GiB per tensor)")
+    if resid:
+        codes, scales, ro = rq.residual_rmsnorm_fp8(x.dev, r.dev, g.to(DEV), eps=1e-6, scale_ub=1200.0)
+    else:
+        codes, scales = rq.rmsnorm_fp8(x.dev, g.to(DEV), eps=1e-6, scale_ub=1200.0)
+        ro = None
+    torch.cuda.synchronize()
+    idx = boundary_rows(rows, [hidden * 2, hidden], seed=43)
+    sel = torch.as_tensor(idx, device=DEV)
+    hx = workloads.bits(x.host_rows(idx))
+    hr = workloads.bits(r.host_rows(idx)) if resid else None
+    kw = dict(in_dtype="bf16", eps=1e-6, weight_offset=0.0)
+    ref = oracle.rmsnorm_fp8(hx, workloads.bits(g), residual=hr, scale_ub=1200.0, out_fmt="e4m3fn",
+                             scales_dtype="f32", **kw)
+    y = oracle.rmsnorm_y(hx, workloads.bits(g), residual=hr, **kw)["y"]
+    rep = compare_fp8(codes[sel].cpu().numpy(), workloads.bits(scales[sel].cpu()), ref, y, out_fmt="e4m3fn",
+                      scales_dtype="f32", gpu_residual_out=workloads.bits(ro[sel].cpu()) if resid else None)
+    say(f"  parity rows {idx.tolist()}: {rep}")
+    del x, r, codes, scales, ro
+    free()
+
+
+def test_wide_fp4_past_4gib():
+    """65536-wide rows without a residual (registers), FP4 with E4M3 scales."""
+    hidden = 65536
+    rows = rows_past_4gib(hidden, 2, 53)
+    x = Tiled(rows, hidden, "bf16", 44, tag_cols=(11, 60000))
+    g = torch.from_numpy(np.random.default_rng(45).uniform(0.5, 1.5, hidden)).to(torch.bfloat16)
+    gst = torch.tensor([64.0], dtype=torch.float32, device=DEV)
+    say(f"[large] wide FP4 bf16 {rows}x{hidden}")
+    packed, bs = rq.rmsnorm_fp4quant(x.dev, g.to(DEV), eps=1e-6, global_scale=gst)
+    torch.cuda.synchronize()
+    idx = boundary_rows(rows, [hidden * 2, hidden // 2], seed=46)
+    sel = torch.as_tensor(idx, device=DEV)
+    hx = workloads.bits(x.host_rows(idx))
+    kwo = dict(in_dtype="bf16", eps=1e-6, weight_offset=0.0)
+    ref = oracle.rmsnorm_fp4(hx, workloads.bits(g), global_scale=64.0, **kwo)
+    y = oracle.rmsnorm_y(hx, workloads.bits(g), **kwo)["y"]
+    rep = compare_fp4(packed[sel].cpu().numpy(), bs[sel].cpu().numpy(), ref, y, global_scale=64.0)
+    say(f"  parity rows {idx.tolist()}: {rep}")
+    del x, packed, bs
+    free()
+
+
 def test_summed_inputs_fp8_past_4gib():
     hidden = 8192
     rows = rows_past_4gib(hidden, 2, 61)
