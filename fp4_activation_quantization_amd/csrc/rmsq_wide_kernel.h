@@ -27,7 +27,7 @@
 //    16-byte words at 4 VGPRs each (NV = 10, 40 VGPRs, at the widest row),
 //    every load of the row in flight at once.
 // Measured on MI355X (A/B in one process, outputs identical): without a
-// residual the register form is 11-27% faster whenever the LDS form leaves
+// residual the register form is 10-28% faster whenever the LDS form leaves
 // room for only one block per CU (rows above ~80 KiB), and 8% slower on
 // rows that let two LDS blocks share a CU; with a residual the LDS form is
 // faster (2-26%: the second input's loads push the register form to spill).
