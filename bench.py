@@ -340,12 +340,27 @@ def copy_calibration(nbytes: int, steps: int) -> None:
     print(json.dumps({"copy_calibration_bytes": nbytes, "steps": steps}), flush=True)
 
 
+def workload_of(name: str) -> workloads.Workload:
+    """A named workload, or an ad-hoc shape 'op:ROWSxHIDDEN:dtype' (for example
+    rmsnorm_fp8:1024x65536:bf16, op as in workloads.Workload) with seeded
+    normal activations, eps 1e-6 and the Workload defaults otherwise."""
+    if name in workloads.WORKLOADS:
+        return workloads.WORKLOADS[name]
+    try:
+        op, shape, dt = name.split(":")
+        rows, hidden = (int(v) for v in shape.split("x"))
+    except ValueError:
+        raise SystemExit(f"unknown workload {name!r}: a name from workloads.py or op:ROWSxHIDDEN:dtype")
+    return workloads.Workload(name, op, rows, hidden, dt, 95, eps=1e-6)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workloads", default="all", help="'all', 'headline' or comma-separated workload names")
+    ap.add_argument("--workloads", default="all",
+                    help="'all', 'headline' or comma-separated workload names or shapes op:ROWSxHIDDEN:dtype")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming reference kernel")
@@ -376,9 +391,11 @@ def main() -> int:
 
     results = {}
     for name in names:
-        w = workloads.WORKLOADS[name]
+        w = workload_of(name)
         k = copies_for(w)
-        case = Case(w, k, fp4_global_scale(name) if w.fp4 else None)
+        # ad-hoc FP4 shapes take a global scale of 64 (named ones their stored value)
+        gs = (fp4_global_scale(name) if name in workloads.WORKLOADS else 64.0) if w.fp4 else None
+        case = Case(w, k, gs)
         steps = args.steps if name == workloads.HEADLINE else max(10, args.steps // 2)
         res = time_case(case, steps, args.warmup)
         res["buffer_sets"] = k
@@ -399,7 +416,7 @@ def main() -> int:
               f"launch {res['launch']}", file=sys.stderr, flush=True)
 
     h = results[lead]
-    w = workloads.WORKLOADS[lead]
+    w = workload_of(lead)
     line = {
         "metric": "GB/s (algorithmic HBM bytes) for fused residual+RMSNorm+FP8 quant, 1 GPU"
                   if lead == workloads.HEADLINE else f"GB/s (algorithmic HBM bytes) for {w.op}, 1 GPU",
