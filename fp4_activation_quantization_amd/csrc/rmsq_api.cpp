@@ -141,7 +141,7 @@ int fp8_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
     Shape shape;
     const int path = resid ? kPathFp8Residual : kPathFp8;
     if (wide ? !choose_wide_shape(nvec, &shape)
-             : (vec || phased) ? !choose_shape(rows, nvec, path, &shape) : !choose_elem_shape(rows, hidden, &shape))
+             : (vec || phased) ? !choose_shape(rows, nvec, path, (int)esz, &shape) : !choose_elem_shape(rows, hidden, &shape))
         return RMSQ_ERR_UNSUPPORTED;
     FusedArgs a{};
     a.x = x;
@@ -211,7 +211,7 @@ int sum_common(int64_t rows, int64_t hidden, int in_dtype, int ninputs, const vo
     if (residual_out != residual && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
 
     Shape shape;
-    if (!choose_shape(rows, (int)nvec, kPathFp8Sum, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    if (!choose_shape(rows, (int)nvec, kPathFp8Sum, (int)esz, &shape)) return RMSQ_ERR_UNSUPPORTED;
     SumArgs sa{};
     FusedArgs& a = sa.a;
     a.residual = residual;
@@ -298,7 +298,7 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
         if (!on_r && overlap(sro, sr)) return RMSQ_ERR_ALIAS;
     }
     Shape shape;
-    if (wide ? !choose_wide_shape(nvec, &shape) : !choose_shape(rows, nvec, resid ? kPathFp4Residual : kPathFp4, &shape))
+    if (wide ? !choose_wide_shape(nvec, &shape) : !choose_shape(rows, nvec, resid ? kPathFp4Residual : kPathFp4, (int)esz, &shape))
         return RMSQ_ERR_UNSUPPORTED;
     FusedArgs a{};
     a.x = x;
@@ -328,7 +328,7 @@ int fp4_common(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_
 
 }  // namespace
 
-bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
+bool choose_shape(int64_t rows, int nvec, int path, int esz, Shape* s) {
     int waves = g_tune_waves.load(std::memory_order_relaxed);
     int vpt = g_tune_vpt.load(std::memory_order_relaxed);
     if (waves == 0 && vpt == 0) {
@@ -363,11 +363,19 @@ bool choose_shape(int64_t rows, int nvec, int path, Shape* s) {
                                : (path == kPathFp4 || path == kPathFp8) ? order_4
                                                                         : order_2;
             const bool one_at_4 = wide && path != kPathFp4Residual && path != kPathFp8Sum;  // 1 vector per lane only at 4 waves
+            // fp32 rows with a residual hold more than 64 VGPRs per lane in
+            // the FP8 kernel, so a 16-wave block leaves room for only one per
+            // CU (12 waves: two): 16-wave shapes are taken only when no
+            // other shape holds the row (32768 x 8192 fp32 rows: 562 us as
+            // 8 x 4 against 649 us as 16 x 2, A/B in one process)
+            const bool cap8 = esz == 4 && path == kPathFp8Residual;
             int64_t best_idle = INT64_MAX;
             waves = 0;
+            for (int pass = 0; pass < (cap8 ? 2 : 1) && waves == 0; ++pass)
             for (int i = 0; i < 3; ++i) {
                 const int v = order[i];
                 for (int w : {1, 2, 4, 8, 12, 16}) {
+                    if (cap8 && pass == 0 && w == 16) continue;
                     if (wide && (w < 4 || (one_at_4 && v == 1 && w > 4))) continue;
                     const int64_t idle = (int64_t)w * 64 * v - nvec;
                     if (idle >= 0 && idle < best_idle) {
@@ -621,7 +629,7 @@ int rmsq_query_shape(int64_t rows, int64_t hidden, int in_dtype, int path, int* 
         if (path == kPathFp8Sum || hidden % elems_per_vec(in_dtype) != 0 || nvec > kMaxWideVec ||
             !choose_wide_shape((int)nvec, &s))
             return RMSQ_ERR_UNSUPPORTED;
-    } else if (!choose_shape(rows, (int)nvec, path, &s)) {
+    } else if (!choose_shape(rows, (int)nvec, path, (int)elem_size(in_dtype), &s)) {
         return RMSQ_ERR_UNSUPPORTED;
     }
     if (waves_per_row) *waves_per_row = s.waves;

@@ -148,14 +148,17 @@ __device__ __forceinline__ float abs_max(float m, const float* t) {
 
 // ---- per-row scalars in fp64 --------------------------------------------------
 // 1/sqrt(m) and 1/d: the hardware estimate (v_rsq_f64 / v_rcp_f64) refined by
-// one Newton step, which squares its relative error to far below fp32's
-// resolution.  Computed once per row, so fp64 costs nothing measurable.
+// two Newton steps, each of which squares the relative error, so the result
+// is within a few fp64 units of the exact value whatever the estimate's
+// accuracy.  Computed once per row or block, so fp64 costs nothing measurable.
 __device__ __forceinline__ double rsqrt_refined(double m) {
-    const double r = __builtin_amdgcn_rsq(m);
+    double r = __builtin_amdgcn_rsq(m);
+    r = r * (1.5 - 0.5 * m * r * r);
     return r * (1.5 - 0.5 * m * r * r);
 }
 __device__ __forceinline__ double rcp_refined(double d) {
-    const double r = __builtin_amdgcn_rcp(d);
+    double r = __builtin_amdgcn_rcp(d);
+    r = r * (2.0 - d * r);
     return r * (2.0 - d * r);
 }
 
@@ -247,6 +250,33 @@ __device__ __forceinline__ float block_max_nonneg(float v) {
     if constexpr (LPB == 2) return pair_max_nonneg(v);
     else if constexpr (LPB == 4) return quad_max_nonneg(v);
     else return oct_max_nonneg(v);
+}
+
+// max over the wave of non-negative doubles, on their bit patterns (the
+// integer order of non-negative IEEE doubles is their numeric order).
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ double wave_max_nonneg(double v) {
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    b = max_u64(b, dpp_u64<DPP_SWAP1>(b));
+    b = max_u64(b, dpp_u64<DPP_SWAP2>(b));
+    b = max_u64(b, dpp_u64<DPP_HALF_MIRROR>(b));
+    b = max_u64(b, dpp_u64<DPP_MIRROR>(b));
+    b = max_u64(max_u64(readlane_u64(b, 0), readlane_u64(b, 16)), max_u64(readlane_u64(b, 32), readlane_u64(b, 48)));
+    return __builtin_bit_cast(double, b);
 }
 
 // ---- conversions ------------------------------------------------------------
@@ -364,6 +394,105 @@ __device__ __forceinline__ void store_scale(void* scales, int64_t i, int scales_
         reinterpret_cast<uint32_t*>(scales)[i] = bits;
     else
         reinterpret_cast<uint16_t*>(scales)[i] = (uint16_t)bits;
+}
+
+// ---- FP8 per-row numerics -------------------------------------------------
+// The codes follow q = s * (gamma + weight_offset) * rstd / stored_scale
+// rounded ONCE to fp32 (the precision the conversion instruction takes), so
+// they agree with the exact definition except where q lies within a few
+// units of 2^-46 of an fp32 rounding midpoint:
+//  * sum of squares: every s^2 is exact in fp64 and accumulated there (the
+//    row's rstd then carries ~2^-50 relative error instead of the ~2^-29 of
+//    fp32 partial sums, which decided near-ties of the codes);
+//  * the factor k = rstd / stored_scale is formed in fp64 and split into two
+//    fp32 terms hi + lo (k to ~2^-48);
+//  * the product s * g' and its row maximum are exact, formed one of three
+//    ways (compile time, chosen by the input type and whether a weight offset
+//    is added):
+//      kProdF32  16-bit inputs, no offset: s * g has at most 22 significant
+//                bits, so t = s * g is exact in fp32; q = t * hi + t * lo
+//                (one multiply, one FMA);
+//      kProdTwo  fp32 inputs, no offset: s * g = th + tl exactly (th the fp32
+//                product, tl its error from an FMA); the row maximum in fp64;
+//                q = th * hi + (th * lo + tl * hi) (three FMAs);
+//      kProdF64  a weight offset (g + offset is not exact in fp32): s * g'
+//                in fp64, q = fp32(s * g' * k).
+//    A row whose |q| could exceed 2^100 (a binding scale_ub far below the
+//    row's scale, or a row maximum below ~2^-92) takes fp64 for every
+//    element: the fp32 terms could overflow.
+enum : int { kProdF32 = 0, kProdTwo = 1, kProdF64 = 2 };
+
+template <typename InT>
+inline constexpr int prod_mode(float weight_offset) {
+    return weight_offset != 0.0f ? kProdF64 : (Vec<InT>::BYTES == 4 ? kProdTwo : kProdF32);
+}
+
+// acc + s^2 in fp64 for each of N fp32 values (their squares are exact in
+// fp64); two interleaved chains keep the FMAs independent.
+template <int N>
+__device__ __forceinline__ void sumsq64(double& a0, double& a1, const float* s) {
+#pragma unroll
+    for (int e = 0; e < N; e += 2) {
+        const double d0 = s[e];
+        a0 = fma(d0, d0, a0);
+        if (e + 1 < N) {
+            const double d1 = s[e + 1];
+            a1 = fma(d1, d1, a1);
+        }
+    }
+}
+
+// |s * (g + off)| exact in fp64 (off = 0 for kProdTwo)
+__device__ __forceinline__ double abs_prod64(float s, float g, double off) {
+    return fabs((double)s * ((double)g + off));
+}
+
+struct Fp8Row {
+    double k;        // rstd / stored scale (0 for a zero scale)
+    float hi, lo;    // k = hi + lo to ~2^-48 relative
+    bool split;      // the fp32-term forms cannot overflow (else fp64)
+    uint32_t sbits;  // the stored scale's bits in the scales dtype
+};
+
+// The row's scale min(amax * rstd / FMAX, scale_ub) (fp64), rounded to fp32
+// and then to the scales dtype, and the quantization factor for it.  amax is
+// max |s * g'| over the row, exact.
+__device__ __forceinline__ Fp8Row fp8_row(double amax, double rstd, double inv_fmax, float scale_ub,
+                                          int scales_dtype) {
+    Fp8Row r;
+    double sc = amax * rstd * inv_fmax;
+    if (sc > (double)scale_ub) sc = (double)scale_ub;
+    const float sc_st = round_scale((float)sc, scales_dtype, &r.sbits);
+    r.k = sc_st > 0.0f ? rstd * rcp_refined((double)sc_st) : 0.0;
+    // hi = k rounded toward zero, so lo = k - hi >= 0: then every term of
+    // the split forms carries the sign of a zero product (an fp32 sum of
+    // zeros of opposite signs would be +0, and the code's sign bit -0)
+    float hi = (float)r.k;
+    if ((double)hi > r.k) hi = __uint_as_float(__float_as_uint(hi) - 1u);
+    r.hi = hi;
+    r.lo = (float)(r.k - (double)hi);
+    // |q| <= amax * k: below 2^100 no fp32 term can overflow; a zero scale
+    // (k = 0) takes fp64, where y * 0 keeps the sign of y
+    r.split = r.k > 0.0 && r.k < 0x1p100 && amax * r.k < 0x1p100;
+    return r;
+}
+
+// kProdF32: q = fp32(t * k) for t exact in fp32 (split rows).
+__device__ __forceinline__ float fp8_q1(float t, const Fp8Row& r) { return fmaf(t, r.hi, t * r.lo); }
+
+// kProdTwo: q = fp32(s * g * k) for fp32 s and raw gamma g (split rows).  The product's
+// error tl = s * g - th (exact) is formed as -(th - s * g) so that it is a
+// zero of th's sign when the product is zero.
+__device__ __forceinline__ float fp8_q2(float s, float g, const Fp8Row& r) {
+    g += 0.0f;  // the definition's g + offset (offset 0 here): a -0 gamma becomes +0
+    const float th = s * g;
+    const float tl = -fmaf(-s, g, th);
+    return fmaf(th, r.hi, fmaf(th, r.lo, tl * r.hi));
+}
+
+// kProdF64 (and every row that is not split): q = fp32(s * (g + off) * k).
+__device__ __forceinline__ float fp8_q64(float s, float g, double off, const Fp8Row& r) {
+    return (float)((double)s * ((double)g + off) * r.k);
 }
 
 }  // namespace rmsq

@@ -19,9 +19,10 @@
 // start works; the price is 8x (16-bit) or 4x (fp32) more memory
 // instructions than the vector kernel, paid only off its fast path.
 //
-// Precision: s^2 summed in fp64 (exact products), rstd, the scale and the
-// quantization factor in fp64 once per row; per element t = s * g' and
-// q = t * k in fp32, as in the vector kernel.
+// Precision: as the vector kernel (the PROD forms of rmsq_device.h): s^2
+// summed in fp64, rstd, the scale and the factor k in fp64 once per row,
+// s * g' and its row maximum exact, and q = s * g' * k rounded once to fp32.
+// Held across the barrier: t = s * g' (kProdF32), or s and gamma's bits.
 #pragma once
 
 #include "rmsq_device.h"
@@ -30,7 +31,7 @@
 
 namespace rmsq {
 
-template <typename InT, bool RESID, bool FNUZ, int EPL>
+template <typename InT, bool RESID, bool FNUZ, int EPL, int PROD>
 __global__ void __launch_bounds__(1024) fp8_elem_kernel(const FusedArgs a) {
     using E = Elem<InT>;
     using Bits = typename E::Bits;
@@ -47,23 +48,26 @@ __global__ void __launch_bounds__(1024) fp8_elem_kernel(const FusedArgs a) {
     const int hidden = a.hidden;
     auto live = [&](int j) { return lt + j * T < hidden; };
     const Bits* gamma = static_cast<const Bits*>(a.gamma);
+    const double offd = PROD == kProdF64 ? (double)a.weight_offset : 0.0;
+    constexpr bool T32 = PROD == kProdF32;  // t = s * g' (exact in fp32) held
 
     __shared__ double red_sum[2][16];
-    __shared__ int red_max[2][16];
+    __shared__ uint64_t red_max[2][16];  // bits of each wave's (non-negative fp64) max |s * g'|
 
     int parity = 0;
     for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
         const int64_t row = row0 + slot;
         const bool active = row < a.rows;
 
-        float t[EPL4];  // s * g' (zero past the row)
+        float sv[EPL4];  // s (zero past the row), or t = s * g' (T32)
+        Bits gv[EPL];    // gamma's bits
 #pragma unroll
-        for (int j = 0; j < EPL4; ++j) t[j] = 0.0f;
-        double ssq = 0.0;
-        float amax = 0.0f;
+        for (int j = 0; j < EPL4; ++j) sv[j] = 0.0f;
+        double ssq0 = 0.0, ssq1 = 0.0;
+        double amax = 0.0;
         if (active) {
             const Bits* xr = reinterpret_cast<const Bits*>(static_cast<const char*>(a.x) + row * a.x_stride);
-            Bits xv[EPL], rv[RESID ? EPL : 1], gv[EPL];
+            Bits xv[EPL], rv[RESID ? EPL : 1];
             // all of the row's loads are issued before any store (residual_out
             // may be x or residual itself)
 #pragma unroll
@@ -88,27 +92,37 @@ __global__ void __launch_bounds__(1024) fp8_elem_kernel(const FusedArgs a) {
                     s = E::widen(sb);
                     if (live(j)) store_elem(ro + lt + j * T, sb);
                 }
-                ssq += (double)s * (double)s;
-                t[j] = s * (E::widen(gv[j]) + a.weight_offset);
-                amax = fmaxf(amax, fabsf(t[j]));
+                const double d = s;
+                if (j & 1)
+                    ssq1 = fma(d, d, ssq1);
+                else
+                    ssq0 = fma(d, d, ssq0);
+                if constexpr (T32) {
+                    // + weight_offset (0.0f here) as the definition's g + offset: a -0 gamma becomes +0
+                    sv[j] = s * (E::widen(gv[j]) + a.weight_offset);
+                    amax = fmax(amax, (double)fabsf(sv[j]));
+                } else {
+                    sv[j] = s;
+                    amax = fmax(amax, abs_prod64(s, E::widen(gv[j]), offd));
+                }
             }
         }
 
-        ssq = wave_sum(ssq);
+        double ssq = wave_sum(ssq0 + ssq1);
         amax = wave_max_nonneg(amax);
         if (waves > 1) {  // uniform over the block
             if ((lt & 63) == 0) {
                 red_sum[parity][red] = ssq;
-                red_max[parity][red] = __float_as_int(amax);
+                red_max[parity][red] = __builtin_bit_cast(uint64_t, amax);
             }
             __syncthreads();
             ssq = 0.0;
-            int m = 0;
+            uint64_t m = 0;
             for (int w = 0; w < waves; ++w) {
                 ssq += red_sum[parity][slot * waves + w];
-                m = max_bits(m, red_max[parity][slot * waves + w]);
+                m = max_u64(m, red_max[parity][slot * waves + w]);
             }
-            amax = __int_as_float(m);
+            amax = __builtin_bit_cast(double, m);
             // the other parity's slots are rewritten only after the next
             // barrier, which every wave reaches after finishing these reads
             parity ^= 1;
@@ -116,29 +130,37 @@ __global__ void __launch_bounds__(1024) fp8_elem_kernel(const FusedArgs a) {
 
         if (active) {
             const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
-            double sc = (double)amax * rstd * INV_FMAX;
-            if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
-            uint32_t sbits;
-            const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
-            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
-
+            const Fp8Row fr = fp8_row(amax, rstd, INV_FMAX, a.scale_ub, a.scales_dtype);
+            const bool split = PROD != kProdF64 && __builtin_amdgcn_readfirstlane((int)fr.split);  // uniform
+            float q[EPL4];
+            if (split) {
+#pragma unroll
+                for (int j = 0; j < EPL4; ++j)
+                    q[j] = j >= EPL ? 0.0f : T32 ? fp8_q1(sv[j], fr) : fp8_q2(sv[j], E::widen(gv[j]), fr);
+            } else {
+#pragma unroll
+                for (int j = 0; j < EPL4; ++j)
+                    q[j] = j >= EPL ? 0.0f
+                           : T32    ? (float)((double)sv[j] * fr.k)
+                                    : fp8_q64(sv[j], E::widen(gv[j]), offd, fr);
+            }
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
 #pragma unroll
             for (int j = 0; j < EPL4; j += 4) {
-                const uint32_t c = fp8_x4<FNUZ>(t[j] * kq, t[j + 1] * kq, t[j + 2] * kq, t[j + 3] * kq);
+                const uint32_t c = fp8_x4<FNUZ>(q[j], q[j + 1], q[j + 2], q[j + 3]);
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     if (j + k < EPL && live(j + k)) store_elem(orow + lt + (j + k) * T, (uint8_t)(c >> (8 * k)));
             }
-            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, fr.sbits);
         }
     }
 }
 
 namespace fp8_elem_launch {
 
-template <typename InT, bool RESID, bool FNUZ, int EPL>
-hipError_t launch(FusedArgs a, Shape s, hipStream_t stream) {
+template <typename InT, bool RESID, bool FNUZ, int EPL, int PROD>
+hipError_t launch_prod(FusedArgs a, Shape s, hipStream_t stream) {
     a.waves = s.waves;
     const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
     // default: one block per row group
@@ -146,9 +168,16 @@ hipError_t launch(FusedArgs a, Shape s, hipStream_t stream) {
     if (grid > groups) grid = groups;
     if (grid > INT32_MAX) grid = INT32_MAX;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((fp8_elem_kernel<InT, RESID, FNUZ, EPL>), dim3((unsigned)grid), dim3(s.waves * s.rpb * 64),
-                       0, stream, a);
+    hipLaunchKernelGGL((fp8_elem_kernel<InT, RESID, FNUZ, EPL, PROD>), dim3((unsigned)grid),
+                       dim3(s.waves * s.rpb * 64), 0, stream, a);
     return hipGetLastError();
+}
+
+// the product form: kProdF32 / kProdTwo without a weight offset, else kProdF64
+template <typename InT, bool RESID, bool FNUZ, int EPL>
+hipError_t launch(const FusedArgs& a, Shape s, hipStream_t stream) {
+    if (prod_mode<InT>(a.weight_offset) == kProdF64) return launch_prod<InT, RESID, FNUZ, EPL, kProdF64>(a, s, stream);
+    return launch_prod<InT, RESID, FNUZ, EPL, prod_mode<InT>(0.0f)>(a, s, stream);
 }
 
 // s.vpt carries the elements per lane: one of kElemPerLane (rmsq_internal.h)

@@ -19,12 +19,15 @@
 // gamma + weight_offset comes from L2).  STRIDED (compile time) reads each
 // row tensor's row stride from the arguments; otherwise rows are adjacent.
 //
-// Precision: s^2 is summed in fp32 within a 16-byte vector (v_dot2c on packed
-// 16-bit pairs, whose squares are exact), then in fp64 per lane and across
-// lanes; rstd, the scale and the quantization factor are formed in fp64 once
-// per row.  Per element the kernel computes t = s * g' and q = t * k
-// (k = rstd / stored_scale) in fp32, so a code sees at most three fp32
-// roundings of relative error.
+// Precision: q = s * g' * rstd / stored_scale is rounded once to fp32 (the
+// helpers and the PROD forms in rmsq_device.h, "FP8 per-row numerics"): s^2
+// is accumulated in fp64, the factor k = rstd / stored_scale is formed in
+// fp64, and s * g' and its row maximum are exact.  What is held across the
+// barrier: t = s * g' in fp32 (kProdF32); the packed row s and packed 16-bit
+// gamma (the other forms), with fp32 gamma staged in LDS instead of held
+// (its 4 VGPRs per vector would leave room for only one 1024-thread block
+// per CU; taken from L2 again after the barrier instead it measured 8% slower
+// on 32768 x 8192 fp32 rows, the load's latency exposed on every row).
 #pragma once
 
 #include "rmsq_device.h"
@@ -32,11 +35,17 @@
 
 namespace rmsq {
 
-template <typename InT, bool RESID, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW, bool STRIDED, bool GAMMA_FIRST>
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW, bool STRIDED, bool GAMMA_FIRST,
+          int PROD>
 __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
     constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
+    static_assert(PROD != kProdF32 || V::BYTES == 2, "fp32 products are not exact in fp32");
+    static_assert(PROD != kProdTwo || V::BYTES == 4, "the two-term form is for fp32 inputs");
+    constexpr bool T32 = PROD == kProdF32;  // t = s * g' held in fp32
+    // gamma held across the barrier (else taken from L2 again after it)
+    constexpr bool HOLD_G = GAMMA_FIRST || V::BYTES == 2;
 
     const int waves = a.waves;       // wavefronts per row
     const int T = waves * 64;        // lanes per row
@@ -54,27 +63,44 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
     const int64_t r_stride = STRIDED ? a.residual_stride : row_bytes;
     const int64_t ro_stride = STRIDED ? a.residual_out_stride : row_bytes;
     const int64_t out_stride = STRIDED ? a.out_stride : (int64_t)a.hidden;
+    const double offd = PROD == kProdF64 ? (double)a.weight_offset : 0.0;
 
     __shared__ double red_sum[2][16];
-    __shared__ int red_max[2][16];
+    __shared__ uint64_t red_max[2][16];  // bits of each wave's (non-negative fp64) max |s * g'|
+    // fp32 gamma, VPT vectors per thread (dynamic LDS of blockDim * VPT * 16
+    // bytes; HOLD_G false only): each lane writes its own vectors with the
+    // row's loads and reads them back to quantize, so no barrier is involved
+    extern __shared__ uint4 g_stash[];
 
-    // gamma + weight_offset for this lane's columns, fp32 (zero past the row).
-    // GAMMA_FIRST (small batches without a residual): loaded and unpacked
-    // once, before the rows; otherwise loaded with each row, after the row's
-    // own loads and in flight together with them.  Measured on MI355X: a
-    // one-row call has ~6% lower latency the first way; large batches stream
-    // 3.5-7% faster the second way without a residual, ~1% with one.
-    float g[VPT][EPV];
+    // Gamma for this lane's columns (zero past the row): g + weight_offset in
+    // fp32 (kProdF32, where the offset is 0), or packed gamma (the other
+    // forms; the offset added in fp64).  GAMMA_FIRST (small batches without a
+    // residual): loaded once, before the rows; otherwise loaded with each
+    // row, after the row's own loads and in flight together with them.
+    // Measured on MI355X: a one-row call has ~6% lower latency the first way;
+    // large batches stream 3.5-7% faster the second way without a residual,
+    // ~1% with one.
+    float g[T32 ? VPT : 1][EPV];
+    uint4 gp[T32 ? 1 : VPT];  // packed gamma (the forms other than kProdF32)
     auto load_gamma = [&]() {
         uint4 gv[VPT];
 #pragma unroll
         for (int k = 0; k < VPT; ++k)
             gv[k] = live(k) ? reinterpret_cast<const uint4*>(a.gamma)[lt + k * T] : make_uint4(0, 0, 0, 0);
+        if constexpr (!T32) {
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            V::unpack(gv[k], g[k]);
+            for (int k = 0; k < VPT; ++k) {
+                gp[k] = gv[k];
+                if constexpr (!HOLD_G) g_stash[k * blockDim.x + tid] = gv[k];
+            }
+        } else {
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) g[k][e] = live(k) ? g[k][e] + a.weight_offset : 0.0f;
+            for (int k = 0; k < VPT; ++k) {
+                V::unpack(gv[k], g[k]);
+                // + 0.0f as the definition's g + offset (a -0 gamma becomes +0)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) g[k][e] = live(k) ? g[k][e] + a.weight_offset : 0.0f;
+            }
         }
     };
     if constexpr (GAMMA_FIRST) load_gamma();
@@ -84,13 +110,14 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
         const int64_t row = row0 + slot;
         const bool active = row < a.rows;
 
-        float t[VPT][EPV];  // s * g'
-        double ssq = 0.0;
-        float amax = 0.0f;
+        float t[T32 ? VPT : 1][EPV];  // s * g' (exact in fp32)
+        uint4 xv[VPT];                // the row s (packed); held across the barrier by the other forms
+        double ssq0 = 0.0, ssq1 = 0.0;
+        float amax32 = 0.0f;
+        double amax64 = 0.0;
         if (active) {
             const char* xr = static_cast<const char*>(a.x) + row * x_stride;
             // vectors past the end of the row are zero: they add nothing
-            uint4 xv[VPT];
 #pragma unroll
             for (int k = 0; k < VPT; ++k) xv[k] = live(k) ? load_stream(xr, lt + k * T) : make_uint4(0, 0, 0, 0);
             // every load of the row is issued before any store: residual_out
@@ -123,30 +150,37 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
             }
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
-                ssq += (double)V::sumsq(xv[k]);
                 float s[EPV];
                 V::unpack(xv[k], s);
+                sumsq64<EPV>(ssq0, ssq1, s);
+                if constexpr (T32) {
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) t[k][e] = s[e] * g[k][e];
-                amax = abs_max<EPV>(amax, t[k]);
+                    for (int e = 0; e < EPV; ++e) t[k][e] = s[e] * g[k][e];
+                    amax32 = abs_max<EPV>(amax32, t[k]);
+                } else {
+                    float gf[EPV];
+                    V::unpack(gp[k], gf);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) amax64 = fmax(amax64, abs_prod64(s[e], gf[e], offd));
+                }
             }
         }
 
-        ssq = wave_sum(ssq);
-        amax = wave_max_nonneg(amax);
+        double ssq = wave_sum(ssq0 + ssq1);
+        double amax = T32 ? (double)wave_max_nonneg(amax32) : wave_max_nonneg(amax64);
         if (waves > 1) {  // uniform over the block
             if ((lt & 63) == 0) {
                 red_sum[parity][red] = ssq;
-                red_max[parity][red] = __float_as_int(amax);
+                red_max[parity][red] = __builtin_bit_cast(uint64_t, amax);
             }
             __syncthreads();
             ssq = 0.0;
-            int m = 0;
+            uint64_t m = 0;
             for (int w = 0; w < waves; ++w) {
                 ssq += red_sum[parity][slot * waves + w];
-                m = max_bits(m, red_max[parity][slot * waves + w]);
+                m = max_u64(m, red_max[parity][slot * waves + w]);
             }
-            amax = __int_as_float(m);
+            amax = __builtin_bit_cast(double, m);
             // the other parity's slots are rewritten only after the next
             // barrier, which every wave reaches after finishing these reads
             parity ^= 1;
@@ -154,48 +188,95 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
 
         if (active) {
             const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
-            double sc = (double)amax * rstd * INV_FMAX;
-            if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
-            uint32_t sbits;
-            const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
-            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
-
+            const Fp8Row fr = fp8_row(amax, rstd, INV_FMAX, a.scale_ub, a.scales_dtype);
+            const bool split = PROD != kProdF64 && __builtin_amdgcn_readfirstlane((int)fr.split);  // uniform
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * out_stride;
+            // vector k's codes stored (8 or 4 bytes per lane)
+            auto emit = [&](int k, const float (&q)[EPV]) {
+                if constexpr (EPV == 8) {
+                    uint2 w;
+                    w.x = fp8_x4<FNUZ>(q[0], q[1], q[2], q[3]);
+                    w.y = fp8_x4<FNUZ>(q[4], q[5], q[6], q[7]);
+                    store_stream(orow, lt + k * T, w);
+                } else {
+                    store_stream(orow, lt + k * T, fp8_x4<FNUZ>(q[0], q[1], q[2], q[3]));
+                }
+            };
+            // the forms that recompute s * g' from the packed row and gamma
+            auto gamma_at = [&](int k, float (&gf)[EPV]) {
+                V::unpack(HOLD_G ? gp[T32 ? 0 : k] : g_stash[k * blockDim.x + tid], gf);
+            };
+            if (split) {
 #pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                if (live(k)) {
-                    if constexpr (EPV == 8) {
-                        uint2 w;
-                        w.x = fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq);
-                        w.y = fp8_x4<FNUZ>(t[k][4] * kq, t[k][5] * kq, t[k][6] * kq, t[k][7] * kq);
-                        store_stream(orow, lt + k * T, w);
+                for (int k = 0; k < VPT; ++k) {
+                    if (!live(k)) continue;
+                    float q[EPV];
+                    if constexpr (T32) {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q1(t[k][e], fr);
                     } else {
-                        store_stream(orow, lt + k * T,
-                                     fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq));
+                        float s[EPV], gf[EPV];
+                        V::unpack(xv[k], s);
+                        gamma_at(k, gf);
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q2(s[e], gf[e], fr);
                     }
+                    emit(k, q);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    if (!live(k)) continue;
+                    float q[EPV];
+                    if constexpr (T32) {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = (float)((double)t[k][e] * fr.k);
+                    } else {
+                        float s[EPV], gf[EPV];
+                        V::unpack(xv[k], s);
+                        gamma_at(k, gf);
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q64(s[e], gf[e], offd, fr);
+                    }
+                    emit(k, q);
                 }
             }
-            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, fr.sbits);
         }
     }
 }
 
 namespace fp8_launch {
 
-template <typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED, bool GAMMA_FIRST>
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED, bool GAMMA_FIRST, int PROD>
 void launch_shape(const FusedArgs& a, Shape s, dim3 gd, dim3 bd, hipStream_t stream) {
     const bool exact = a.nvec == VPT * s.waves * 64;
+    // the LDS gamma stash of fp32 rows (the forms other than kProdF32)
+    const size_t lds = PROD != kProdF32 && Vec<InT>::BYTES == 4 && !GAMMA_FIRST ? (size_t)bd.x * VPT * 16 : 0;
     if (s.rpb == 1) {
         if (exact)
-            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, true, STRIDED, GAMMA_FIRST>), gd, bd, 0, stream, a);
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, true, STRIDED, GAMMA_FIRST, PROD>), gd, bd, lds,
+                               stream, a);
         else
-            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, true, STRIDED, GAMMA_FIRST>), gd, bd, 0, stream, a);
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, true, STRIDED, GAMMA_FIRST, PROD>), gd, bd, lds,
+                               stream, a);
     } else {
         if (exact)
-            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, false, STRIDED, GAMMA_FIRST>), gd, bd, 0, stream, a);
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, false, STRIDED, GAMMA_FIRST, PROD>), gd, bd, lds,
+                               stream, a);
         else
-            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, false, STRIDED, GAMMA_FIRST>), gd, bd, 0, stream, a);
+            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, false, STRIDED, GAMMA_FIRST, PROD>), gd, bd,
+                               lds, stream, a);
     }
+}
+
+// the product form: kProdF32 / kProdTwo without a weight offset, else kProdF64
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED, bool GAMMA_FIRST>
+void launch_numerics(const FusedArgs& a, Shape s, dim3 gd, dim3 bd, hipStream_t stream) {
+    if (prod_mode<InT>(a.weight_offset) == kProdF64)
+        launch_shape<InT, RESID, FNUZ, VPT, STRIDED, GAMMA_FIRST, kProdF64>(a, s, gd, bd, stream);
+    else
+        launch_shape<InT, RESID, FNUZ, VPT, STRIDED, GAMMA_FIRST, prod_mode<InT>(0.0f)>(a, s, gd, bd, stream);
 }
 
 template <typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED>
@@ -210,9 +291,9 @@ hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
     const dim3 gd((unsigned)grid), bd(s.waves * s.rpb * 64);
     // gamma before the rows only for small batches without a residual
     if (!RESID && a.rows <= kLatencyRows)
-        launch_shape<InT, RESID, FNUZ, VPT, STRIDED, !RESID>(a, s, gd, bd, stream);
+        launch_numerics<InT, RESID, FNUZ, VPT, STRIDED, !RESID>(a, s, gd, bd, stream);
     else
-        launch_shape<InT, RESID, FNUZ, VPT, STRIDED, false>(a, s, gd, bd, stream);
+        launch_numerics<InT, RESID, FNUZ, VPT, STRIDED, false>(a, s, gd, bd, stream);
     return hipGetLastError();
 }
 

@@ -26,6 +26,11 @@
 // from the next lane through ds_bpermute instead measured 2-4% slower); the
 // window is cut with byte funnel shifts (v_alignbyte_b32) chosen by a switch
 // on the head, which is uniform over the wavefronts of a row.
+//
+// Precision: as the vector kernel (the PROD forms of rmsq_device.h): s^2
+// accumulated in fp64, s * g' and its row maximum exact, and q = s * g' * k
+// rounded once to fp32.  Held across the barrier: t = s * g' (kProdF32), or
+// the row and its gamma window, packed.
 #pragma once
 
 #include "rmsq_device.h"
@@ -84,7 +89,7 @@ __device__ __forceinline__ uint4 window_from(const uint4& p, const uint4& c, int
     }
 }
 
-template <typename InT, bool RESID, bool FNUZ, int VPT, bool ONE_ROW>
+template <typename InT, bool RESID, bool FNUZ, int VPT, bool ONE_ROW, int PROD>
 __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
     using V = Vec<InT>;
     using E = Elem<InT>;
@@ -104,9 +109,11 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
     const int ngv = (hidden + EPV - 1) / EPV;  // gamma's vectors (gamma is 16-byte aligned)
 
     const uint4* gv = static_cast<const uint4*>(a.gamma);
+    const double offd = PROD == kProdF64 ? (double)a.weight_offset : 0.0;
+    constexpr bool T32 = PROD == kProdF32;  // t = s * g' (exact in fp32) held
 
     __shared__ double red_sum[2][16];
-    __shared__ int red_max[2][16];
+    __shared__ uint64_t red_max[2][16];  // bits of each wave's (non-negative fp64) max |s * g'|
 
     int parity = 0;
     // Adjacent rows share the 16-byte block at their boundary (one's last
@@ -131,19 +138,21 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
         const int tail = hidden - head - (nv - 1) * EPV;
         auto whole = [&](int d) { return d != nv - 1 || tail == EPV; };
 
-        float t[VPT][EPV];  // s * g' (zero outside the row)
-        float ht = 0.0f;    // the head element's s * g' (lanes lt < head)
-        double ssq = 0.0;
-        float amax = 0.0f;
+        uint4 xv[VPT];              // s (zero outside the row), packed
+        uint4 gw[T32 ? 1 : VPT];    // gamma's window for each vector (zero outside the row)
+        float t[T32 ? VPT : 1][EPV];  // s * g' (T32)
+        float hs = 0.0f;    // the head element's s (lanes lt < head)
+        Bits hg = 0;        // and its gamma
+        double ssq0 = 0.0, ssq1 = 0.0;
+        double amax = 0.0;
         if (active) {
             const char* xb = xr + head * ESZ;  // 16-byte aligned
-            uint4 xv[VPT];
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int d = lt + k * T;
                 xv[k] = d < nv ? load_stream(xb, d) : make_uint4(0, 0, 0, 0);
             }
-            Bits hx = 0, hr = 0, hg = 0;
+            Bits hx = 0, hr = 0;
             if (lt < head) {
                 hx = load_elem(reinterpret_cast<const Bits*>(xr) + lt);
                 hg = static_cast<const Bits*>(a.gamma)[lt];
@@ -178,7 +187,7 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
                     if constexpr (RESID) rv[k] = keep_low_bytes(rv[k], tail * ESZ);
                 }
             }
-            float hs = E::widen(hx);
+            hs = E::widen(hx);
             if constexpr (RESID) {
                 char* ro = static_cast<char*>(a.residual_out) + row * a.residual_out_stride;
                 char* rob = ro + head * ESZ;
@@ -216,48 +225,60 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
                     hs = E::widen(sb);
                 }
             }
+            float amax32 = 0.0f;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int d = lt + k * T;
-                if (d < nv) {
-                    ssq += (double)V::sumsq(xv[k]);
-                    uint4 gw = head != 0 ? window_from<ESZ>(gc[k], gn[k], head) : gc[k];
-                    // gamma' past the row is not gamma (or not a number):
-                    // zero, so that t = 0 there
-                    if (!whole(d)) gw = keep_low_bytes(gw, tail * ESZ);
-                    float s[EPV], gf[EPV];
-                    V::unpack(xv[k], s);
-                    V::unpack(gw, gf);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) t[k][e] = s[e] * (gf[e] + a.weight_offset);
-                    amax = abs_max<EPV>(amax, t[k]);
-                } else {
+                if constexpr (T32) {
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) t[k][e] = 0.0f;
+                } else {
+                    gw[k] = make_uint4(0, 0, 0, 0);
+                }
+                if (d < nv) {
+                    uint4 w = head != 0 ? window_from<ESZ>(gc[k], gn[k], head) : gc[k];
+                    // gamma' past the row is not gamma (or not a number):
+                    // zero, so that s * g' = 0 there
+                    if (!whole(d)) w = keep_low_bytes(w, tail * ESZ);
+                    float s[EPV], gf[EPV];
+                    V::unpack(xv[k], s);
+                    V::unpack(w, gf);
+                    sumsq64<EPV>(ssq0, ssq1, s);
+                    if constexpr (T32) {
+                        // + weight_offset (0.0f here) as the definition's g + offset
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) t[k][e] = s[e] * (gf[e] + a.weight_offset);
+                        amax32 = abs_max<EPV>(amax32, t[k]);
+                    } else {
+                        gw[k] = w;
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) amax = fmax(amax, abs_prod64(s[e], gf[e], offd));
+                    }
                 }
             }
+            amax = fmax(amax, (double)amax32);
             if (lt < head) {
-                ssq += (double)hs * (double)hs;
-                ht = hs * (E::widen(hg) + a.weight_offset);
-                amax = fmaxf(amax, fabsf(ht));
+                const double d = hs;
+                ssq0 = fma(d, d, ssq0);
+                amax = fmax(amax, abs_prod64(hs, E::widen(hg), T32 ? (double)a.weight_offset : offd));
             }
         }
 
-        ssq = wave_sum(ssq);
+        double ssq = wave_sum(ssq0 + ssq1);
         amax = wave_max_nonneg(amax);
         if (waves > 1) {  // uniform over the block
             if ((lt & 63) == 0) {
                 red_sum[parity][red] = ssq;
-                red_max[parity][red] = __float_as_int(amax);
+                red_max[parity][red] = __builtin_bit_cast(uint64_t, amax);
             }
             __syncthreads();
             ssq = 0.0;
-            int m = 0;
+            uint64_t m = 0;
             for (int w = 0; w < waves; ++w) {
                 ssq += red_sum[parity][slot * waves + w];
-                m = max_bits(m, red_max[parity][slot * waves + w]);
+                m = max_u64(m, red_max[parity][slot * waves + w]);
             }
-            amax = __int_as_float(m);
+            amax = __builtin_bit_cast(double, m);
             // the other parity's slots are rewritten only after the next
             // barrier, which every wave reaches after finishing these reads
             parity ^= 1;
@@ -265,11 +286,8 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
 
         if (active) {
             const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
-            double sc = (double)amax * rstd * INV_FMAX;
-            if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
-            uint32_t sbits;
-            const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
-            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
+            const Fp8Row fr = fp8_row(amax, rstd, INV_FMAX, a.scale_ub, a.scales_dtype);
+            const bool split = PROD != kProdF64 && __builtin_amdgcn_readfirstlane((int)fr.split);  // uniform
 
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
             // codes of vector d start at ob + d * EPV (the host checked that
@@ -279,10 +297,30 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
             for (int k = 0; k < VPT; ++k) {
                 const int d = lt + k * T;
                 if (d >= nv) continue;
+                float q[EPV];
+                if constexpr (T32) {
+                    if (split) {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q1(t[k][e], fr);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = (float)((double)t[k][e] * fr.k);
+                    }
+                } else {
+                    float s[EPV], gf[EPV];
+                    V::unpack(xv[k], s);
+                    V::unpack(gw[k], gf);
+                    if (split) {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q2(s[e], gf[e], fr);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q64(s[e], gf[e], offd, fr);
+                    }
+                }
                 uint32_t wd[EPV / 4];
-                wd[0] = fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq);
-                if constexpr (EPV == 8)
-                    wd[1] = fp8_x4<FNUZ>(t[k][4] * kq, t[k][5] * kq, t[k][6] * kq, t[k][7] * kq);
+                wd[0] = fp8_x4<FNUZ>(q[0], q[1], q[2], q[3]);
+                if constexpr (EPV == 8) wd[1] = fp8_x4<FNUZ>(q[4], q[5], q[6], q[7]);
                 if (whole(d)) {
                     if constexpr (EPV == 8)
                         store_stream(ob, d, make_uint2(wd[0], wd[1]));
@@ -294,16 +332,18 @@ __global__ void __launch_bounds__(1024) fp8_phased_kernel(const FusedArgs a) {
                         if (e < tail) ob[d * EPV + e] = (uint8_t)(wd[e >> 2] >> (8 * (e & 3)));
                 }
             }
-            if (lt < head) orow[lt] = (uint8_t)fp8_x4<FNUZ>(ht * kq, 0.0f, 0.0f, 0.0f);
-            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+            if (lt < head)
+                orow[lt] = (uint8_t)fp8_x4<FNUZ>(fp8_q64(hs, E::widen(hg), T32 ? (double)a.weight_offset : offd, fr),
+                                                 0.0f, 0.0f, 0.0f);
+            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, fr.sbits);
         }
     }
 }
 
 namespace fp8_phased_launch {
 
-template <typename InT, bool RESID, bool FNUZ, int VPT>
-hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
+template <typename InT, bool RESID, bool FNUZ, int VPT, int PROD>
+hipError_t launch_prod(FusedArgs a, Shape s, hipStream_t stream) {
     a.waves = s.waves;
     const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
     // default: one block per row group
@@ -313,10 +353,17 @@ hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
     if (grid < 1) grid = 1;
     const dim3 gd((unsigned)grid), bd(s.waves * s.rpb * 64);
     if (s.rpb == 1)
-        hipLaunchKernelGGL((fp8_phased_kernel<InT, RESID, FNUZ, VPT, true>), gd, bd, 0, stream, a);
+        hipLaunchKernelGGL((fp8_phased_kernel<InT, RESID, FNUZ, VPT, true, PROD>), gd, bd, 0, stream, a);
     else
-        hipLaunchKernelGGL((fp8_phased_kernel<InT, RESID, FNUZ, VPT, false>), gd, bd, 0, stream, a);
+        hipLaunchKernelGGL((fp8_phased_kernel<InT, RESID, FNUZ, VPT, false, PROD>), gd, bd, 0, stream, a);
     return hipGetLastError();
+}
+
+// the product form: kProdF32 / kProdTwo without a weight offset, else kProdF64
+template <typename InT, bool RESID, bool FNUZ, int VPT>
+hipError_t launch_vpt(const FusedArgs& a, Shape s, hipStream_t stream) {
+    if (prod_mode<InT>(a.weight_offset) == kProdF64) return launch_prod<InT, RESID, FNUZ, VPT, kProdF64>(a, s, stream);
+    return launch_prod<InT, RESID, FNUZ, VPT, prod_mode<InT>(0.0f)>(a, s, stream);
 }
 
 template <typename InT, bool RESID, bool FNUZ>

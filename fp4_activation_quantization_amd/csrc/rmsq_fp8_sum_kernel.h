@@ -13,9 +13,9 @@
 // conversion; 16-bit types: rounded to odd at fp32 precision, then to nearest
 // even at 8 / 11 bits, which is exact because fp32 keeps more than two
 // extra bits).  s is stored to residual_out and normalized and quantized as
-// in the residual FP8 kernel (rmsq_fp8_kernel.h), with the same mapping:
-// `waves` wavefronts per row, lane l owns the 16-byte vectors l, l + T, ...
-// Rows are adjacent and whole vectors.
+// in the residual FP8 kernel (rmsq_fp8_kernel.h), with the same mapping and
+// numerics (the PROD forms of rmsq_device.h): `waves` wavefronts per row, lane l owns the
+// 16-byte vectors l, l + T, ...  Rows are adjacent and whole vectors.
 #pragma once
 
 #include "rmsq_device.h"
@@ -50,7 +50,7 @@ __device__ __forceinline__ uint4 round_sum(const double (&acc)[Vec<InT>::EPV]) {
     return V::pack(f);
 }
 
-template <typename InT, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW>
+template <typename InT, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW, int PROD>
 __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
     const FusedArgs& a = sa.a;
     using V = Vec<InT>;
@@ -69,18 +69,26 @@ __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
     constexpr int GRP = VPT > 2 ? 4 : 8;  // input vectors loaded together (measured: 8 is 4% faster at 2)
     auto live = [&](int k) { return EXACT || lt + k * T < nvec; };
     const int64_t row_bytes = (int64_t)a.hidden * V::BYTES;
+    const double offd = PROD == kProdF64 ? (double)a.weight_offset : 0.0;
+    static_assert(PROD != kProdF32 || V::BYTES == 2, "fp32 products are not exact in fp32");
+    static_assert(PROD != kProdTwo || V::BYTES == 4, "the two-term form is for fp32 inputs");
+    constexpr bool T32 = PROD == kProdF32;  // t = s * g' held in fp32
+    constexpr bool HOLD_G = V::BYTES == 2;  // packed gamma held; fp32 gamma from L2 again
 
     __shared__ double red_sum[2][16];
-    __shared__ int red_max[2][16];
+    __shared__ uint64_t red_max[2][16];
 
     int parity = 0;
     for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
         const int64_t row = row0 + slot;
         const bool active = row < a.rows;
 
-        float t[VPT][EPV];  // s * g'
-        double ssq = 0.0;
-        float amax = 0.0f;
+        float t[T32 ? VPT : 1][EPV];   // s * g' (exact in fp32)
+        uint4 sv[VPT];                 // the row s (packed); held across the barrier by the other forms
+        uint4 gp[T32 ? 1 : VPT];       // packed gamma (the other forms)
+        double ssq0 = 0.0, ssq1 = 0.0;
+        float amax32 = 0.0f;
+        double amax64 = 0.0;
         if (active) {
             const int64_t off = row * row_bytes;
             // s, vector by vector: the residual's vector, then the inputs'
@@ -88,7 +96,6 @@ __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
             // the registers bounded), summed in fp64 and rounded once; every
             // load of the row comes before any store (residual_out may be
             // residual)
-            uint4 sv[VPT];
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 sv[k] = make_uint4(0, 0, 0, 0);
@@ -119,33 +126,40 @@ __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 if (live(k)) store_stream(ro, lt + k * T, sv[k]);
-                ssq += (double)V::sumsq(sv[k]);
-                // gamma + weight_offset with the row (L2 hits)
+                // gamma with the row (L2 hits)
                 float s[EPV], g[EPV];
                 const uint4 gv = live(k) ? reinterpret_cast<const uint4*>(a.gamma)[lt + k * T] : make_uint4(0, 0, 0, 0);
                 V::unpack(gv, g);
                 V::unpack(sv[k], s);
+                sumsq64<EPV>(ssq0, ssq1, s);
+                if constexpr (!T32) {
+                    gp[k] = gv;
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) t[k][e] = live(k) ? s[e] * (g[e] + a.weight_offset) : 0.0f;
-                amax = abs_max<EPV>(amax, t[k]);
+                    for (int e = 0; e < EPV; ++e) amax64 = fmax(amax64, abs_prod64(s[e], g[e], offd));
+                } else {
+                    // + weight_offset (0.0f here) as the definition's g + offset: a -0 gamma becomes +0
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) t[k][e] = live(k) ? s[e] * (g[e] + a.weight_offset) : 0.0f;
+                    amax32 = abs_max<EPV>(amax32, t[k]);
+                }
             }
         }
 
-        ssq = wave_sum(ssq);
-        amax = wave_max_nonneg(amax);
+        double ssq = wave_sum(ssq0 + ssq1);
+        double amax = T32 ? (double)wave_max_nonneg(amax32) : wave_max_nonneg(amax64);
         if (waves > 1) {  // uniform over the block
             if ((lt & 63) == 0) {
                 red_sum[parity][red] = ssq;
-                red_max[parity][red] = __float_as_int(amax);
+                red_max[parity][red] = __builtin_bit_cast(uint64_t, amax);
             }
             __syncthreads();
             ssq = 0.0;
-            int m = 0;
+            uint64_t m = 0;
             for (int w = 0; w < waves; ++w) {
                 ssq += red_sum[parity][slot * waves + w];
-                m = max_bits(m, red_max[parity][slot * waves + w]);
+                m = max_u64(m, red_max[parity][slot * waves + w]);
             }
-            amax = __int_as_float(m);
+            amax = __builtin_bit_cast(double, m);
             // the other parity's slots are rewritten only after the next
             // barrier, which every wave reaches after finishing these reads
             parity ^= 1;
@@ -153,34 +167,51 @@ __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
 
         if (active) {
             const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
-            double sc = (double)amax * rstd * INV_FMAX;
-            if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
-            uint32_t sbits;
-            const float sc_st = round_scale((float)sc, a.scales_dtype, &sbits);
-            const float kq = sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
-
+            const Fp8Row fr = fp8_row(amax, rstd, INV_FMAX, a.scale_ub, a.scales_dtype);
+            const bool split = PROD != kProdF64 && __builtin_amdgcn_readfirstlane((int)fr.split);  // uniform
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * (int64_t)a.hidden;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 if (!live(k)) continue;
+                float q[EPV];
+                if constexpr (T32) {
+                    if (split) {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q1(t[k][e], fr);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = (float)((double)t[k][e] * fr.k);
+                    }
+                } else {
+                    float s[EPV], g[EPV];
+                    V::unpack(sv[k], s);
+                    V::unpack(HOLD_G ? gp[k] : reinterpret_cast<const uint4*>(a.gamma)[lt + k * T], g);
+                    if (split) {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q2(s[e], g[e], fr);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) q[e] = fp8_q64(s[e], g[e], offd, fr);
+                    }
+                }
                 if constexpr (EPV == 8) {
                     uint2 w;
-                    w.x = fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq);
-                    w.y = fp8_x4<FNUZ>(t[k][4] * kq, t[k][5] * kq, t[k][6] * kq, t[k][7] * kq);
+                    w.x = fp8_x4<FNUZ>(q[0], q[1], q[2], q[3]);
+                    w.y = fp8_x4<FNUZ>(q[4], q[5], q[6], q[7]);
                     store_stream(orow, lt + k * T, w);
                 } else {
-                    store_stream(orow, lt + k * T, fp8_x4<FNUZ>(t[k][0] * kq, t[k][1] * kq, t[k][2] * kq, t[k][3] * kq));
+                    store_stream(orow, lt + k * T, fp8_x4<FNUZ>(q[0], q[1], q[2], q[3]));
                 }
             }
-            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+            if (lt == 0) store_scale(a.scales, row, a.scales_dtype, fr.sbits);
         }
     }
 }
 
 namespace fp8_sum_launch {
 
-template <typename InT, bool FNUZ, int VPT>
-hipError_t launch_vpt(SumArgs sa, Shape s, hipStream_t stream) {
+template <typename InT, bool FNUZ, int VPT, int PROD>
+hipError_t launch_prod(SumArgs sa, Shape s, hipStream_t stream) {
     FusedArgs& a = sa.a;
     a.waves = s.waves;
     const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
@@ -193,16 +224,23 @@ hipError_t launch_vpt(SumArgs sa, Shape s, hipStream_t stream) {
     const bool exact = a.nvec == VPT * s.waves * 64;
     if (s.rpb == 1) {
         if (exact)
-            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, true, true>), gd, bd, 0, stream, sa);
+            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, true, true, PROD>), gd, bd, 0, stream, sa);
         else
-            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, false, true>), gd, bd, 0, stream, sa);
+            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, false, true, PROD>), gd, bd, 0, stream, sa);
     } else {
         if (exact)
-            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, true, false>), gd, bd, 0, stream, sa);
+            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, true, false, PROD>), gd, bd, 0, stream, sa);
         else
-            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, false, false>), gd, bd, 0, stream, sa);
+            hipLaunchKernelGGL((fp8_sum_kernel<InT, FNUZ, VPT, false, false, PROD>), gd, bd, 0, stream, sa);
     }
     return hipGetLastError();
+}
+
+// the product form: kProdF32 / kProdTwo without a weight offset, else kProdF64
+template <typename InT, bool FNUZ, int VPT>
+hipError_t launch_vpt(const SumArgs& sa, Shape s, hipStream_t stream) {
+    if (prod_mode<InT>(sa.a.weight_offset) == kProdF64) return launch_prod<InT, FNUZ, VPT, kProdF64>(sa, s, stream);
+    return launch_prod<InT, FNUZ, VPT, prod_mode<InT>(0.0f)>(sa, s, stream);
 }
 
 template <typename InT, bool FNUZ>

@@ -72,9 +72,10 @@ enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPath
 // variants are chosen for the time of one call); larger ones stream.
 constexpr int64_t kLatencyRows = 256;
 
-// Pick the automatic shape for a row of nvec 16-byte vectors (or apply the
-// process-wide override).  Returns false if no supported shape holds the row.
-bool choose_shape(int64_t rows, int nvec, int path, Shape* s);
+// Pick the automatic shape for a row of nvec 16-byte vectors of esz-byte
+// elements (or apply the process-wide override).  Returns false if no
+// supported shape holds the row.
+bool choose_shape(int64_t rows, int nvec, int path, int esz, Shape* s);
 
 // Shape of the wide-row kernels (16 waves, the row in LDS or registers; vpt
 // reports the vectors per lane they walk): false if a forced wave count other than 16 or

@@ -7,15 +7,19 @@
 // per-row scale; the residual form of "allreduce_residual_rmsnorm_fp8") and
 // of rmsq_fp4_kernel.h (FlashInfer "rmsnorm_fp4quant.py": E4M3 or UE8M0
 // block scales over 16 or 32 elements, row-major or swizzled, optionally the
-// page's 16-bit x * w product), with or without the residual, computed with
-// the same fp32 / fp64 steps as those kernels.
+// page's 16-bit x * w product), with or without the residual.  The sum of
+// squares and the steps after it are those of the register kernels: FP8
+// accumulates the squares in fp64 and rounds q = s * g' * k once to fp32
+// (t = s * g' exact in fp32 for 16-bit inputs without a weight offset, else
+// s * g' and its row maximum in fp64); FP4 takes the FP4 kernel's fp32
+// element steps.
 //
 // Work mapping: one 1024-thread block per row (blocks stride over rows);
 // lane l owns the 16-byte vectors l, l + 1024, ...  Pass 1 forms s (x, or
 // x + residual rounded once to the input type and stored to residual_out)
 // and accumulates sum(s^2) and, for FP8, max |s * g'| (g' = gamma +
 // weight_offset, read from L2); the block reduces both.  Pass 2 forms
-// t = s * g' again (the same fp32 products) and quantizes: FP8 with the
+// s * g' again (the same products) and quantizes: FP8 with the
 // row's scale, FP4 per block, whose lanes are adjacent as in the FP4 kernel.
 // HBM traffic is that of the register kernels: every input element read
 // once, every output written once.
@@ -62,52 +66,73 @@ __device__ __forceinline__ void product(const FusedArgs& a, int d, const uint4& 
     for (int e = 0; e < Vec<InT>::EPV; ++e) t[e] *= g[e];
 }
 
+// The FP8 product form (rmsq_device.h) for these arguments: uniform, so the
+// branches on it are scalar
+template <typename InT>
+__device__ __forceinline__ int prod_of(const FusedArgs& a) {
+    return prod_mode<InT>(a.weight_offset);
+}
+
 // Sum of squares and amax over the block (16 waves).  The slots are read
 // after the barrier; the caller keeps a later row from rewriting them before
 // every wave has read them.
-__device__ __forceinline__ void block_reduce(double& ssq, float& amax, bool with_max, double* red_sum,
-                                             int* red_max) {
+__device__ __forceinline__ void block_reduce(double& ssq, double& amax, bool with_max, double* red_sum,
+                                             uint64_t* red_max) {
     const int tid = threadIdx.x;
     ssq = wave_sum(ssq);
     if (with_max) amax = wave_max_nonneg(amax);
     if ((tid & 63) == 0) {
         red_sum[tid >> 6] = ssq;
-        red_max[tid >> 6] = __float_as_int(amax);
+        red_max[tid >> 6] = __builtin_bit_cast(uint64_t, amax);
     }
     __syncthreads();
     ssq = 0.0;
-    int m = 0;
+    uint64_t m = 0;
     for (int w = 0; w < kWideThreads / 64; ++w) {
         ssq += red_sum[w];
-        m = max_bits(m, red_max[w]);
+        m = max_u64(m, red_max[w]);
     }
-    amax = __int_as_float(m);
-}
-
-// FP8: the row's scale min(amax * rstd / FMAX, scale_ub), rounded to the
-// stored scale type (bits into *sbits); returns the element factor
-// rstd / stored scale (0 for an all-zero row)
-template <bool FNUZ>
-__device__ __forceinline__ float fp8_row_factor(const FusedArgs& a, float amax, double rstd, uint32_t* sbits) {
-    constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
-    double sc = (double)amax * rstd * INV_FMAX;
-    if (sc > (double)a.scale_ub) sc = (double)a.scale_ub;
-    const float sc_st = round_scale((float)sc, a.scales_dtype, sbits);
-    return sc_st > 0.0f ? (float)(rstd * rcp_refined((double)sc_st)) : 0.0f;
+    amax = __builtin_bit_cast(double, m);
 }
 
 // FP8 codes of vector d (s packed) into the row's output
 template <typename InT, bool FNUZ>
-__device__ __forceinline__ void fp8_store(const FusedArgs& a, uint8_t* orow, int d, const uint4& s, float kq) {
-    float t[Vec<InT>::EPV];
-    product<InT>(a, d, s, t);
-    if constexpr (Vec<InT>::EPV == 8) {
+__device__ __forceinline__ void fp8_store(const FusedArgs& a, uint8_t* orow, int d, const uint4& s, const Fp8Row& r,
+                                          bool split) {
+    using V = Vec<InT>;
+    constexpr int EPV = V::EPV;
+    float q[EPV];
+    const int prod = prod_of<InT>(a);
+    if (prod == kProdF32) {
+        float t[EPV];
+        product<InT>(a, d, s, t);
+        if (split) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) q[e] = fp8_q1(t[e], r);
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) q[e] = (float)((double)t[e] * r.k);
+        }
+    } else {
+        float sf[EPV], g[EPV];
+        V::unpack(s, sf);
+        V::unpack(static_cast<const uint4*>(a.gamma)[d], g);
+        if (prod == kProdTwo && split) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) q[e] = fp8_q2(sf[e], g[e], r);
+        } else {
+            const double offd = (double)a.weight_offset;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) q[e] = fp8_q64(sf[e], g[e], offd, r);
+        }
+    }
+    if constexpr (EPV == 8) {
         uint2 w;
-        w.x = fp8_x4<FNUZ>(t[0] * kq, t[1] * kq, t[2] * kq, t[3] * kq);
-        w.y = fp8_x4<FNUZ>(t[4] * kq, t[5] * kq, t[6] * kq, t[7] * kq);
+        w.x = fp8_x4<FNUZ>(q[0], q[1], q[2], q[3]);
+        w.y = fp8_x4<FNUZ>(q[4], q[5], q[6], q[7]);
         store_stream(orow, d, w);
     } else {
-        store_stream(orow, d, fp8_x4<FNUZ>(t[0] * kq, t[1] * kq, t[2] * kq, t[3] * kq));
+        store_stream(orow, d, fp8_x4<FNUZ>(q[0], q[1], q[2], q[3]));
     }
 }
 
@@ -184,10 +209,11 @@ __device__ __forceinline__ void fp4_store(const FusedArgs& a, const Fp4Row& r, i
 }
 
 // Pass 1's per-vector step: s of vector d (x, or x + residual rounded once
-// and stored to residual_out), its sum of squares and, for FP8, its amax
+// and stored to residual_out), its sum of squares (fp64) and, for FP8, its
+// max |s * g'| (exact)
 template <typename InT, bool RESID, bool FP8>
 __device__ __forceinline__ uint4 form_s(const FusedArgs& a, char* ro, int d, const uint4& xv, const uint4& rv,
-                                        double& ssq, float& amax) {
+                                        double& ssq, double& amax) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
     uint4 s = xv;
@@ -200,11 +226,28 @@ __device__ __forceinline__ uint4 form_s(const FusedArgs& a, char* ro, int d, con
         s = V::pack(xf);  // one rounding of the fp32 sum
         store_stream(ro, d, s);
     }
-    ssq += (double)V::sumsq(s);
-    if constexpr (FP8) {
-        float t[EPV];
-        product<InT>(a, d, s, t);
-        amax = abs_max<EPV>(amax, t);
+    if constexpr (!FP8) {
+        // FP4: fp32 within the vector (v_dot2c on packed 16-bit pairs), as
+        // the FP4 register kernel; unpacked floats here would be carried into
+        // pass 2 by the compiler and spill the register form
+        ssq += (double)V::sumsq(s);
+    } else {
+        float sf[EPV];
+        V::unpack(s, sf);
+        double s1 = 0.0;
+        sumsq64<EPV>(ssq, s1, sf);
+        ssq += s1;
+        if (prod_of<InT>(a) != kProdF32) {
+            float g[EPV];
+            V::unpack(static_cast<const uint4*>(a.gamma)[d], g);
+            const double offd = (double)a.weight_offset;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) amax = fmax(amax, abs_prod64(sf[e], g[e], offd));
+        } else {
+            float t[EPV];
+            product<InT>(a, d, s, t);
+            amax = fmax(amax, (double)abs_max<EPV>(0.0f, t));
+        }
     }
     return s;
 }
@@ -225,7 +268,7 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
 
     extern __shared__ uint4 row_s[];  // s of the current row: nvec vectors
     __shared__ double red_sum[16];
-    __shared__ int red_max[16];
+    __shared__ uint64_t red_max[16];
 
     const int tid = threadIdx.x;
     const int nvec = a.nvec;
@@ -236,8 +279,7 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
         const char* xr = static_cast<const char*>(a.x) + row * a.x_stride;
         const char* rr = RESID ? static_cast<const char*>(a.residual) + row * a.residual_stride : nullptr;
         char* ro = RESID ? static_cast<char*>(a.residual_out) + row * a.residual_out_stride : nullptr;
-        double ssq = 0.0;
-        float amax = 0.0f;
+        double ssq = 0.0, amax = 0.0;
         for (int i = 0; i < steps; ++i) {
             // chunk i: this lane's vectors tid + (i * U + u) * T.  Every load
             // of a chunk comes before any of its stores (residual_out may be
@@ -265,17 +307,17 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
 
         // ---- pass 2: quantize from LDS ----
         if constexpr (!FP4) {
-            uint32_t sbits;
-            const float kq = fp8_row_factor<FNUZ>(a, amax, rstd, &sbits);
+            const Fp8Row fr = fp8_row(amax, rstd, FNUZ ? 1.0 / 240.0 : 1.0 / 448.0, a.scale_ub, a.scales_dtype);
+            const bool split = __builtin_amdgcn_readfirstlane((int)fr.split);  // uniform over the block
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
             for (int i = 0; i < steps; ++i) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int d = tid + (i * U + u) * T;
-                    if (d < nvec) fp8_store<InT, FNUZ>(a, orow, d, row_s[d], kq);
+                    if (d < nvec) fp8_store<InT, FNUZ>(a, orow, d, row_s[d], fr, split);
                 }
             }
-            if (tid == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+            if (tid == 0) store_scale(a.scales, row, a.scales_dtype, fr.sbits);
         } else {
             const Fp4Row r = fp4_row<BLOCK>(a, row, rstd);
             for (int i = 0; i < steps; ++i) {
@@ -305,7 +347,7 @@ __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
     // the next row's barrier has passed this row's, so no wave can still be
     // reading the set it writes; one barrier per row
     __shared__ double red_sum[2][16];
-    __shared__ int red_max[2][16];
+    __shared__ uint64_t red_max[2][16];
 
     const int tid = threadIdx.x;
     const int nvec = a.nvec;
@@ -319,8 +361,7 @@ __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
             const int d = tid + k * T;
             sv[k] = d < nvec ? load_stream(xr, d) : make_uint4(0, 0, 0, 0);
         }
-        double ssq = 0.0;
-        float amax = 0.0f;
+        double ssq = 0.0, amax = 0.0;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int d = tid + k * T;
@@ -331,15 +372,15 @@ __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
 
         // ---- pass 2: quantize from registers ----
         if constexpr (!FP4) {
-            uint32_t sbits;
-            const float kq = fp8_row_factor<FNUZ>(a, amax, rstd, &sbits);
+            const Fp8Row fr = fp8_row(amax, rstd, FNUZ ? 1.0 / 240.0 : 1.0 / 448.0, a.scale_ub, a.scales_dtype);
+            const bool split = __builtin_amdgcn_readfirstlane((int)fr.split);  // uniform over the block
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 const int d = tid + k * T;
-                if (d < nvec) fp8_store<InT, FNUZ>(a, orow, d, sv[k], kq);
+                if (d < nvec) fp8_store<InT, FNUZ>(a, orow, d, sv[k], fr, split);
             }
-            if (tid == 0) store_scale(a.scales, row, a.scales_dtype, sbits);
+            if (tid == 0) store_scale(a.scales, row, a.scales_dtype, fr.sbits);
         } else {
             const Fp4Row r = fp4_row<BLOCK>(a, row, rstd);
 #pragma unroll

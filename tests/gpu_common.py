@@ -10,7 +10,7 @@ import torch
 import fp4_activation_quantization_amd as rq
 import oracle
 import workloads
-from parity import compare_fp4, compare_fp8, unswizzle_scales
+from parity import check_cap, compare_fp4, compare_fp8, unswizzle_scales
 
 DEV = "cuda:0"
 
@@ -76,11 +76,21 @@ def oracle_fp8(w, inp, *, rows_idx=None, ub=None, out_fmt=None, scales_dtype=Non
         if rows_idx is not None:
             ins = [t[rows_idx] for t in ins]
         ref = oracle.allreduce_residual_rmsnorm_fp8(ins, r, g, **q, **kw)
-        y = oracle.rmsnorm_y(ref["residual_out"], g, **kw)["y"]
-        return ref, y
+        return ref, _lazy(lambda: oracle.rmsnorm_y(ref["residual_out"], g, **kw)["y"])
     ref = oracle.rmsnorm_fp8(x, g, residual=r, **q, **kw)
-    y = oracle.rmsnorm_y(x, g, residual=r, round_product=w.fp4_round_product, **kw)["y"]
-    return ref, y
+    return ref, _lazy(lambda: oracle.rmsnorm_y(x, g, residual=r, round_product=w.fp4_round_product, **kw)["y"])
+
+
+def _lazy(fn):
+    """The oracle's y for the same rows, computed on first use only (the
+    comparator needs it where a 16-bit or block scale differs)."""
+    memo = []
+
+    def get():
+        if not memo:
+            memo.append(fn())
+        return memo[0]
+    return get
 
 
 def check_fp8(w, inp, *, rows_idx=None, label="", **kw):
@@ -144,10 +154,69 @@ def check_fp4(w, inp, gs, *, rows_idx=None, label="", weight_offset=None):
                              round_product=w.fp4_round_product, **kw)
     if r is not None:
         assert np.array_equal(ro, ref["residual_out"]), "residual_out differs from the oracle's"
-    y = oracle.rmsnorm_y(x, g, residual=r, round_product=w.fp4_round_product, **kw)["y"]
+    y = _lazy(lambda: oracle.rmsnorm_y(x, g, residual=r, round_product=w.fp4_round_product, **kw)["y"])
     rep = compare_fp4(p, bs, ref, y, global_scale=gsv, block_size=w.fp4_block, scale_format=w.fp4_scale)
     say(f"  parity {label or w.name}: {rep}")
     return rep
+
+
+_SUMMED = ("codes_total", "codes_boundary", "codes_boundary_ties", "block_scale_total", "block_scale_boundary",
+           "scale_boundary_rows")
+
+
+def check_whole(w, inp, gs=None, *, chunk_rows=2048, label=""):
+    """Every row of a workload at its full size: one call of the library on
+    the whole tensor (its automatic launch shape, the one the benchmark
+    times), then the oracle over row chunks, every element compared.  The
+    boundary flips of all chunks together must be at most 0.01% of the
+    tensor's codes (and of its 16-bit or block scales)."""
+    rows = w.rows
+    if w.fp4:
+        p_all, bs_all, ro_all = run_fp4(w, inp, gs)
+    else:
+        c_all, s_all, ro_all = run_fp8(w, inp)
+    tot = {k: 0 for k in _SUMMED}
+    scale_rel = 0.0
+    g = workloads.bits(inp["gamma"])
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        sl = slice(r0, r1)
+        if w.fp4:
+            x = workloads.bits(inp["x"][sl])
+            r = workloads.bits(inp["residual"][sl]) if w.residual else None
+            kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset)
+            ref = oracle.rmsnorm_fp4(x, g, global_scale=1.0 if gs is None else gs, block_size=w.fp4_block,
+                                     scale_format=w.fp4_scale, residual=r, round_product=w.fp4_round_product, **kw)
+            if r is not None:
+                assert np.array_equal(ro_all[sl], ref["residual_out"]), f"residual_out differs in rows {r0}..{r1}"
+            y = _lazy(lambda: oracle.rmsnorm_y(x, g, residual=r, round_product=w.fp4_round_product, **kw)["y"])
+            rep = compare_fp4(p_all[sl], bs_all[sl], ref, y, global_scale=1.0 if gs is None else gs,
+                              block_size=w.fp4_block, scale_format=w.fp4_scale, cap=False)
+        else:
+            part = dict(inp, x=inp["x"][sl])
+            if inp.get("residual") is not None:
+                part["residual"] = inp["residual"][sl]
+            if w.ninputs > 1:
+                part["inputs"] = [t[sl] for t in inp["inputs"]]
+            ref, y = oracle_fp8(w, part)
+            rep = compare_fp8(c_all[sl], s_all[sl], ref, y, out_fmt=w.out_fmt, scales_dtype=w.scales_dtype,
+                              gpu_residual_out=ro_all[sl] if ro_all is not None else None, cap=False)
+            scale_rel = max(scale_rel, rep.get("scale_max_rel", 0.0))
+        for k in _SUMMED:
+            tot[k] += rep.get(k, 0)
+        say(f"  [{label or w.name}] rows {r0}..{r1}: codes_boundary {rep['codes_boundary']}")
+    frac = tot["codes_boundary"] / max(tot["codes_total"], 1)
+    say(f"  whole-tensor parity {label or w.name}: codes_boundary/codes_total = {tot['codes_boundary']}/"
+        f"{tot['codes_total']} = {frac:.3g} (ties {tot['codes_boundary_ties']}), "
+        f"block_scale_boundary {tot['block_scale_boundary']}/{tot['block_scale_total']}, "
+        f"16-bit scale rows {tot['scale_boundary_rows']}, fp32 scale max rel {scale_rel:.3g}")
+    check_cap(tot["codes_boundary"], tot["codes_total"], f"{label or w.name} codes")
+    if w.fp4:
+        check_cap(tot["block_scale_boundary"], tot["block_scale_total"], f"{label or w.name} block scales")
+    else:
+        check_cap(tot["scale_boundary_rows"], rows, f"{label or w.name} 16-bit scales")
+    tot["fraction"] = frac
+    return tot
 
 
 def sample_rows(rows: int, k: int, seed: int, must=()):

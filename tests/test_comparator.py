@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from parity import compare_fp4, compare_fp8, near_midpoint
+from parity import check_cap, compare_fp4, compare_fp8, near_midpoint
 
 
 def _case(dt="bf16", rows=16, hidden=256, seed=0, resid=False, sdt="f32", fmt="e4m3fn"):
@@ -65,14 +65,27 @@ def test_one_step_across_a_midpoint_passes_but_wrong_direction_fails():
         compare_fp8(codes, ref["scales"], ref, y, out_fmt="e4m3fn", scales_dtype="f32")
 
 
-def test_exact_ties_are_not_capped_but_other_boundary_flips_are():
+def test_every_boundary_flip_counts_against_the_cap_ties_included():
+    # 4 rows x 6 exact ties: 24 flips in 32 codes, far above 0.01%
     ref, y = _tie_rows(4)
     codes = ref["codes"].copy()
     tie = (ref["codes"] == 0x7A) | (ref["codes"] == 0x7B)
-    codes[tie] ^= 0x01  # 0x7A <-> 0x7B at exact ties: every flip is a correct RNE result
-    rep = compare_fp8(codes, ref["scales"], ref, y, out_fmt="e4m3fn", scales_dtype="f32")
-    assert rep["codes_boundary_ties"] == int(tie.sum()) > 0
-    # q = 336 * (1 + 5e-7): inside the 1e-6 boundary band, not a tie
+    codes[tie] ^= 0x01  # 0x7A <-> 0x7B at exact ties
+    with pytest.raises(AssertionError, match="exceed"):
+        compare_fp8(codes, ref["scales"], ref, y, out_fmt="e4m3fn", scales_dtype="f32")
+    rep = compare_fp8(codes, ref["scales"], ref, y, out_fmt="e4m3fn", scales_dtype="f32", cap=False)
+    assert rep["codes_boundary"] == rep["codes_boundary_ties"] == int(tie.sum()) > 0
+    # one tie flip in 2000 x 8 = 16000 codes is within the cap; two are not
+    ref, y = _tie_rows(2000)
+    codes = ref["codes"].copy()
+    flip = lambda c: 0x7B if c == 0x7A else 0x7A  # noqa: E731
+    codes[0, 0] = flip(codes[0, 0])
+    assert compare_fp8(codes, ref["scales"], ref, y, out_fmt="e4m3fn", scales_dtype="f32")["codes_boundary"] == 1
+    codes[5, 2] = flip(codes[5, 2])
+    with pytest.raises(AssertionError, match="exceed"):
+        compare_fp8(codes, ref["scales"], ref, y, out_fmt="e4m3fn", scales_dtype="f32")
+    # q = 336 * (1 + 5e-7): inside the 1e-6 boundary band, not a tie; one
+    # flip in 32 codes exceeds the cap
     x = np.full((4, 8), 3.0, np.float32)
     x[:, 0] = np.float32(3.0 * (1 + 5e-7))
     x[:, 1] = 4.0
@@ -82,9 +95,14 @@ def test_exact_ties_are_not_capped_but_other_boundary_flips_are():
     y2 = oracle.rmsnorm_y(x, g, **kw)["y"]
     assert near_midpoint("e4m3fn", ref2["q"][:, 0]).all() and not near_midpoint("e4m3fn", ref2["q"][:, 0], 2.0**-22).any()
     c2 = ref2["codes"].copy()
-    c2[:, 0] = 0x7A if c2[0, 0] == 0x7B else 0x7B
+    c2[0, 0] = 0x7A if c2[0, 0] == 0x7B else 0x7B
     with pytest.raises(AssertionError, match="exceed"):
         compare_fp8(c2, ref2["scales"], ref2, y2, out_fmt="e4m3fn", scales_dtype="f32")
+    rep = compare_fp8(c2, ref2["scales"], ref2, y2, out_fmt="e4m3fn", scales_dtype="f32", cap=False)
+    assert rep["codes_boundary"] == 1 and rep["codes_boundary_ties"] == 0
+    with pytest.raises(AssertionError, match="exceed"):
+        check_cap(rep["codes_boundary"], rep["codes_total"])
+    check_cap(1, 10_000)
 
 
 def test_scale_tolerance():
