@@ -2,21 +2,27 @@
 
 One step = one call of the fused kernel over one batch of seeded synthetic
 activations already resident in HBM.  The headline workload is the residual
-path at Llama-3-8B width (8192 rows x 4096, bf16 in, e4m3fn out, fp32
-scales, bf16 residual_out); the metric is algorithmic HBM bytes per second.
+path at the large-batch 70B-class shape (32768 rows x 8192, bf16 in,
+e4m3fn out, fp32 scales, bf16 residual_out); the metric is algorithmic HBM
+bytes per second.
 
-Timing: W untimed warm-up steps, then K back-to-back steps between two HIP
-events recorded on the stream the kernel runs on, bracketed by device
-synchronizations.  A step is one kernel launch, so the average step time is
-the kernel's average launch duration (including the ~1 us dispatch gap
-between launches); per-launch event pairs are not used because they add
-several microseconds to every launch.  Buffers rotate through enough
-independent copies (>= 1 GiB in total) that the 256 MB Infinity Cache cannot
-serve a step from a previous one.
+Timing of the headline: untimed launches until the GPU has run at least
+--settle-ms of them (its clocks settle: a cold start runs the first
+milliseconds of launches slower), W untimed warm-up steps, then K
+back-to-back steps between two HIP events recorded on the stream the kernel
+runs on, bracketed by device synchronizations.  A step is one kernel launch,
+so the average step time is the kernel's average launch duration (including
+the ~1 us dispatch gap between launches); per-launch event pairs are not
+used because they add several microseconds to every launch.  Buffers rotate
+through enough independent copies (>= 1 GiB in total) that the 256 MB
+Infinity Cache cannot serve a step from a previous one.  Every other
+workload is timed after the same settling as the median of --windows
+windows of back-to-back launches, each at least --window-ms of GPU time.
 
 Printed: one JSON line.  Other workloads are reported in its "workloads"
 object; --workloads selects them (the headline leads when it is selected).
-The CPU baseline is the float64 oracle timed on the whole headline workload.
+The CPU baseline is the float64 oracle timed on each workload (the whole
+tensor or its first rows, bounded), on the CPU share the GPU job has.
 --copy-calibration runs only a plain copy of known size, the reference that
 rocprofv3's FETCH_SIZE / WRITE_SIZE readings are scaled by.
 """
@@ -26,6 +32,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -42,14 +49,18 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 CACHE_DEFEAT_BYTES = 1 << 30
 STREAM_MIN_BYTES = 16 << 20  # smaller workloads are latency-bound: no bandwidth reference
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["rmsq_fp8_kernel.h", "rmsq_fp4_kernel.h", "rmsq_device.h", "rmsq_api.cpp"]
+CSRC = os.path.join(ROOT, "fp4_activation_quantization_amd", "csrc")
 SC_T = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def kernel_source_hash() -> str:
+    """Hash of every source the library is built from (csrc/ and the public
+    header): counter summaries taken on other sources are stale."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, "fp4_activation_quantization_amd", "csrc", f), "rb").read())
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)) + [os.path.join(ROOT, "include", "rmsq.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -87,6 +98,8 @@ class Case:
         inp = workloads.make(w)
         dev = "cuda:0"
         self.w = w
+        self.inp = inp  # host tensors (the CPU baseline runs the oracle on them)
+        self.gs = gs
         x0 = inp["x"].to(dev)
         g = inp["gamma"].to(dev)
         r0 = inp["residual"].to(dev) if inp["residual"] is not None else None
@@ -188,6 +201,36 @@ def time_case(case: Case, steps: int, warmup: int) -> dict:
             "gbps": b / (per_us * 1e-6) / 1e9, "rows_per_s": case.w.rows / (per_us * 1e-6)}
 
 
+def settle(case: Case, min_ms: float) -> int:
+    """Untimed launches until at least min_ms of GPU time has elapsed (in
+    chunks timed by events): the GPU's clocks settle before measuring."""
+    done, elapsed, chunk = 0, 0.0, 8
+    while elapsed < min_ms:
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(chunk):
+            case.step(done + i)
+        t1.record()
+        torch.cuda.synchronize()
+        elapsed += t0.elapsed_time(t1)
+        done += chunk
+        chunk = min(chunk * 2, 4096)
+    return done
+
+
+def time_windows(case: Case, window_ms: float, windows: int) -> dict:
+    """Median over `windows` windows of back-to-back launches, each at least
+    window_ms of GPU time, timed like time_case."""
+    probe = time_case(case, 8, 0)["launch_us"]
+    n = max(8, int(math.ceil(window_ms * 1e3 / max(probe, 1e-3))))
+    per = sorted(time_case(case, n, 0)["launch_us"] for _ in range(windows))
+    med = per[len(per) // 2]
+    b = algorithmic_bytes(case.w)
+    return {"steps": n * windows, "window_launches": n, "windows": windows, "launch_us": med,
+            "launch_us_min": per[0], "launch_us_max": per[-1], "ms_per_step": med * 1e-3, "bytes": b,
+            "gbps": b / (med * 1e-6) / 1e9, "rows_per_s": case.w.rows / (med * 1e-6)}
+
+
 def time_graph(case: Case, calls: int, replays: int) -> dict:
     """Per-call GPU time of latency-sized launches without host launch
     overhead: `calls` back-to-back calls captured into one HIP graph (on the
@@ -233,38 +276,41 @@ def time_graph(case: Case, calls: int, replays: int) -> dict:
             "graph_replays": replays}
 
 
-def stream_ceiling(w: workloads.Workload, copies: int, steps: int, warmup: int) -> float:
-    """GB/s of the plain streaming reference kernel (rmsq_stream_probe) moving
-    this workload's read and write bytes, timed like the fused kernel and with
-    the same number of rotated buffer sets."""
-    rb, wb = algorithmic_split(w)
-    rb, wb = -(-rb // 16) * 16, -(-wb // 16) * 16
-    L = rq.lib()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    bufs = []
-    for _ in range(copies):
-        src = torch.ones(rb // 4, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty(wb // 4, dtype=torch.float32, device="cuda:0")
-        bufs.append((src, dst, (ctypes.c_void_p(src.data_ptr()), rb, ctypes.c_void_p(dst.data_ptr()), wb, stream)))
+class _Probe:
+    """rmsq_stream_probe moving a workload's read and write bytes, in the
+    shape time_case / time_windows expect (rotated buffer sets)."""
 
-    def step(i):
-        rc = L.rmsq_stream_probe(*bufs[i % copies][2])
+    def __init__(self, w: workloads.Workload, copies: int):
+        rb, wb = algorithmic_split(w)
+        self.rb, self.wb = -(-rb // 16) * 16, -(-wb // 16) * 16
+        self.w = w
+        L = rq.lib()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.bufs = []
+        for _ in range(copies):
+            src = torch.ones(self.rb // 4, dtype=torch.float32, device="cuda:0")
+            dst = torch.empty(self.wb // 4, dtype=torch.float32, device="cuda:0")
+            self.bufs.append((src, dst, (ctypes.c_void_p(src.data_ptr()), self.rb, ctypes.c_void_p(dst.data_ptr()),
+                                         self.wb, stream)))
+        self.fn = L.rmsq_stream_probe
+
+    def step(self, i: int) -> None:
+        rc = self.fn(*self.bufs[i % len(self.bufs)][2])
         if rc != 0:
-            raise rq.RmsqError("rmsq_stream_probe", rc, L.rmsq_last_hip_error())
+            raise rq.RmsqError("rmsq_stream_probe", rc, rq.lib().rmsq_last_hip_error())
 
-    for i in range(warmup):
-        step(i)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        step(warmup + i)
-    t1.record()
-    torch.cuda.synchronize()
-    per_s = t0.elapsed_time(t1) * 1e-3 / steps
-    del bufs
+
+def stream_ceiling(w: workloads.Workload, copies: int, settle_ms: float, window_ms: float, windows: int) -> float:
+    """GB/s of the plain streaming reference kernel (rmsq_stream_probe) moving
+    this workload's read and write bytes, timed like the workloads (settled,
+    median window) with the same number of rotated buffer sets."""
+    probe = _Probe(w, copies)
+    settle(probe, settle_ms)
+    us = time_windows(probe, window_ms, windows)["launch_us"]
+    gbps = (probe.rb + probe.wb) / (us * 1e-6) / 1e9
+    del probe
     torch.cuda.empty_cache()
-    return (rb + wb) / per_s / 1e9
+    return gbps
 
 
 def fp4_global_scale(name: str) -> float:
@@ -295,38 +341,79 @@ def traffic_from_profiles(name: str) -> float | None:
     return None
 
 
-def cpu_baseline(min_seconds: float) -> dict:
-    """The float64 oracle over the whole headline workload on host cores, repeated
-    until min_seconds have elapsed (at least one pass)."""
+def cpu_threads() -> int:
+    """Oracle threads: the 16-CPU share one GPU's job is allotted on a
+    shared MI355X host, or fewer where the machine has fewer cores."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_rate(case: Case, max_rows: int, threads: int, min_seconds: float) -> dict:
+    """The float64 oracle over the workload's first max_rows rows (all of
+    them if fewer) on `threads` threads, repeated until min_seconds have
+    elapsed (median pass), and on one thread over a 64-row sample; rows/s and
+    GB/s with the workload's algorithmic bytes per row."""
     import oracle
 
-    w = workloads.WORKLOADS[workloads.HEADLINE]
-    inp = workloads.make(w)
-    threads = max(1, min(16, os.cpu_count() or 1))
-    x, r, g = workloads.bits(inp["x"]), workloads.bits(inp["residual"]), workloads.bits(inp["gamma"])
+    w, inp = case.w, case.inp
+    n = min(w.rows, max_rows)
+    x = workloads.bits(inp["x"][:n])
+    r = workloads.bits(inp["residual"][:n]) if inp.get("residual") is not None else None
+    g = workloads.bits(inp["gamma"])
+    kw = dict(in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset, want_q=False)
+
+    def run(rows, th):
+        if w.fp4:
+            oracle.rmsnorm_fp4(x[:rows], g, global_scale=case.gs or 1.0, block_size=w.fp4_block,
+                               scale_format=w.fp4_scale, residual=r[:rows] if r is not None else None,
+                               round_product=w.fp4_round_product, threads=th, **kw)
+        elif w.ninputs > 1:
+            ins = [workloads.bits(t[:rows]) for t in inp["inputs"]]
+            oracle.allreduce_residual_rmsnorm_fp8(ins, r[:rows], g, scale_ub=w.scale_ub, out_fmt=w.out_fmt,
+                                                  scales_dtype=w.scales_dtype, threads=th, **kw)
+        else:
+            oracle.rmsnorm_fp8(x[:rows], g, scale_ub=w.scale_ub, out_fmt=w.out_fmt, scales_dtype=w.scales_dtype,
+                               residual=r[:rows] if r is not None else None, threads=th, **kw)
+
     oracle.lib()
-    passes, t0 = 0, time.perf_counter()
+    times, t_all = [], time.perf_counter()
     while True:
-        oracle.rmsnorm_fp8(x, g, in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset, scale_ub=w.scale_ub,
-                           out_fmt=w.out_fmt, scales_dtype=w.scales_dtype, residual=r, threads=threads, want_q=False)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
+        t0 = time.perf_counter()
+        run(n, threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all >= min_seconds or len(times) >= 3:
             break
-    per_pass = dt / passes
-    # one thread on the first rows, for the per-core rate
-    n1 = min(w.rows, 1024)
-    t1 = time.perf_counter()
-    oracle.rmsnorm_fp8(x[:n1], g, in_dtype=w.in_dtype, eps=w.eps, weight_offset=w.weight_offset, scale_ub=w.scale_ub,
-                       out_fmt=w.out_fmt, scales_dtype=w.scales_dtype, residual=r[:n1], threads=1, want_q=False)
-    d1 = time.perf_counter() - t1
+    per_pass = sorted(times)[len(times) // 2]
+    n1 = min(n, 64)
+    t0 = time.perf_counter()
+    run(n1, 1)
+    d1 = time.perf_counter() - t0
     row_bytes = algorithmic_bytes(w) / w.rows
-    return {"value": round(algorithmic_bytes(w) / per_pass / 1e9, 6), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "rows_per_s": round(w.rows / per_pass, 1), "seconds": round(dt, 2),
-            "sample": f"the whole {w.name} workload ({w.rows} rows), {passes} pass(es), float64 C oracle "
-                      f"split by rows over {threads} threads",
-            "single_thread": {"value": round(row_bytes * n1 / d1 / 1e9, 6), "unit": "GB/s",
-                              "rows_per_s": round(n1 / d1, 1), "sample": f"the first {n1} rows, one thread"}}
+    return {"rows_per_s": round(n / per_pass, 1), "gbps": round(row_bytes * n / per_pass / 1e9, 6),
+            "rows": n, "passes": len(times), "threads": threads,
+            "single_thread_rows_per_s": round(n1 / d1, 1)}
+
+
+def cpu_baseline(results: dict, lead: str) -> dict:
+    """The headline's oracle rate in the contract's form, with every timed
+    workload's beside it."""
+    threads = cpu_threads()
+    per = {n: r["cpu"] for n, r in results.items() if r.get("cpu")}
+    h = per.get(lead)
+    if h is None:
+        return {}
+    try:
+        quota = open("/sys/fs/cgroup/cpu.max").read().split()
+        cg = None if quota[0] == "max" else round(int(quota[0]) / int(quota[1]), 2)
+    except (OSError, ValueError, IndexError):
+        cg = None
+    return {"value": h["gbps"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {h['rows']} rows of {lead} (of {workload_of(lead).rows}), median of "
+                      f"{h['passes']} pass(es), float64 C oracle split by rows over {threads} threads",
+            "rows_per_s": h["rows_per_s"], "single_thread_rows_per_s": h["single_thread_rows_per_s"],
+            "host_logical_cpus": os.cpu_count(), "cgroup_cpu_quota": cg,
+            "threads_note": "a one-GPU job is allotted a 16-CPU share of the host; the oracle runs one thread "
+                            "per CPU of it (host_logical_cpus counts what the process sees)",
+            "per_workload": per}
 
 
 def copy_calibration(nbytes: int, steps: int) -> None:
@@ -361,7 +448,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workloads", default="all",
                     help="'all', 'headline' or comma-separated workload names or shapes op:ROWSxHIDDEN:dtype")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline time")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed GPU time before each workload's warm-up (clock settling)")
+    ap.add_argument("--window-ms", type=float, default=100.0, help="GPU time per timing window (other workloads)")
+    ap.add_argument("--windows", type=int, default=5, help="timing windows per workload other than the headline")
+    ap.add_argument("--cpu-seconds", type=float, default=1.0, help="minimum oracle time per workload")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of each workload the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming reference kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -388,6 +480,9 @@ def main() -> int:
     else:
         names = args.workloads.split(",")
     lead = workloads.HEADLINE if workloads.HEADLINE in names else names[0]
+    # the lead workload runs first, on a GPU whose memory no other workload
+    # has used yet (later runs of the same kernel measured up to 2% slower)
+    names = [lead] + [n for n in names if n != lead]
 
     results = {}
     for name in names:
@@ -396,29 +491,36 @@ def main() -> int:
         # ad-hoc FP4 shapes take a global scale of 64 (named ones their stored value)
         gs = (fp4_global_scale(name) if name in workloads.WORKLOADS else 64.0) if w.fp4 else None
         case = Case(w, k, gs)
-        steps = args.steps if name == workloads.HEADLINE else max(10, args.steps // 2)
-        res = time_case(case, steps, args.warmup)
+        settled = settle(case, args.settle_ms)
+        if name == lead:
+            res = time_case(case, args.steps, args.warmup)  # exactly K timed steps
+        else:
+            res = time_windows(case, args.window_ms, args.windows)
+        res["settle_launches"] = settled
         res["buffer_sets"] = k
         res["launch"] = rq.query_shape(w.rows, w.hidden, workloads.TORCH_DTYPES[w.in_dtype], w.fp4, w.residual,
                                        summed=w.ninputs > 1)
         # latency-sized calls: also their GPU time inside a graph (decode steps run graphed)
-        res.update(time_graph(case, 100, max(5, steps // 100)) if algorithmic_bytes(w) < STREAM_MIN_BYTES else {})
+        res.update(time_graph(case, 100, max(5, args.steps // 100)) if algorithmic_bytes(w) < STREAM_MIN_BYTES else {})
+        # the oracle on this workload's host inputs, after the GPU timing
+        res["cpu"] = None if args.no_cpu_baseline else oracle_rate(case, args.cpu_rows, cpu_threads(), args.cpu_seconds)
         results[name] = res
         del case
         torch.cuda.empty_cache()
         # the achievable ceiling for this traffic mix (bandwidth-sized workloads only)
-        res["stream_gbps"] = (stream_ceiling(w, k, steps, args.warmup)
+        res["stream_gbps"] = (stream_ceiling(w, k, args.settle_ms, args.window_ms, args.windows)
                               if algorithmic_bytes(w) >= STREAM_MIN_BYTES and not args.no_stream_ceiling else None)
         ceil = f", streaming reference {res['stream_gbps']:.0f} GB/s" if res["stream_gbps"] else ""
         if "graph_us" in res:
             ceil += f", {res['graph_us']:.2f} us per call in a graph (p50 over replays {res['graph_us_p50']:.2f})"
-        print(f"# {name}: {res['launch_us']:.2f} us/launch, {res['gbps']:.0f} GB/s{ceil}, {k} buffer set(s), "
+        cpu = f", oracle {res['cpu']['rows_per_s']:.0f} rows/s" if res["cpu"] else ""
+        print(f"# {name}: {res['launch_us']:.2f} us/launch, {res['gbps']:.0f} GB/s{ceil}{cpu}, {k} buffer set(s), "
               f"launch {res['launch']}", file=sys.stderr, flush=True)
 
     h = results[lead]
     w = workload_of(lead)
     line = {
-        "metric": "GB/s (algorithmic HBM bytes) for fused residual+RMSNorm+FP8 quant, 1 GPU"
+        "metric": "GB/s and % of HBM peak (rows/s) for fused residual+RMSNorm+FP8 quant, 1 GPU"
                   if lead == workloads.HEADLINE else f"GB/s (algorithmic HBM bytes) for {w.op}, 1 GPU",
         "value": round(h["gbps"], 2),
         "unit": "GB/s",
@@ -432,7 +534,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic (seeded PCG64 activations; see workloads.py)",
         "config": {"workload": w.name, "rows": w.rows, "hidden": w.hidden, "in_dtype": w.in_dtype,
-                   "op": w.op, "global_batch": w.rows, "buffer_sets": h["buffer_sets"], "launch": h["launch"]},
+                   "op": w.op, "global_batch": w.rows, "buffer_sets": h["buffer_sets"], "launch": h["launch"],
+                   "settle_launches": h["settle_launches"]},
         "rows_per_s": round(h["rows_per_s"], 1),
         "pct_hbm_peak": round(100.0 * h["gbps"] / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(h["gbps"], 2), "peak": HBM_PEAK_GBS,
@@ -441,6 +544,10 @@ def main() -> int:
                      "stream_reference": round(h["stream_gbps"], 1) if h["stream_gbps"] else None,
                      "launch_us": round(h["launch_us"], 3), "bytes_per_launch": h["bytes"]},
         "workloads": {n: {"launch_us": round(r["launch_us"], 3), "gbps": round(r["gbps"], 1),
+                          "timing": "exactly K steps" if n == lead else
+                          f"median of {r['windows']} windows of {r['window_launches']} launches",
+                          "launch_us_min": round(r.get("launch_us_min", r["launch_us"]), 3),
+                          "launch_us_max": round(r.get("launch_us_max", r["launch_us"]), 3),
                           "frac_hbm": round(r["gbps"] / HBM_PEAK_GBS, 4), "rows_per_s": round(r["rows_per_s"], 1),
                           "bytes": r["bytes"], "buffer_sets": r["buffer_sets"], "launch": r["launch"],
                           "graph_us": round(r["graph_us"], 3) if "graph_us" in r else None,
@@ -452,7 +559,7 @@ def main() -> int:
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(results, lead)
     print(json.dumps(line), flush=True)
     return 0
 

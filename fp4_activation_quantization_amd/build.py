@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librmsq.so")
 SOURCES = ["rmsq_api.cpp", "rmsq_fp8.hip", "rmsq_fp8_f16.hip", "rmsq_fp8_f32.hip", "rmsq_fp8_ragged.hip",
            "rmsq_fp8_sum.hip", "rmsq_fp8_sum_f16.hip", "rmsq_fp8_sum_f32.hip",
-           "rmsq_fp8_ragged_f16.hip", "rmsq_fp8_ragged_f32.hip", "rmsq_fp4.hip",
+           "rmsq_fp8_ragged_f16.hip", "rmsq_fp8_ragged_f32.hip", "rmsq_fp4.hip", "rmsq_fp4_wave.hip", "rmsq_fp4_wave_f16.hip",
            "rmsq_fp4_f16.hip", "rmsq_fp4_f32.hip", "rmsq_wide.hip", "rmsq_wide_f16.hip", "rmsq_wide_f32.hip",
            "rmsq_convert.hip", "rmsq_stream.hip"]
 ARCH = os.environ.get("RMSQ_OFFLOAD_ARCH", "gfx950")

@@ -338,6 +338,25 @@ bool choose_shape(int64_t rows, int nvec, int path, int esz, Shape* s) {
             // 8 x 2 on MI355X, 3.0 us as 16 x 1 and 2.8 us as 4 x 4)
             vpt = nvec <= 64 ? 1 : (nvec <= 16 * 64 * 2 ? 2 : 4);
             waves = (int)std::min<int64_t>(16, ceil_div(nvec, 64 * vpt));
+        } else if (path == kPathFp4 && esz == 2 && nvec > 256 && nvec <= 64 * 12) {
+            // FP4 of 16-bit rows of 257..768 vectors: one wavefront per row
+            // with every load of the row in flight (the wave-per-row kernel).
+            // A/B on MI355X against the block kernel's 4 x 4 / 4 x 2 shapes:
+            // 16384 x 5120 bf16 0.93x the time, 8192 x 4096 0.97x; at 14 and
+            // 16 vectors per lane it was slower (16384 x 7168 1.05x,
+            // 8192 x 8192 1.08x: 100-112 VGPRs, four waves per SIMD)
+            waves = 1;
+            for (int v : kWaveRowVpt) {
+                if ((int64_t)v * 64 >= nvec) {
+                    vpt = v;
+                    break;
+                }
+            }
+            s->waves = waves;
+            s->vpt = vpt;
+            s->rpb = 4;
+            s->grid = g_tune_blocks.load(std::memory_order_relaxed);
+            return true;
         } else {
             // large batches: blocks of a multiple of 4 wavefronts, so the 4
             // SIMDs of a CU get equal work (odd counts measured 20-35% slower

@@ -23,7 +23,8 @@
 // spans LPB = BLOCK / EPV adjacent lanes (2, 4 or 8); they combine their
 // partial amax through DPP lane swaps, all compute the block scale, the
 // first lane stores the scale byte and each lane stores its own EPV / 2
-// bytes of codes.
+// bytes of codes (16-byte stores after an exchange through LDS within the
+// wave measured 1-6% slower on MI355X).
 // The grid strides over rows, so gamma + weight_offset is unpacked into
 // registers once per block, and the row loop is software-pipelined.
 #pragma once
@@ -34,6 +35,89 @@
 #include "rmsq_internal.h"
 
 namespace rmsq {
+
+// One 16-byte vector of a row quantized to E2M1 with its block's scale:
+// t = s * g' (g' = gamma + weight_offset, fp32), optionally rounded once to
+// the input type (the page's 16-bit x * w), the block's amax from the
+// LPB = BLOCK / EPV lanes holding it (DPP swaps; every lane of the wave takes
+// part, vectors past the row being zero), the scale code, the element factor,
+// and the codes (EPV / 2 bytes at vector v of the row) and, from the block's
+// first lane, its scale byte at sbyte (the caller's place for it: row-major,
+// or the 128 x 4 tile slot, fp4_scale_step).
+//   E4M3: scale = E4M3(min(gs * amax_t * rstd / 6, 448)) with c_scale =
+//   gs * rstd / 6; factor c_elem / decoded scale (c_elem = gs * rstd), 0 for
+//   a zero code.  UE8M0 (gs = 1): code from amax_t * rstd / 6, factor
+//   rstd * 2^(127 - code).
+template <typename InT, int BLOCK, bool UE8M0>
+__device__ __forceinline__ uint32_t fp4_codes_vector(const uint4& sv, const float (&g)[Vec<InT>::EPV], bool live, int v,
+                                                     float c_scale, float c_elem, bool round_prod, uint8_t* sbyte) {
+    using V = Vec<InT>;
+    constexpr int EPV = V::EPV;
+    constexpr int LPB = BLOCK / EPV;  // lanes (vectors) per block: 2, 4 or 8
+    float t[EPV];  // s * g'
+    V::unpack(sv, t);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) t[e] *= g[e];
+    // the page's numerics (optional, uniform): its kernel forms x * w as a
+    // 16-bit product, i.e. s * g' rounded once
+    if (round_prod) V::unpack(V::pack(t), t);
+    const float amax = block_max_nonneg<LPB>(abs_max<EPV>(0.0f, t));
+    uint32_t code;
+    float kq;
+    if constexpr (UE8M0) {
+        code = ue8m0_code(amax * c_scale);
+        kq = ue8m0_factor(c_elem, code);
+    } else {
+        code = e4m3fn_scale_code(amax * c_scale);
+        const float d = e4m3fn_decode(code);
+        kq = d > 0.0f ? c_elem * __builtin_amdgcn_rcpf(d) : 0.0f;
+    }
+    float q[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) q[e] = t[e] * kq;
+    if (live && (v & (LPB - 1)) == 0) *sbyte = (uint8_t)code;
+    return EPV == 8 ? e2m1_x8(q) : e2m1_x4(q);  // 4 bytes (2 for fp32 inputs: the low half)
+}
+
+// The codes of vector v (the word fp4_codes_vector returned) stored on their
+// own: 4 bytes per lane (2 for fp32 inputs).
+template <int EPV>
+__device__ __forceinline__ void fp4_store_codes(uint8_t* orow, int v, uint32_t cw) {
+    if constexpr (EPV == 8)
+        store_stream(orow, v, cw);
+    else
+        store_stream(orow, v, (uint16_t)cw);
+}
+
+// Swizzled scales: a 128-byte line of the scale buffer holds the scales of 32
+// rows (same row / 128, same (row % 32) / 8).  Blocks go to the 8 XCDs round
+// robin and each XCD has its own L2, so in row order a line would be
+// assembled from pieces written back by up to 8 L2s.  Logical row index i is
+// therefore mapped to a row so that the indices with i % 8 == x (those the
+// blocks of XCD x take when the grid is a multiple of 8) are whole 32-row
+// groups; indices from perm_rows on (past the last multiple of 256) are not
+// remapped.  The map permutes each run of 256 rows.
+__device__ __forceinline__ int64_t fp4_row_of(int64_t i, int64_t perm_rows) {
+    if (i >= perm_rows) return i;
+    const int64_t grp = (i >> 8) * 8 + (i & 7);  // 32-row group
+    const int m = (int)((i >> 3) & 31);          // member of the group
+    return (grp >> 2) * 128 + (m >> 3) * 32 + (grp & 3) * 8 + (m & 7);
+}
+
+// The scale byte of block j of a row: row-major, srow[j]; swizzled,
+// srow[(j / 4) * 512 + j % 4].  A lane holds the vectors v0 + k * T (T a
+// multiple of 64), whose blocks j0 + k * (T / LPB) advance by a multiple of 4,
+// so its scale bytes are sbase + k * step with fp4_scale_base and this step.
+__device__ __forceinline__ int fp4_scale_base(int j0, bool swz) { return swz ? (j0 >> 2) * 512 + (j0 & 3) : j0; }
+__device__ __forceinline__ int fp4_scale_step(int T, int lpb, bool swz) { return swz ? 128 * (T / lpb) : T / lpb; }
+
+// This row's first scale byte: row-major, or the row's place in its 128 x 4
+// tiles ((row/128) * K * 512 + (row%32) * 16 + ((row%128)/32) * 4).
+__device__ __forceinline__ uint8_t* fp4_scale_row(const FusedArgs& a, int64_t row, int nblk) {
+    return static_cast<uint8_t*>(a.scales) +
+           (a.sf_swizzled ? (row >> 7) * ((int64_t)a.sf_k_tiles * 512) + (row & 31) * 16 + ((row & 127) >> 5) * 4
+                          : row * (int64_t)nblk);
+}
 
 template <typename InT, bool RESID, int VPT, bool EXACT, bool ONE_ROW, int DEPTH, int BLOCK, bool UE8M0>
 __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
@@ -55,11 +139,9 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
     const int nblk = a.hidden / BLOCK;
     const bool swz = a.sf_swizzled != 0;
     const bool round_prod = a.round_product != 0;
-    const int64_t m_tile_bytes = (int64_t)a.sf_k_tiles * 512;
     auto live = [&](int k) { return EXACT || lt + k * T < nvec; };
 
     __shared__ double red_sum[2][16];
-
     // E4M3 scales only (the API passes no global scale with UE8M0 scales)
     const double gs = a.global_scale ? (double)*a.global_scale : 1.0;
 
@@ -91,21 +173,10 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
 #pragma unroll
         for (int k = 0; k < RV; ++k) rb[b][k] = make_uint4(0, 0, 0, 0);
     }
-    // Swizzled scales: a 128-byte line of the scale buffer holds the scales
-    // of 32 rows (same row / 128, same (row % 32) / 8).  Blocks go to the 8
-    // XCDs round robin and each XCD has its own L2, so in row order a line
-    // would be assembled from pieces written back by up to 8 L2s.  Logical
-    // row index i is therefore mapped to a row so that the indices with
-    // i % 8 == x (those blocks of XCD x take when the grid is a multiple of
-    // 8) are whole 32-row groups; indices past the last multiple of 256 are
-    // not remapped.  The map permutes each run of 256 rows.
+    // swizzled scales: rows remapped so that each XCD writes whole 128-byte
+    // scale lines (fp4_row_of)
     const int64_t perm_rows = swz ? (a.rows & ~(int64_t)255) : 0;
-    auto row_of = [&](int64_t i) -> int64_t {
-        if (i >= perm_rows) return i;
-        const int64_t grp = (i >> 8) * 8 + (i & 7);  // 32-row group
-        const int m = (int)((i >> 3) & 31);          // member of the group
-        return (grp >> 2) * 128 + (m >> 3) * 32 + (grp & 3) * 8 + (m & 7);
-    };
+    auto row_of = [&](int64_t i) -> int64_t { return fp4_row_of(i, perm_rows); };
 
     auto fetch = [&](uint4 (&xn)[VPT], uint4 (&rn)[RV], int64_t i) {
         if (i < a.rows) {
@@ -174,47 +245,13 @@ __global__ void __launch_bounds__(1024) fp4_kernel(const FusedArgs a) {
             const float c_elem = (float)(gs * rstd);
 
             uint8_t* orow = static_cast<uint8_t*>(a.out) + row * a.out_stride;
-            // this row's scale bytes: row-major, or the row's place in its
-            // 128 x 4 tiles ((row/128) * K * 512 + (row%32) * 16 + ((row%128)/32) * 4)
-            uint8_t* srow = static_cast<uint8_t*>(a.scales) +
-                            (swz ? (row >> 7) * m_tile_bytes + (row & 31) * 16 + ((row & 127) >> 5) * 4
-                                 : row * (int64_t)nblk);
+            uint8_t* sbase = fp4_scale_row(a, row, nblk) + fp4_scale_base(lt / LPB, swz);
+            const int sstep = fp4_scale_step(T, LPB, swz);
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
-                const int v = lt + k * T;
-                float t[EPV];  // s * g'
-                V::unpack(sv[k], t);
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) t[e] *= g[k][e];
-                // the page's numerics (optional, uniform): its kernel forms
-                // x * w as a 16-bit product, i.e. s * g' rounded once
-                if (round_prod) V::unpack(V::pack(t), t);
-                // all lanes take part in the swaps (vectors past the row are
-                // zero, and a block's lanes are all live or all past the row)
-                const float amax = block_max_nonneg<LPB>(abs_max<EPV>(0.0f, t));
-                uint32_t code;
-                float kq;
-                if constexpr (UE8M0) {
-                    code = ue8m0_code(amax * c_scale);
-                    kq = ue8m0_factor(c_elem, code);
-                } else {
-                    code = e4m3fn_scale_code(amax * c_scale);
-                    const float d = e4m3fn_decode(code);
-                    kq = d > 0.0f ? c_elem * __builtin_amdgcn_rcpf(d) : 0.0f;
-                }
-                if (live(k)) {
-                    float q[EPV];
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) q[e] = t[e] * kq;
-                    if constexpr (EPV == 8)
-                        store_stream(orow, v, e2m1_x8(q));               // 4 bytes per lane
-                    else
-                        store_stream(orow, v, (uint16_t)e2m1_x4(q));     // 2 bytes per lane
-                    if ((v & (LPB - 1)) == 0) {
-                        const int j = v / LPB;  // block index in the row
-                        srow[swz ? (j >> 2) * 512 + (j & 3) : j] = (uint8_t)code;
-                    }
-                }
+                const uint32_t cw = fp4_codes_vector<InT, BLOCK, UE8M0>(sv[k], g[k], live(k), lt + k * T, c_scale,
+                                                                        c_elem, round_prod, sbase + k * sstep);
+                if (live(k)) fp4_store_codes<EPV>(orow, lt + k * T, cw);
             }
         }
     };

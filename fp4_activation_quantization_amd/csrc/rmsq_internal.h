@@ -56,14 +56,20 @@ struct Fp4Format {
 
 // Launch shape: one row is handled by `waves` wavefronts (64 lanes each, any
 // count 1..16), each lane holding `vpt` 16-byte vectors of the row (on the
-// FP8 element path: `vpt` single elements, one of kElemPerLane); a block
-// holds `rpb` rows (waves * rpb wavefronts); `grid` blocks (0 = default).
+// FP8 element path: `vpt` single elements, one of kElemPerLane; on the FP4
+// path, vpt above 4 selects the wave-per-row kernel with one wavefront per
+// row and vpt one of kWaveRowVpt); a block holds `rpb` rows (waves * rpb
+// wavefronts); `grid` blocks (0 = default).
 struct Shape {
     int waves;
     int vpt;
     int rpb;
     int grid;
 };
+
+// Vectors per lane the wave-per-row FP4 kernel is compiled for (rows of 257
+// to 768 vectors of 16-bit elements, without a residual, large batches).
+constexpr int kWaveRowVpt[] = {8, 12};
 
 // Which fused path a shape is chosen for (the rmsq_query_shape `path` values).
 enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPathFp8Residual = 5, kPathFp8Sum = 6 };

@@ -426,6 +426,12 @@ def test_automatic_shape_fills_simds(fp4, residual):
                 nvec = hidden // epv
                 s = rq.query_shape(4096, hidden, dt, fp4, residual)
                 w, v, r = s["waves_per_row"], s["vectors_per_lane"], s["rows_per_block"]
+                if fp4 and not residual and dt != rq.torch.float32 and 256 < nvec <= 768:
+                    # the wave-per-row FP4 kernel: one wavefront per row, 4 per
+                    # block, the fewest compiled vectors per lane that hold it
+                    assert (w, r) == (1, 4), (hidden, s)
+                    assert v == min(vv for vv in (8, 12) if vv * 64 >= nvec), (hidden, s)
+                    continue
                 assert (w * r) % 4 == 0 and w * r <= 16, (hidden, s)
                 assert r == (1 if w >= 4 else 4 // w), (hidden, s)
                 idle = w * 64 * v - nvec
@@ -448,9 +454,11 @@ def test_automatic_shape_fills_simds(fp4, residual):
         assert shape(q(16384, 8192, rq.torch.bfloat16, res=True)) == (8, 2)
         assert shape(q(16384, 16384, rq.torch.bfloat16)) == (8, 4)
         assert shape(q(16384, 8192, rq.torch.float32, res=True)) == (8, 4)  # not 16 x 2: one such block per CU
-        assert shape(q(16384, 7168, rq.torch.bfloat16, True)) == (4, 4)
+        assert shape(q(16384, 7168, rq.torch.bfloat16, True)) == (4, 4)  # the block kernel
+        assert shape(q(16384, 6144, rq.torch.bfloat16, True)) == (1, 12)  # the wave-per-row kernel
         assert shape(q(16384, 7168, rq.torch.bfloat16, True, True)) == (16, 1)
-        assert shape(q(16384, 5120, rq.torch.bfloat16, True)) == (4, 4)
+        assert shape(q(16384, 5120, rq.torch.bfloat16, True)) == (1, 12)
+        assert shape(q(256, 7168, rq.torch.bfloat16, True)) == (7, 2)  # small batches: the block kernel, latency shape
         assert shape(q(16384, 16384, rq.torch.bfloat16, True, True)) == (16, 2)
     finally:
         rq.set_tuning(1, 1, 0)

@@ -144,6 +144,24 @@ def test_automatic_large_batch_shapes(dt, hidden):
             check_fp8(w, inp, label=f"{op} {dt} {hidden} {s}")
 
 
+@pytest.mark.parametrize("dt,hidden", [("bf16", 4096), ("f16", 2560), ("bf16", 5120), ("f16", 6144)])
+def test_wave_per_row_fp4_formats(dt, hidden):
+    """The one-wavefront-per-row FP4 kernel (16-bit rows of 257..768
+    vectors, large batches: 8 or 12 vectors per lane, whole or ragged) in
+    every scale format and block size, on 1000 rows: the swizzled layout's
+    row map covers 768 rows and leaves a tail of 232."""
+    rows = 1000
+    s = rq.query_shape(rows, hidden, workloads.TORCH_DTYPES[dt], True, False)
+    assert s["waves_per_row"] == 1 and s["rows_per_block"] == 4, s
+    inp = _rand_inputs(rows, hidden, dt, seed=hidden + 7)
+    for kw in ({}, {"fp4_block": 32}, {"fp4_scale": "ue8m0", "fp4_block": 32}, {"fp4_swizzled": True},
+               {"fp4_round_product": True, "weight_offset": 1.0}):
+        w = _wl("rmsnorm_fp4", rows, hidden, dt, **kw)
+        say(f"[fp4 wave row] {dt} {rows}x{hidden} {kw} shape {s}")
+        gs = None if w.fp4_scale == "ue8m0" else fp4_gs_for(inp, w)
+        check_fp4(w, inp, gs, label=f"fp4 wave row {dt} {hidden} {kw}")
+
+
 @pytest.mark.parametrize("dt,hidden", [("bf16", 32768), ("f16", 32768), ("f32", 16384)])
 def test_largest_hidden(dt, hidden):
     w = _wl("residual_rmsnorm_fp8", 5, hidden, dt)
