@@ -55,9 +55,11 @@ SC_T = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 def kernel_source_hash() -> str:
     """Hash of every source the library is built from (csrc/ and the public
-    header): counter summaries taken on other sources are stale."""
+    headers): counter summaries taken on other sources are stale."""
     h = hashlib.sha256()
-    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)) + [os.path.join(ROOT, "include", "rmsq.h")]
+    inc = os.path.join(ROOT, "include")
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)) + sorted(os.path.join(inc, f)
+                                                                             for f in os.listdir(inc))
     for f in files:
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
@@ -276,41 +278,130 @@ def time_graph(case: Case, calls: int, replays: int) -> dict:
             "graph_replays": replays}
 
 
-class _Probe:
-    """rmsq_stream_probe moving a workload's read and write bytes, in the
-    shape time_case / time_windows expect (rotated buffer sets)."""
+def probe_layout(w: workloads.Workload) -> tuple[int, int, list[int]]:
+    """The fused kernel's row tensors: (inputs per row, bytes of each input
+    row, bytes of each output row).  A per-row scale narrower than 4 bytes
+    counts as 4 (the probe's smallest store)."""
+    esz = {"bf16": 2, "f16": 2, "f32": 4}[w.in_dtype]
+    row = w.hidden * esz
+    nin = (w.ninputs if w.ninputs > 1 else 1) + (1 if w.residual else 0)
+    outs = [row] if w.residual else []
+    if w.fp4:
+        outs += [w.hidden // 2, w.hidden // w.fp4_block]
+    else:
+        outs += [w.hidden, max(4, {"f32": 4, "bf16": 2, "f16": 2}[w.scales_dtype])]
+    return nin, row, outs
 
-    def __init__(self, w: workloads.Workload, copies: int):
-        rb, wb = algorithmic_split(w)
-        self.rb, self.wb = -(-rb // 16) * 16, -(-wb // 16) * 16
-        self.w = w
-        L = rq.lib()
-        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        self.bufs = []
-        for _ in range(copies):
-            src = torch.ones(self.rb // 4, dtype=torch.float32, device="cuda:0")
-            dst = torch.empty(self.wb // 4, dtype=torch.float32, device="cuda:0")
-            self.bufs.append((src, dst, (ctypes.c_void_p(src.data_ptr()), self.rb, ctypes.c_void_p(dst.data_ptr()),
-                                         self.wb, stream)))
-        self.fn = L.rmsq_stream_probe
+
+class _ProbeCase:
+    """A streaming reference launch (librmsq_probe) over a workload's bytes,
+    in the shape time_case / time_windows expect (rotated buffer sets)."""
+
+    def __init__(self, w: workloads.Workload, copies: int, cfg: dict):
+        from fp4_activation_quantization_amd import probe
+
+        self.w, self.cfg, self.keep, self.launches = w, cfg, [], []
+        dev = "cuda:0"
+        if cfg["kind"] == "rows":
+            nin, row, outs = probe_layout(w)
+            self.nbytes = w.rows * (nin * row + sum(outs))
+            for _ in range(copies):
+                ins = [torch.ones(w.rows * row, dtype=torch.uint8, device=dev) for _ in range(nin)]
+                ous = [torch.empty(w.rows * b, dtype=torch.uint8, device=dev) for b in outs]
+                self.keep += ins + ous
+                self.launches.append(probe.Rows(w.rows, ins, row, ous, outs, block=cfg["block"], vpt=cfg["vpt"],
+                                                grid=cfg.get("grid", 0)))
+        else:
+            rb, wb = (-(-b // 16) * 16 for b in algorithmic_split(w))
+            self.nbytes = rb + wb
+            for _ in range(copies):
+                src = torch.ones(rb, dtype=torch.uint8, device=dev)
+                dst = torch.empty(wb, dtype=torch.uint8, device=dev)
+                self.keep += [src, dst]
+                self.launches.append(probe.Chunks(src, rb, dst, wb, rv=cfg["rv"], wv=cfg["wv"], block=cfg["block"],
+                                                  loads_in_flight=cfg["nl"], blocks_per_cu=cfg.get("per_cu", 0),
+                                                  interleave=cfg.get("interleave", False)))
 
     def step(self, i: int) -> None:
-        rc = self.fn(*self.bufs[i % len(self.bufs)][2])
-        if rc != 0:
-            raise rq.RmsqError("rmsq_stream_probe", rc, rq.lib().rmsq_last_hip_error())
+        self.launches[i % len(self.launches)]()
 
 
-def stream_ceiling(w: workloads.Workload, copies: int, settle_ms: float, window_ms: float, windows: int) -> float:
-    """GB/s of the plain streaming reference kernel (rmsq_stream_probe) moving
-    this workload's read and write bytes, timed like the workloads (settled,
-    median window) with the same number of rotated buffer sets."""
-    probe = _Probe(w, copies)
-    settle(probe, settle_ms)
-    us = time_windows(probe, window_ms, windows)["launch_us"]
-    gbps = (probe.rb + probe.wb) / (us * 1e-6) / 1e9
-    del probe
-    torch.cuda.empty_cache()
-    return gbps
+def _unit_ratio(rb: int, wb: int, limit: int = 64) -> tuple[int, int]:
+    """Smallest rv, wv (each <= limit) whose ratio is within 2% of rb : wb."""
+    want = rb / wb
+    for tot in range(2, 2 * limit + 1):
+        for r in range(1, tot):
+            wv = tot - r
+            if r <= limit and wv <= limit and abs(r / wv - want) <= 0.02 * want:
+                return r, wv
+    return (limit, 1) if want > 1 else (1, limit)
+
+
+def probe_candidates(w: workloads.Workload, full: bool = False) -> list[dict]:
+    """Streaming reference configurations for a workload: the row layout of
+    the fused kernel (one block per row, every load of the row in flight) at
+    block sizes whose lanes hold the row, and the two-stream chunk form at the
+    byte ratio; `full` widens the set to the sweep (loads in flight,
+    persistent grids, interleaved writes)."""
+    nin, row, outs = probe_layout(w)
+    nvec = row // 16
+    cands = []
+    for block in ((64, 128, 256, 512, 1024) if full else (256, 512, 1024)):
+        for vpt in (1, 2, 4, 8):
+            if block * vpt >= nvec:
+                break
+        else:
+            continue
+        if nin * vpt > 16 or row % 16 or any(b % 16 and (b % 4 or b > 4 * block) for b in outs) or \
+                any(b % 16 == 0 and b > row for b in outs):
+            continue
+        for grid in ((0, 256, 1024, 2048) if full else (0,)):
+            cands.append({"kind": "rows", "block": block, "vpt": vpt, "grid": grid})
+    rb, wb = algorithmic_split(w)
+    base = _unit_ratio(rb, wb)
+    # the default set: the configurations that won the full sweep on the
+    # named workloads (MI355X)
+    ratios = [base] + ([(2 * base[0], 2 * base[1])] if 2 * max(base) <= 64 else [])
+    for rv, wv in ratios:
+        for block in ((256, 512, 1024) if full else (256, 1024)):
+            for nl in ((4, 8, 16) if full else (8, 16)):
+                for per_cu in ((0, 4) if full else (0,)):
+                    for inter in (False, True):
+                        cands.append({"kind": "chunks", "rv": rv, "wv": wv, "block": block, "nl": nl,
+                                      "per_cu": per_cu, "interleave": inter})
+    return cands
+
+
+def stream_ceiling(w: workloads.Workload, copies: int, settle_ms: float, window_ms: float, windows: int,
+                   full: bool = False, log=None, retime: tuple | None = None) -> dict:
+    """The streaming ceiling for this workload's traffic: every candidate
+    streaming reference configuration (probe_candidates) timed like the
+    workloads (settled, median window, the same number of rotated buffer
+    sets); the fastest, in GB/s of the bytes it moves, with its
+    configuration, and all of them.  retime = (settle_ms, window_ms,
+    windows) times the fastest once more that way."""
+    results = []
+    for cfg in probe_candidates(w, full):
+        c = _ProbeCase(w, copies, cfg)
+        settle(c, settle_ms)
+        us = time_windows(c, window_ms, windows)["launch_us"]
+        results.append({"gbps": round(c.nbytes / (us * 1e-6) / 1e9, 1), "launch_us": round(us, 3), **cfg})
+        if log:
+            log(f"  {results[-1]}")
+        del c
+        torch.cuda.empty_cache()
+    results.sort(key=lambda r: -r["gbps"])
+    best = dict(results[0])
+    if retime:
+        # the fastest configuration again under the fused kernels' own
+        # protocol (their settling and windows)
+        c = _ProbeCase(w, copies, {k: v for k, v in best.items() if k not in ("gbps", "launch_us")})
+        settle(c, retime[0])
+        us = time_windows(c, retime[1], retime[2])["launch_us"]
+        best.update(gbps=round(c.nbytes / (us * 1e-6) / 1e9, 1), launch_us=round(us, 3))
+        del c
+        torch.cuda.empty_cache()
+    return {"gbps": best["gbps"], "config": best, "all": results}
 
 
 def fp4_global_scale(name: str) -> float:
@@ -455,7 +546,13 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=1.0, help="minimum oracle time per workload")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of each workload the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming reference kernel")
+    ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming reference kernels")
+    ap.add_argument("--probe-window-ms", type=float, default=30.0, help="GPU time per timing window of each "
+                    "streaming reference configuration")
+    ap.add_argument("--probe-windows", type=int, default=3, help="timing windows per streaming reference "
+                    "configuration")
+    ap.add_argument("--probe-sweep", action="store_true", help="only sweep the streaming reference kernels over "
+                    "their full configuration set for the selected workloads, print a table and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (for counter scaling) and exit")
     args = ap.parse_args()
@@ -484,6 +581,18 @@ def main() -> int:
     # has used yet (later runs of the same kernel measured up to 2% slower)
     names = [lead] + [n for n in names if n != lead]
 
+    if args.probe_sweep:
+        for name in names:
+            w = workload_of(name)
+            sc = stream_ceiling(w, copies_for(w), 20.0, args.probe_window_ms, args.probe_windows, full=True,
+                                log=lambda m: print(m, file=sys.stderr, flush=True))
+            print(f"## {name} ({len(sc['all'])} configurations, {copies_for(w)} buffer set(s))", flush=True)
+            print("| GB/s | us | kind | config |\n|---|---|---|---|", flush=True)
+            for r in sc["all"]:
+                cfg = {k: v for k, v in r.items() if k not in ("gbps", "launch_us", "kind")}
+                print(f"| {r['gbps']:.0f} | {r['launch_us']:.2f} | {r['kind']} | {cfg} |", flush=True)
+        return 0
+
     results = {}
     for name in names:
         w = workload_of(name)
@@ -508,9 +617,12 @@ def main() -> int:
         del case
         torch.cuda.empty_cache()
         # the achievable ceiling for this traffic mix (bandwidth-sized workloads only)
-        res["stream_gbps"] = (stream_ceiling(w, k, args.settle_ms, args.window_ms, args.windows)
-                              if algorithmic_bytes(w) >= STREAM_MIN_BYTES and not args.no_stream_ceiling else None)
-        ceil = f", streaming reference {res['stream_gbps']:.0f} GB/s" if res["stream_gbps"] else ""
+        sc = (stream_ceiling(w, k, 20.0, args.probe_window_ms, args.probe_windows,
+                             retime=(args.settle_ms, args.window_ms, args.windows))
+              if algorithmic_bytes(w) >= STREAM_MIN_BYTES and not args.no_stream_ceiling else None)
+        res["stream_gbps"] = sc["gbps"] if sc else None
+        res["stream_config"] = {k_: v for k_, v in sc["config"].items() if k_ != "gbps"} if sc else None
+        ceil = f", streaming ceiling {res['stream_gbps']:.0f} GB/s ({res['stream_config']})" if sc else ""
         if "graph_us" in res:
             ceil += f", {res['graph_us']:.2f} us per call in a graph (p50 over replays {res['graph_us_p50']:.2f})"
         cpu = f", oracle {res['cpu']['rows_per_s']:.0f} rows/s" if res["cpu"] else ""
@@ -553,6 +665,7 @@ def main() -> int:
                           "graph_us": round(r["graph_us"], 3) if "graph_us" in r else None,
                           "graph_us_p50": round(r["graph_us_p50"], 3) if "graph_us_p50" in r else None,
                           "stream_reference_gbps": round(r["stream_gbps"], 1) if r["stream_gbps"] else None,
+                          "stream_reference_config": r["stream_config"],
                           "frac_of_stream_reference": round(r["gbps"] / r["stream_gbps"], 4)
                           if r["stream_gbps"] else None}
                       for n, r in results.items()},

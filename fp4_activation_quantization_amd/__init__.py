@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
     P, I64, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     L.rmsnorm_fp8.argtypes = [I64, I64, I, P, P, F, F, F, I, P, I, P, P]
     L.residual_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, P, F, F, F, I, P, I, P, P]
+    L.gated_rmsnorm_fp8.argtypes = [I64, I64, I, P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4.argtypes = [I64, I64, I, P, P, F, F, P, P, P, P]
     L.allreduce_residual_rmsnorm_fp8.argtypes = [I64, I64, I, I, ctypes.POINTER(P), P, P, P, F, F, F, I, P, I, P, P]
     L.rmsnorm_fp4quant.argtypes = [I64, I64, I, P, P, F, F, P, I, I, I, I, P, P, P]
@@ -74,14 +75,13 @@ def lib() -> ctypes.CDLL:
     L.rmsq_fp4_scale_bytes.argtypes = [I64, I64, I, I]
     L.rmsq_fp4_scale_bytes.restype = I64
     L.rmsq_convert.argtypes = [I, P, P, I64, P]
-    L.rmsq_stream_probe.argtypes = [P, I64, P, I64, P]
     L.rmsq_set_tuning.argtypes = [I, I, I]
     L.rmsq_query_shape.argtypes = [I64, I64, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)]
     L.rmsq_status_string.argtypes = [I]
     L.rmsq_status_string.restype = ctypes.c_char_p
-    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "allreduce_residual_rmsnorm_fp8", "rmsnorm_fp4",
+    for fn in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "allreduce_residual_rmsnorm_fp8", "gated_rmsnorm_fp8",
+               "rmsnorm_fp4",
                "rmsnorm_fp4quant", "residual_rmsnorm_fp4quant", "rmsnorm_fp8_strided", "rmsnorm_fp4quant_strided", "rmsq_convert",
-               "rmsq_stream_probe",
                "rmsq_set_tuning",
                "rmsq_query_shape", "rmsq_abi_version", "rmsq_last_hip_error"):
         getattr(L, fn).restype = I
@@ -173,6 +173,30 @@ def rmsnorm_fp8(x, gamma, eps=1e-6, weight_offset=0.0, scale_ub=float("inf"), ou
         _check("rmsnorm_fp8", lib().rmsnorm_fp8(rows, hidden, _DT[x.dtype], _ptr(x), _ptr(gamma), eps, weight_offset,
                                                 scale_ub, _FMT[out_fp8], _ptr(_u8(out)), _DT[scales.dtype],
                                                 _ptr(scales), _stream(x, stream)))
+    return out, scales
+
+
+def gated_rmsnorm_fp8(a, b, gamma, eps=1e-6, weight_offset=0.0, scale_ub=float("inf"), out_fp8="e4m3fn",
+                      out=None, scales=None, scales_dtype=torch.float32, stream=None):
+    """RMSNorm + per-row dynamic FP8 of x = a * b (rounded to a.dtype), formed
+    as the kernel loads a and b (C: gated_rmsnorm_fp8).  Returns (codes, scales)."""
+    rows, hidden = _rows_hidden(a)
+    if b.dtype != a.dtype or b.shape != a.shape:
+        raise ValueError("b must match a in dtype and shape")
+    if out is None:
+        out = torch.empty(a.shape, dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty(a.shape[:-1], dtype=scales_dtype, device=a.device)
+    ctx = _device(a)
+    _check_gamma(gamma, a, hidden)
+    _buf("b", b, a.device, rows * hidden, (a.dtype,))
+    _buf("out", out, a.device, rows * hidden, _BYTE)
+    _buf("scales", scales, a.device, rows, tuple(_DT))
+    with ctx:
+        _check("gated_rmsnorm_fp8",
+               lib().gated_rmsnorm_fp8(rows, hidden, _DT[a.dtype], _ptr(a), _ptr(b), _ptr(gamma), eps, weight_offset,
+                                       scale_ub, _FMT[out_fp8], _ptr(_u8(out)), _DT[scales.dtype], _ptr(scales),
+                                       _stream(a, stream)))
     return out, scales
 
 
@@ -480,18 +504,6 @@ def convert(kind: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> tor
     with ctx:
         _check("rmsq_convert", lib().rmsq_convert(kind, _ptr(src), _ptr(dst), n, _stream(src, stream)))
     return dst
-
-
-def stream_probe(src: torch.Tensor, read_bytes: int, dst: torch.Tensor, write_bytes: int, stream=None) -> None:
-    """Measurement reference kernel (C: rmsq_stream_probe): reads read_bytes of
-    src and writes write_bytes of dst, in that proportion, computing nothing."""
-    if src.numel() * src.element_size() < read_bytes or dst.numel() * dst.element_size() < write_bytes:
-        raise ValueError("stream_probe: buffer smaller than the byte count")
-    ctx = _device(src)
-    _gpu("dst", dst, src.device)
-    with ctx:
-        _check("rmsq_stream_probe", lib().rmsq_stream_probe(_ptr(src), read_bytes, _ptr(dst), write_bytes,
-                                                            _stream(src, stream)))
 
 
 def set_tuning(waves_per_row: int = 0, vectors_per_lane: int = 0, grid_blocks: int = 0) -> None:

@@ -25,7 +25,6 @@ std::atomic<int> g_tune_blocks{0};
 
 // Largest row the register-resident kernels hold: 16 waves x 64 lanes x 4
 // vectors of 16 bytes.
-constexpr int kMaxVec = 16 * 64 * 4;
 
 bool valid_dtype(int dt) { return dt == RMSQ_F32 || dt == RMSQ_F16 || dt == RMSQ_BF16; }
 int64_t elem_size(int dt) { return dt == RMSQ_F32 ? 4 : 2; }
@@ -531,6 +530,48 @@ int allreduce_residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, i
                       weight_offset, scale_ub, out_fp8, out, scales_dtype, scales, stream);
 }
 
+int gated_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, const void* a, const void* b, const void* gamma,
+                      float eps, float weight_offset, float scale_ub, int out_fp8, void* out, int scales_dtype,
+                      void* scales, hipStream_t stream) {
+    if (!valid_dtype(in_dtype) || !valid_dtype(scales_dtype)) return RMSQ_ERR_DTYPE;
+    if (out_fp8 != RMSQ_E4M3FN && out_fp8 != RMSQ_E4M3FNUZ) return RMSQ_ERR_DTYPE;
+    const int64_t esz = elem_size(in_dtype), epv = elems_per_vec(in_dtype);
+    if (rows < 0 || hidden <= 0 || hidden % epv != 0 || !size_ok(rows, hidden, esz)) return RMSQ_ERR_SHAPE;
+    if (int rc = check_scalars(eps, weight_offset, scale_ub, true)) return rc;
+    const int64_t nvec = hidden / epv;
+    if (nvec > kMaxVec) return RMSQ_ERR_UNSUPPORTED;
+    if (rows == 0) return RMSQ_OK;
+    if (!a || !b || !gamma || !out || !scales) return RMSQ_ERR_NULL;
+    const int64_t ssz = elem_size(scales_dtype);
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(gamma, 16) || !aligned(out, 16) ||
+        !aligned(scales, (uintptr_t)ssz))
+        return RMSQ_ERR_ALIGN;
+    const int64_t rb = rows * hidden * esz;
+    const Span sa(a, rb), sb(b, rb), sg(gamma, hidden * esz), so(out, rows * hidden), ss(scales, rows * ssz);
+    // the outputs overlap no input and not each other; a and b may share
+    // memory (they are only read)
+    for (const Span& o : {so, ss})
+        if (overlap(o, sa) || overlap(o, sb) || overlap(o, sg)) return RMSQ_ERR_ALIAS;
+    if (overlap(so, ss)) return RMSQ_ERR_ALIAS;
+    Shape shape;
+    if (!choose_shape(rows, (int)nvec, kPathFp8, (int)esz, &shape)) return RMSQ_ERR_UNSUPPORTED;
+    FusedArgs fa{};
+    fa.gamma = gamma;
+    fa.out = out;
+    fa.scales = scales;
+    fa.rows = rows;
+    fa.hidden = (int32_t)hidden;
+    fa.inv_hidden = 1.0 / (double)hidden;
+    fa.nvec = (int32_t)nvec;
+    fa.eps = eps;
+    fa.weight_offset = weight_offset;
+    fa.scale_ub = scale_ub;
+    fa.scales_dtype = scales_dtype;
+    fa.x_stride = hidden * esz;
+    fa.out_stride = hidden;
+    return launched(launch_fp8_gated(fa, a, b, in_dtype, out_fp8 == RMSQ_E4M3FNUZ, shape, stream));
+}
+
 int rmsnorm_fp8_strided(int64_t rows, int64_t hidden, int in_dtype, const void* x, int64_t x_stride,
                         const void* residual, int64_t residual_stride, void* residual_out,
                         int64_t residual_out_stride, const void* gamma, float eps, float weight_offset,
@@ -598,15 +639,6 @@ int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t str
                                                                                                 : n;
     if (overlap(Span(in, in_bytes), Span(out, out_bytes))) return RMSQ_ERR_ALIAS;
     return launched(launch_convert(kind, in, out, n, stream));
-}
-
-int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, hipStream_t stream) {
-    if (read_bytes <= 0 || write_bytes <= 0 || read_bytes % 16 != 0 || write_bytes % 16 != 0)
-        return RMSQ_ERR_SHAPE;
-    if (!src || !dst) return RMSQ_ERR_NULL;
-    if (!aligned(src, 16) || !aligned(dst, 16)) return RMSQ_ERR_ALIGN;
-    if (overlap(Span(src, read_bytes), Span(dst, write_bytes))) return RMSQ_ERR_ALIAS;
-    return launched(launch_stream(src, read_bytes, dst, write_bytes, stream));
 }
 
 int rmsq_set_tuning(int waves_per_row, int vectors_per_lane, int grid_blocks) {

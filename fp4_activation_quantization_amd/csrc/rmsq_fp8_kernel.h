@@ -28,16 +28,29 @@
 // (its 4 VGPRs per vector would leave room for only one 1024-thread block
 // per CU; taken from L2 again after the barrier instead it measured 8% slower
 // on 32768 x 8192 fp32 rows, the load's latency exposed on every row).
+//
+// The row to normalize comes from a source policy Src (the analogue of the
+// input_fn parameter of Mojo docs "rms_norm_fused_fp8"): either InputRows
+// (the x tensor of the arguments), or a copyable struct with
+//   __device__ uint4 operator()(int64_t row, int v) const
+// returning the 16-byte vector v of that row as packed InT elements, which a
+// producer computes from its own operands (each vector is requested once per
+// row, by the lane that owns it, before any of the row's stores).
 #pragma once
+
+#include <type_traits>
 
 #include "rmsq_device.h"
 #include "rmsq_internal.h"
 
 namespace rmsq {
 
-template <typename InT, bool RESID, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW, bool STRIDED, bool GAMMA_FIRST,
-          int PROD>
-__global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
+// The default source: the rows of FusedArgs::x (x_stride bytes apart).
+struct InputRows {};
+
+template <class Src, typename InT, bool RESID, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW, bool STRIDED,
+          bool GAMMA_FIRST, int PROD>
+__global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a, const Src src) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
     constexpr double INV_FMAX = FNUZ ? 1.0 / 240.0 : 1.0 / 448.0;
@@ -116,10 +129,15 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
         float amax32 = 0.0f;
         double amax64 = 0.0;
         if (active) {
-            const char* xr = static_cast<const char*>(a.x) + row * x_stride;
             // vectors past the end of the row are zero: they add nothing
+            if constexpr (std::is_same_v<Src, InputRows>) {
+                const char* xr = static_cast<const char*>(a.x) + row * x_stride;
 #pragma unroll
-            for (int k = 0; k < VPT; ++k) xv[k] = live(k) ? load_stream(xr, lt + k * T) : make_uint4(0, 0, 0, 0);
+                for (int k = 0; k < VPT; ++k) xv[k] = live(k) ? load_stream(xr, lt + k * T) : make_uint4(0, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) xv[k] = live(k) ? src(row, lt + k * T) : make_uint4(0, 0, 0, 0);
+            }
             // every load of the row is issued before any store: residual_out
             // may alias residual, so a load placed after a store could not be
             // moved ahead of it and each vector would cost a round trip
@@ -248,39 +266,40 @@ __global__ void __launch_bounds__(1024) fp8_kernel(const FusedArgs a) {
 
 namespace fp8_launch {
 
-template <typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED, bool GAMMA_FIRST, int PROD>
-void launch_shape(const FusedArgs& a, Shape s, dim3 gd, dim3 bd, hipStream_t stream) {
+template <class Src, typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED, bool GAMMA_FIRST, int PROD>
+void launch_shape(const FusedArgs& a, const Src& src, Shape s, dim3 gd, dim3 bd, hipStream_t stream) {
     const bool exact = a.nvec == VPT * s.waves * 64;
     // the LDS gamma stash of fp32 rows (the forms other than kProdF32)
     const size_t lds = PROD != kProdF32 && Vec<InT>::BYTES == 4 && !GAMMA_FIRST ? (size_t)bd.x * VPT * 16 : 0;
     if (s.rpb == 1) {
         if (exact)
-            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, true, STRIDED, GAMMA_FIRST, PROD>), gd, bd, lds,
-                               stream, a);
+            hipLaunchKernelGGL((fp8_kernel<Src, InT, RESID, FNUZ, VPT, true, true, STRIDED, GAMMA_FIRST, PROD>), gd, bd,
+                               lds, stream, a, src);
         else
-            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, true, STRIDED, GAMMA_FIRST, PROD>), gd, bd, lds,
-                               stream, a);
+            hipLaunchKernelGGL((fp8_kernel<Src, InT, RESID, FNUZ, VPT, false, true, STRIDED, GAMMA_FIRST, PROD>), gd, bd,
+                               lds, stream, a, src);
     } else {
         if (exact)
-            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, true, false, STRIDED, GAMMA_FIRST, PROD>), gd, bd, lds,
-                               stream, a);
+            hipLaunchKernelGGL((fp8_kernel<Src, InT, RESID, FNUZ, VPT, true, false, STRIDED, GAMMA_FIRST, PROD>), gd,
+                               bd, lds, stream, a, src);
         else
-            hipLaunchKernelGGL((fp8_kernel<InT, RESID, FNUZ, VPT, false, false, STRIDED, GAMMA_FIRST, PROD>), gd, bd,
-                               lds, stream, a);
+            hipLaunchKernelGGL((fp8_kernel<Src, InT, RESID, FNUZ, VPT, false, false, STRIDED, GAMMA_FIRST, PROD>), gd,
+                               bd, lds, stream, a, src);
     }
 }
 
 // the product form: kProdF32 / kProdTwo without a weight offset, else kProdF64
-template <typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED, bool GAMMA_FIRST>
-void launch_numerics(const FusedArgs& a, Shape s, dim3 gd, dim3 bd, hipStream_t stream) {
+template <class Src, typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED, bool GAMMA_FIRST>
+void launch_numerics(const FusedArgs& a, const Src& src, Shape s, dim3 gd, dim3 bd, hipStream_t stream) {
     if (prod_mode<InT>(a.weight_offset) == kProdF64)
-        launch_shape<InT, RESID, FNUZ, VPT, STRIDED, GAMMA_FIRST, kProdF64>(a, s, gd, bd, stream);
+        launch_shape<Src, InT, RESID, FNUZ, VPT, STRIDED, GAMMA_FIRST, kProdF64>(a, src, s, gd, bd, stream);
     else
-        launch_shape<InT, RESID, FNUZ, VPT, STRIDED, GAMMA_FIRST, prod_mode<InT>(0.0f)>(a, s, gd, bd, stream);
+        launch_shape<Src, InT, RESID, FNUZ, VPT, STRIDED, GAMMA_FIRST, prod_mode<InT>(0.0f)>(a, src, s, gd, bd,
+                                                                                             stream);
 }
 
-template <typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED>
-hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
+template <class Src, typename InT, bool RESID, bool FNUZ, int VPT, bool STRIDED>
+hipError_t launch_vpt(FusedArgs a, const Src& src, Shape s, hipStream_t stream) {
     a.waves = s.waves;
     const int64_t groups = (a.rows + s.rpb - 1) / s.rpb;
     // default: one block per row group
@@ -291,25 +310,29 @@ hipError_t launch_vpt(FusedArgs a, Shape s, hipStream_t stream) {
     const dim3 gd((unsigned)grid), bd(s.waves * s.rpb * 64);
     // gamma before the rows only for small batches without a residual
     if (!RESID && a.rows <= kLatencyRows)
-        launch_numerics<InT, RESID, FNUZ, VPT, STRIDED, !RESID>(a, s, gd, bd, stream);
+        launch_numerics<Src, InT, RESID, FNUZ, VPT, STRIDED, !RESID>(a, src, s, gd, bd, stream);
     else
-        launch_numerics<InT, RESID, FNUZ, VPT, STRIDED, false>(a, s, gd, bd, stream);
+        launch_numerics<Src, InT, RESID, FNUZ, VPT, STRIDED, false>(a, src, s, gd, bd, stream);
     return hipGetLastError();
 }
 
-template <typename InT, bool RESID, bool FNUZ, bool STRIDED>
-hipError_t by_vpt(const FusedArgs& a, Shape s, hipStream_t st) {
+template <class Src, typename InT, bool RESID, bool FNUZ, bool STRIDED>
+hipError_t by_vpt(const FusedArgs& a, const Src& src, Shape s, hipStream_t st) {
     switch (s.vpt) {
-    case 1: return launch_vpt<InT, RESID, FNUZ, 1, STRIDED>(a, s, st);
-    case 2: return launch_vpt<InT, RESID, FNUZ, 2, STRIDED>(a, s, st);
-    default: return launch_vpt<InT, RESID, FNUZ, 4, STRIDED>(a, s, st);
+    case 1: return launch_vpt<Src, InT, RESID, FNUZ, 1, STRIDED>(a, src, s, st);
+    case 2: return launch_vpt<Src, InT, RESID, FNUZ, 2, STRIDED>(a, src, s, st);
+    default: return launch_vpt<Src, InT, RESID, FNUZ, 4, STRIDED>(a, src, s, st);
     }
 }
 
 template <typename InT, bool STRIDED>
 hipError_t by_variant(const FusedArgs& a, bool resid, bool fnuz, Shape s, hipStream_t st) {
-    if (resid) return fnuz ? by_vpt<InT, true, true, STRIDED>(a, s, st) : by_vpt<InT, true, false, STRIDED>(a, s, st);
-    return fnuz ? by_vpt<InT, false, true, STRIDED>(a, s, st) : by_vpt<InT, false, false, STRIDED>(a, s, st);
+    const InputRows src;
+    if (resid)
+        return fnuz ? by_vpt<InputRows, InT, true, true, STRIDED>(a, src, s, st)
+                    : by_vpt<InputRows, InT, true, false, STRIDED>(a, src, s, st);
+    return fnuz ? by_vpt<InputRows, InT, false, true, STRIDED>(a, src, s, st)
+                : by_vpt<InputRows, InT, false, false, STRIDED>(a, src, s, st);
 }
 
 }  // namespace fp8_launch
@@ -323,6 +346,14 @@ hipError_t launch_fp8_typed(const FusedArgs& a, bool residual, bool fnuz, Shape 
                           (!residual || (a.residual_stride == rb && a.residual_out_stride == rb));
     return adjacent ? fp8_launch::by_variant<InT, false>(a, residual, fnuz, s, stream)
                     : fp8_launch::by_variant<InT, true>(a, residual, fnuz, s, stream);
+}
+
+// The FP8 kernel without a residual over rows from a source policy (adjacent
+// output rows; `a.x` and `a.x_stride` unused).
+template <typename InT, class Src>
+hipError_t launch_fp8_from(const FusedArgs& a, const Src& src, bool fnuz, Shape s, hipStream_t stream) {
+    return fnuz ? fp8_launch::by_vpt<Src, InT, false, true, false>(a, src, s, stream)
+                : fp8_launch::by_vpt<Src, InT, false, false, false>(a, src, s, stream);
 }
 
 }  // namespace rmsq

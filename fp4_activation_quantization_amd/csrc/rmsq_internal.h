@@ -78,6 +78,10 @@ enum { kPathFp8 = 0, kPathFp4 = 1, kPathFp4Residual = 2, kPathFp8Elem = 3, kPath
 // variants are chosen for the time of one call); larger ones stream.
 constexpr int64_t kLatencyRows = 256;
 
+// Widest row of the vector kernels (16 waves x 4 vectors per lane); wider
+// rows of whole vectors take the wide-row kernels.
+constexpr int kMaxVec = 16 * 64 * 4;
+
 // Pick the automatic shape for a row of nvec 16-byte vectors of esz-byte
 // elements (or apply the process-wide override).  Returns false if no
 // supported shape holds the row.
@@ -99,6 +103,10 @@ constexpr int64_t kMaxElemHidden = 16 * 64 * 16;
 bool choose_elem_shape(int64_t rows, int64_t hidden, Shape* s);
 
 // Kernel launchers (no argument checks).  Return the hipError_t of the launch.
+// gated_rmsnorm_fp8: the FP8 kernel without a residual over x = a * b
+// (rmsq_fp8_gated.hip; `fa.x` unused).
+hipError_t launch_fp8_gated(const FusedArgs& fa, const void* a, const void* b, int in_dtype, bool fnuz, Shape s,
+                            hipStream_t stream);
 hipError_t launch_fp8(const FusedArgs& a, int in_dtype, bool residual, int out_fp8,
                       Shape shape, hipStream_t stream);
 hipError_t launch_fp8_phased(const FusedArgs& a, int in_dtype, bool residual, int out_fp8, Shape shape,
@@ -122,7 +130,6 @@ enum { kWideFp8 = 0, kWideFp8Fnuz = 1, kWideFp4 = 2 };
 // grid_blocks: 0 = one block per resident slot (the row count at most).
 hipError_t launch_wide(const FusedArgs& a, int in_dtype, bool residual, int out, Fp4Format fmt, int grid_blocks,
                        hipStream_t stream);
-hipError_t launch_stream(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, hipStream_t stream);
 
 // Occupancy-based persistent grid size for a kernel with that block size and
 // dynamic LDS per block (cached per device, kernel and launch parameters).

@@ -176,6 +176,31 @@ int allreduce_residual_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype, i
                                    hipStream_t stream);
 
 /*
+ * gated_rmsnorm_fp8 -- RMSNorm + per-row FP8 quantization of rows produced
+ * while they are loaded: x = a * b element by element, rounded once to
+ * in_dtype (RNE), never stored.  This is rms_norm_fused_fp8 with an input_fn
+ * (Mojo docs "rms_norm_fused_fp8", Parameters: input_fn, the function that
+ * loads input values) that multiplies the gate and up projections of a
+ * gated MLP (the activation applied upstream); C++ callers can feed the same
+ * kernel from a producer of their own (include/rmsq_fused.hpp).
+ *   a, b    : [rows, hidden] in in_dtype, 16-byte aligned, rows adjacent;
+ *             they may share memory (they are only read).  The product is
+ *             formed in fp32: for 16-bit operands it is exact (unless below
+ *             2^-126 in magnitude, bf16 only) and then rounded once; for
+ *             fp32 operands the multiply rounds once.
+ *   hidden  : a multiple of 8 (16-bit) or 4 (fp32), at most 4096 16-byte
+ *             vectors (RMSQ_ERR_UNSUPPORTED above).
+ *   out     : [rows, hidden], 16-byte aligned; out and scales overlap
+ *             neither a, b, gamma nor each other (RMSQ_ERR_ALIAS).
+ *   other arguments and the result as rmsnorm_fp8 of x.
+ */
+int gated_rmsnorm_fp8(int64_t rows, int64_t hidden, int in_dtype,
+                      const void* a, const void* b, const void* gamma,
+                      float eps, float weight_offset, float scale_ub,
+                      int out_fp8, void* out, int scales_dtype, void* scales,
+                      hipStream_t stream);
+
+/*
  * rmsnorm_fp4 -- RMSNorm + block-scaled FP4 (NVFP4-style) quantization:
  * FlashInfer "rmsnorm_fp4quant.py" (rmsnorm_fp4quant, block_size 16, E4M3
  * scale factors, row-major scale layout).
@@ -330,22 +355,6 @@ enum {
     RMSQ_CVT_E4M3FN_TO_F32 = 5
 };
 int rmsq_convert(int kind, const void* in, void* out, int64_t n, hipStream_t stream);
-
-/*
- * rmsq_stream_probe -- measurement reference, not part of the method: a
- * kernel that reads read_bytes from src and writes write_bytes to dst with
- * the fused kernels' 16-byte non-temporal accesses and no arithmetic, in the
- * same read : write proportion (within 2%) and the same order per block (a
- * chunk of reads, then a chunk of writes).  Its rate is the achievable HBM
- * ceiling for a fused workload with that traffic, the "plain streaming
- * kernel that moves the same bytes" the measurement compares with.
- *   src, dst   : DEVICE pointers, 16-byte aligned, not overlapping.
- *   read_bytes, write_bytes : > 0, multiples of 16.
- * The bytes written are unspecified.  Returns RMSQ_ERR_SHAPE, _NULL, _ALIGN
- * or _ALIAS before any HIP call, RMSQ_ERR_LAUNCH on a failed launch.
- */
-int rmsq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
-                      hipStream_t stream);
 
 /*
  * rmsq_set_tuning -- process-wide launch-shape override for subsequent calls

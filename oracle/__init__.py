@@ -295,6 +295,19 @@ def _run(work, rows: int, threads: int | None):
         raise RuntimeError(f"oracle failed with status {rc}")
 
 
+# ---- producers (rms_norm_fused_fp8's input_fn) ----------------------------
+
+def gated_product(a, b, *, in_dtype: str) -> np.ndarray:
+    """x = a * b element by element, rounded once to in_dtype (RNE); returns
+    x's stored bits.  This is the producer gated_rmsnorm_fp8 puts in front of
+    the normalization, in the place of the input_fn parameter of Mojo docs
+    "rms_norm_fused_fp8" (the function that loads input values).  The float64
+    product of two values of in_dtype is exact (at most 2 x 24 significant
+    bits, and float64's exponent range holds it), so the one rounding is
+    round_to's."""
+    return round_to(in_dtype, value_of(in_dtype, a) * value_of(in_dtype, b))
+
+
 # ---- codecs ---------------------------------------------------------------
 
 def encode(fmt: str, values) -> np.ndarray:

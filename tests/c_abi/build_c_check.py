@@ -16,12 +16,18 @@ EXE = os.path.join(HERE, "rmsq_c_check")
 
 
 def build(out: str = EXE, verbose: bool = False) -> str:
+    # RMSQ_SANITIZE=1 (tests/sanitize/run_sanitized.py): the program under
+    # ASan / UBSan, over the sanitized host layer built there
+    san = os.environ.get("RMSQ_SANITIZE") == "1"
+    libdir = os.path.join(ROOT, "tests", "sanitize") if san else LIBDIR
+    flags = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"] if san \
+        else []
     # hip_runtime_api.h selects its AMD declarations by this macro (hipcc
     # defines it; a plain C compiler needs it spelled out)
-    cmd = ["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+    cmd = ["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", *flags, "-D__HIP_PLATFORM_AMD__",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"), SRC, "-o", out + ".tmp",
-           "-L", LIBDIR, "-lrmsq", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
-           "-Wl,-rpath," + LIBDIR, "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+           "-L", libdir, "-lrmsq", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath," + libdir, "-Wl,-rpath," + os.path.join(ROCM, "lib")]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -41,9 +41,10 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "allreduce_residual_rmsnorm_fp8", "rmsnorm_fp4", "rmsnorm_fp4quant", "residual_rmsnorm_fp4quant",
+    for f in ("rmsnorm_fp8", "residual_rmsnorm_fp8", "allreduce_residual_rmsnorm_fp8", "gated_rmsnorm_fp8",
+              "rmsnorm_fp4", "rmsnorm_fp4quant", "residual_rmsnorm_fp4quant",
               "rmsnorm_fp8_strided", "rmsnorm_fp4quant_strided", "rmsq_fp4_scale_bytes",
-              "rmsq_convert", "rmsq_stream_probe",
+              "rmsq_convert",
               "rmsq_set_tuning", "rmsq_query_shape", "rmsq_status_string", "rmsq_abi_version",
               "rmsq_last_hip_error"):
         assert f in fns, f
@@ -94,6 +95,37 @@ def fp4(rows=4, hidden=4096, dt=rq.BF16, x=None, g=None, gs=None, out=None, bs=N
     out = P(2) if out is None else out
     bs = P(3) if bs is None else bs
     return rq.lib().rmsnorm_fp4(rows, hidden, dt, x, g, eps, off, gs, out, bs, None)
+
+
+def gfp8(rows=4, hidden=4096, dt=rq.BF16, a=None, b=None, g=None, eps=1e-6, off=0.0, ub=1200.0, fmt=rq.E4M3FN,
+         out=None, sdt=rq.F32, sc=None):
+    a = P(0) if a is None else a
+    b = P(4) if b is None else b
+    g = P(1) if g is None else g
+    out = P(2) if out is None else out
+    sc = P(3) if sc is None else sc
+    return rq.lib().gated_rmsnorm_fp8(rows, hidden, dt, a, b, g, eps, off, ub, fmt, out, sdt, sc, None)
+
+
+def test_gated_argument_errors():
+    """gated_rmsnorm_fp8 rejects before any launch (the forced one-wave shape
+    cannot hold a valid call's row either: UNSUPPORTED, still no launch)."""
+    assert gfp8(dt=9) == DTYPE and gfp8(sdt=5) == DTYPE and gfp8(fmt=3) == DTYPE
+    assert gfp8(rows=-1) == SHAPE and gfp8(hidden=0) == SHAPE and gfp8(hidden=4100) == SHAPE
+    assert gfp8(hidden=4102, dt=rq.F32) == SHAPE and gfp8(rows=1 << 62, hidden=1 << 20) == SHAPE
+    assert gfp8(eps=-1.0) == VALUE and gfp8(ub=0.0) == VALUE and gfp8(off=math.nan) == VALUE
+    assert gfp8(hidden=8 * 4096 + 8) == UNSUP and gfp8(hidden=4 * 4096 + 4, dt=rq.F32) == UNSUP
+    assert gfp8(rows=0, a=ctypes.c_void_p(0)) == OK  # nothing to do
+    z = ctypes.c_void_p(0)
+    assert gfp8(a=z) == NULL and gfp8(b=z) == NULL and gfp8(g=z) == NULL and gfp8(out=z) == NULL
+    assert gfp8(sc=z) == NULL
+    odd = lambda i: ctypes.c_void_p(BASE + i * MB + 8)  # noqa: E731
+    assert gfp8(a=odd(0)) == ALIGN and gfp8(b=odd(4)) == ALIGN and gfp8(g=odd(1)) == ALIGN
+    assert gfp8(out=odd(2)) == ALIGN and gfp8(sc=ctypes.c_void_p(BASE + 3 * MB + 2)) == ALIGN
+    assert gfp8(out=P(0)) == ALIAS and gfp8(sc=P(4)) == ALIAS and gfp8(out=P(1)) == ALIAS
+    assert gfp8(sc=P(2)) == ALIAS
+    assert gfp8(b=P(0)) == UNSUP  # a and b may be the same tensor
+    assert gfp8() == UNSUP
 
 
 def test_fp8_dtype_errors():
@@ -356,18 +388,6 @@ def test_convert_errors():
     assert L.rmsq_convert(rq.CVT_F32_TO_BF16, P(0), ctypes.c_void_p(BASE + 16), 8, None) == ALIAS
 
 
-def test_stream_probe_argument_checks():
-    """Every rejection happens before a launch (no device needed)."""
-    L = rq.lib()
-    P = lambda off: ctypes.c_void_p(BASE + off)
-    assert L.rmsq_stream_probe(P(0), 0, P(1 << 20), 16, None) == SHAPE
-    assert L.rmsq_stream_probe(P(0), 16, P(1 << 20), 0, None) == SHAPE
-    assert L.rmsq_stream_probe(P(0), 24, P(1 << 20), 16, None) == SHAPE
-    assert L.rmsq_stream_probe(ctypes.c_void_p(0), 16, P(1 << 20), 16, None) == NULL
-    assert L.rmsq_stream_probe(P(8), 16, P(1 << 20), 16, None) == ALIGN
-    assert L.rmsq_stream_probe(P(0), 64, P(32), 64, None) == ALIAS
-
-
 def test_tuning_and_query_shape():
     L = rq.lib()
     assert L.rmsq_set_tuning(17, 0, 0) == VALUE
@@ -484,8 +504,7 @@ def test_binding_rejects_host_tensors():
                  lambda: rq.residual_rmsnorm_fp4quant(x, x.clone(), g),
                  lambda: rq.allreduce_residual_rmsnorm_fp8([x.clone()], x, g),
                  lambda: rq.rmsnorm_fp8_strided(x, g), lambda: rq.rmsnorm_fp4quant_strided(x, g),
-                 lambda: rq.convert(rq.CVT_F32_TO_E4M3FN, x.float(), torch.empty(4096, dtype=torch.uint8)),
-                 lambda: rq.stream_probe(x, 16, x.clone(), 16)):
+                 lambda: rq.convert(rq.CVT_F32_TO_E4M3FN, x.float(), torch.empty(4096, dtype=torch.uint8))):
         with pytest.raises(ValueError, match="GPU"):
             call()
 

@@ -1,10 +1,10 @@
-"""The streaming reference kernel (rmsq_stream_probe) used as the bandwidth
-reference in bench.py: it runs, writes exactly write_bytes of its destination
-(guard bytes past the end keep their values) and reads only its source."""
+"""The streaming reference kernels (librmsq_probe) bench.py takes its
+bandwidth ceiling from: they run, write exactly the bytes they are given
+(guard bytes past the end keep their values) and only read their sources."""
 import pytest
 import torch
 
-import fp4_activation_quantization_amd as rq
+from fp4_activation_quantization_amd import probe
 from gpu_common import DEV, say
 
 pytestmark = pytest.mark.gpu
@@ -12,22 +12,46 @@ pytestmark = pytest.mark.gpu
 GUARD = 4096
 
 
-@pytest.mark.parametrize("read_bytes,write_bytes", [
-    (16, 16),                         # one vector each
-    (134225920, 100696064),           # the 8192 x 4096 residual workload's split (4 : 3)
-    (234895376, 66060288),            # the 16384 x 7168 FP4 workload's split (about 7 : 2)
-    (4096 * 16 + 48, 16 * 3),         # ragged, read-heavy beyond 32 : 1
-    (16 * 5, 4096 * 16 + 32),         # write-heavy
+@pytest.mark.parametrize("read_bytes,write_bytes,rv,wv,block,nl,per_cu,inter", [
+    (16, 16, 1, 1, 256, 16, 0, False),                     # one vector each
+    (134225920, 100696064, 4, 3, 256, 16, 0, False),       # the 8192 x 4096 residual workload's split
+    (234895376, 66060288, 7, 2, 512, 8, 4, True),          # the 16384 x 7168 FP4 split, persistent, interleaved
+    (4096 * 16 + 48, 16 * 3, 64, 1, 1024, 4, 0, True),     # ragged, read-heavy
+    (16 * 5, 4096 * 16 + 32, 1, 64, 64, 1, 1, False),      # write-heavy
 ])
-def test_stream_probe_writes_exactly_its_range(read_bytes, write_bytes):
-    say(f"[stream] read {read_bytes} write {write_bytes}")
+def test_chunk_probe_writes_exactly_its_range(read_bytes, write_bytes, rv, wv, block, nl, per_cu, inter):
+    say(f"[chunk probe] read {read_bytes} write {write_bytes} rv:wv {rv}:{wv} block {block} nl {nl}")
     src = torch.full((read_bytes + GUARD,), 7, dtype=torch.uint8, device=DEV)
     dst = torch.full((write_bytes + GUARD,), 0xA5, dtype=torch.uint8, device=DEV)
     before = src.clone()
-    rq.stream_probe(src, read_bytes, dst, write_bytes)
+    probe.Chunks(src, read_bytes, dst, write_bytes, rv=rv, wv=wv, block=block, loads_in_flight=nl,
+                 blocks_per_cu=per_cu, interleave=inter)()
     torch.cuda.synchronize()
     assert torch.equal(src, before)
     assert bool((dst[write_bytes:] == 0xA5).all())
-    # every written vector holds the XOR of the source vectors a block read
-    # (7s cancel in pairs) plus the chunk index: the range was written
-    assert not bool((dst[:write_bytes] == 0xA5).all())
+    # each written vector is its lane's XOR of 7s plus the chunk index, never
+    # the fill: every 16-byte vector of the range was written
+    v = dst[:write_bytes].view(-1, 16)
+    assert not bool((v == 0xA5).all(dim=1).any())
+
+
+@pytest.mark.parametrize("rows,nin,row_bytes,outs,block,vpt,grid", [
+    (1, 1, 16, [16, 4], 64, 1, 0),
+    (300, 2, 16384, [16384, 8192, 4], 512, 2, 0),           # the residual FP8 layout (bf16 8192 wide)
+    (257, 1, 14336, [3584, 448], 256, 4, 64),               # the FP4 layout, a strided grid
+    (33, 9, 8192, [8192, 4096, 4], 512, 1, 0),              # eight summed inputs and the residual
+    (5, 2, 32768, [32768, 8192, 4], 1024, 2, 3),
+])
+def test_row_probe_writes_exactly_its_rows(rows, nin, row_bytes, outs, block, vpt, grid):
+    say(f"[row probe] rows {rows} nin {nin} row {row_bytes} outs {outs} block {block} vpt {vpt} grid {grid}")
+    ins = [torch.full((rows * row_bytes + GUARD,), 3 + i, dtype=torch.uint8, device=DEV) for i in range(nin)]
+    ous = [torch.full((rows * b + GUARD,), 0xA5, dtype=torch.uint8, device=DEV) for b in outs]
+    before = [t.clone() for t in ins]
+    probe.Rows(rows, ins, row_bytes, ous, outs, block=block, vpt=vpt, grid=grid)()
+    torch.cuda.synchronize()
+    for t, b in zip(ins, before):
+        assert torch.equal(t, b)
+    for t, b in zip(ous, outs):
+        assert bool((t[rows * b:] == 0xA5).all())
+        gran = 16 if b % 16 == 0 else 4
+        assert not bool((t[:rows * b].view(-1, gran) == 0xA5).all(dim=1).any())
