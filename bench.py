@@ -23,8 +23,9 @@ Printed: one JSON line.  Other workloads are reported in its "workloads"
 object; --workloads selects them (the headline leads when it is selected).
 The CPU baseline is the float64 oracle timed on each workload (the whole
 tensor or its first rows, bounded), on the CPU share the GPU job has.
---copy-calibration runs only a plain copy of known size, the reference that
-rocprofv3's FETCH_SIZE / WRITE_SIZE readings are scaled by.
+--copy-calibration runs only reference kernels of known traffic (the
+streaming probe, then a device copy), the references that rocprofv3's
+FETCH_SIZE / WRITE_SIZE readings are scaled by.
 """
 from __future__ import annotations
 
@@ -508,14 +509,78 @@ def cpu_baseline(results: dict, lead: str) -> dict:
 
 
 def copy_calibration(nbytes: int, steps: int) -> None:
-    """A plain device-to-device copy of nbytes (torch's copy kernel), for scaling
-    rocprofv3's FETCH_SIZE / WRITE_SIZE counters: it reads and writes nbytes."""
-    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
-    dst = torch.empty_like(src)
+    """Reference kernels of known traffic for scaling rocprofv3's FETCH_SIZE /
+    WRITE_SIZE counters: the streaming probe (the fused kernels' non-temporal
+    16-byte loads and stores) reading nbytes and writing nbytes / 4, then
+    torch's device copy of nbytes (ordinary loads and stores)."""
+    from fp4_activation_quantization_amd import probe
+
+    nbytes -= nbytes % 64
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    f = probe.Chunks(src, nbytes, dst, nbytes // 4, rv=4, wv=1, block=256, loads_in_flight=16)
+    for _ in range(steps):
+        f()
     for _ in range(steps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": nbytes, "steps": steps}), flush=True)
+    print(json.dumps({"probe_read_bytes": nbytes, "probe_write_bytes": nbytes // 4, "copy_bytes": nbytes,
+                      "steps": steps}), flush=True)
+
+
+def placement_sweep(w: workloads.Workload, log) -> None:
+    """How a residual FP8 workload's rate depends on where its row tensors
+    sit: (1) five fresh allocations of the workload's buffers in this process,
+    a growing spacer allocation held between them; (2) x, residual and
+    residual_out carved from one allocation at chosen offsets, with the
+    row-form streaming reference on the same views.  Each time is the median
+    of 3 windows of 50 ms after 30 ms of settling."""
+    from fp4_activation_quantization_amd import probe
+
+    assert w.residual and not w.fp4 and w.ninputs == 1, "a residual FP8 workload"
+    spacers = []
+    for t in range(5):
+        c = Case(w, 1, None)
+        settle(c, 30)
+        r = time_windows(c, 50, 3)
+        log(f"| fresh allocation {t} | {r['launch_us']:.2f} | | x at {c.keep[1].data_ptr():#x} |")
+        del c
+        torch.cuda.empty_cache()
+        spacers.append(torch.empty((t + 1) * (256 << 20), dtype=torch.uint8, device="cuda:0"))
+    spacers.clear()
+    torch.cuda.empty_cache()
+    inp = workloads.make(w)
+    esz = {"bf16": 2, "f16": 2, "f32": 4}[w.in_dtype]
+    td = workloads.TORCH_DTYPES[w.in_dtype]
+    tb = w.rows * w.hidden * esz
+    MB = 1 << 20
+    big = torch.empty(3 * tb + 64 * MB, dtype=torch.uint8, device="cuda:0")
+    g = inp["gamma"].to("cuda:0")
+    out = torch.empty(w.rows * w.hidden, dtype=torch.uint8, device="cuda:0")
+    sc = torch.empty(w.rows, dtype=torch.float32, device="cuda:0")
+    row = w.hidden * esz
+
+    class _Timed:
+        def __init__(self, fn):
+            self.w, self.step = w, (lambda i: fn())
+
+    for d1, d2 in [(0, 0), (4096, 8192), (65536, 131072), (MB, 2 * MB), (2 * MB + 4096, 4 * MB + 8192),
+                   (8 * MB, 16 * MB), (16 * MB + 65536, 32 * MB + 131072), (3 * MB, 7 * MB)]:
+        views = [big[o:o + tb].view(td).view(w.rows, w.hidden) for o in (0, tb + d1, 2 * tb + d2)]
+        x, r, ro = views
+        x.copy_(inp["x"])
+        r.copy_(inp["residual"])
+        fused = _Timed(lambda: rq.residual_rmsnorm_fp8(x, r, g, eps=w.eps, scale_ub=w.scale_ub, out=out, scales=sc,
+                                                       residual_out=ro))
+        settle(fused, 30)
+        tf = time_windows(fused, 50, 3)["launch_us"]
+        u8 = [v.view(torch.uint8).view(-1) for v in views]
+        f = probe.Rows(w.rows, u8[:2], row, [u8[2], out, sc.view(torch.uint8)], [row, w.hidden, 4], block=256,
+                       vpt=max(1, min(8, row // 4096)))
+        ref = _Timed(f)
+        settle(ref, 30)
+        tp = time_windows(ref, 50, 3)["launch_us"]
+        log(f"| residual at +{d1 // 1024} KiB, residual_out at +{d2 // 1024} KiB | {tf:.2f} | {tp:.2f} | |")
 
 
 def workload_of(name: str) -> workloads.Workload:
@@ -553,8 +618,11 @@ def main() -> int:
                     "configuration")
     ap.add_argument("--probe-sweep", action="store_true", help="only sweep the streaming reference kernels over "
                     "their full configuration set for the selected workloads, print a table and exit")
+    ap.add_argument("--placement-sweep", action="store_true", help="only time the selected residual FP8 workloads "
+                    "on several buffer placements, print a table and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain copy of BYTES (for counter scaling) and exit")
+                    help="only run the counter-scaling references (the streaming probe reading BYTES and writing "
+                    "BYTES/4, then a device copy of BYTES) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -580,6 +648,13 @@ def main() -> int:
     # the lead workload runs first, on a GPU whose memory no other workload
     # has used yet (later runs of the same kernel measured up to 2% slower)
     names = [lead] + [n for n in names if n != lead]
+
+    if args.placement_sweep:
+        for name in names:
+            print(f"## {name}\n\n| placement | fused us | row-form streaming reference us | |\n|---|---|---|---|",
+                  flush=True)
+            placement_sweep(workload_of(name), lambda m: print(m, flush=True))
+        return 0
 
     if args.probe_sweep:
         for name in names:
