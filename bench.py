@@ -311,7 +311,8 @@ class _ProbeCase:
                 ous = [torch.empty(w.rows * b, dtype=torch.uint8, device=dev) for b in outs]
                 self.keep += ins + ous
                 self.launches.append(probe.Rows(w.rows, ins, row, ous, outs, block=cfg["block"], vpt=cfg["vpt"],
-                                                grid=cfg.get("grid", 0)))
+                                                grid=cfg.get("grid", 0), phased=cfg.get("phased", False),
+                                                mapped=cfg.get("mapped", False), lds_bytes=cfg.get("lds", 0)))
         else:
             rb, wb = (-(-b // 16) * 16 for b in algorithmic_split(w))
             self.nbytes = rb + wb
@@ -358,6 +359,13 @@ def probe_candidates(w: workloads.Workload, full: bool = False) -> list[dict]:
             continue
         for grid in ((0, 256, 1024, 2048) if full else (0,)):
             cands.append({"kind": "rows", "block": block, "vpt": vpt, "grid": grid})
+        # the fused kernels' own order (first output, a barrier, the others)
+        # and store pieces (codes by the lane holding their input vector),
+        # with 4, 3 or 2 blocks per CU at most (unused LDS)
+        if len(outs) > 1:
+            for lds in (0, 40960, 54272, 65536):
+                cands.append({"kind": "rows", "block": block, "vpt": vpt, "grid": 0, "phased": True, "mapped": True,
+                              "lds": lds})
     rb, wb = algorithmic_split(w)
     base = _unit_ratio(rb, wb)
     # the default set: the configurations that won the full sweep on the
@@ -365,7 +373,7 @@ def probe_candidates(w: workloads.Workload, full: bool = False) -> list[dict]:
     ratios = [base] + ([(2 * base[0], 2 * base[1])] if 2 * max(base) <= 64 else [])
     for rv, wv in ratios:
         for block in ((256, 512, 1024) if full else (256, 1024)):
-            for nl in ((4, 8, 16) if full else (8, 16)):
+            for nl in ((4, 8, 16) if full else (16,)):
                 for per_cu in ((0, 4) if full else (0,)):
                     for inter in (False, True):
                         cands.append({"kind": "chunks", "rv": rv, "wv": wv, "block": block, "nl": nl,

@@ -24,7 +24,7 @@ def lib() -> ctypes.CDLL:
         L.rmsq_probe_chunks.argtypes = [P, I64, P, I64, I, I, I, I, I, I, P]
         L.rmsq_probe_chunks.restype = I
         L.rmsq_probe_rows.argtypes = [I64, I, ctypes.POINTER(P), I64, I, ctypes.POINTER(P), ctypes.POINTER(I64), I, I,
-                                      I, P]
+                                      I, I, I, P]
         L.rmsq_probe_rows.restype = I
         _lib = L
     return _lib
@@ -64,7 +64,8 @@ class Rows:
     arguments marshalled once."""
 
     def __init__(self, rows: int, inputs: list[torch.Tensor], in_row_bytes: int, outputs: list[torch.Tensor],
-                 out_row_bytes: list[int], *, block: int, vpt: int, grid: int = 0, stream=None):
+                 out_row_bytes: list[int], *, block: int, vpt: int, grid: int = 0, phased: bool = False,
+                 mapped: bool = False, lds_bytes: int = 0, stream=None):
         _on_gpu(*inputs, *outputs)
         if any(_bytes(t) < rows * in_row_bytes for t in inputs) or \
                 any(_bytes(t) < rows * b for t, b in zip(outputs, out_row_bytes)) or len(outputs) != len(out_row_bytes):
@@ -75,7 +76,7 @@ class Rows:
         self._ob = (ctypes.c_int64 * len(outputs))(*out_row_bytes)
         s = stream if stream is not None else torch.cuda.current_stream(inputs[0].device).cuda_stream
         self.args = (rows, len(inputs), self._ins, in_row_bytes, len(outputs), self._outs, self._ob, block, vpt, grid,
-                     P(s))
+                     int(phased) | (2 if mapped else 0), lds_bytes, P(s))
 
     def __call__(self) -> None:
         rc = lib().rmsq_probe_rows(*self.args)

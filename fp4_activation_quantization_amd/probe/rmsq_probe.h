@@ -59,10 +59,21 @@ int rmsq_probe_chunks(const void* src, int64_t read_bytes, void* dst, int64_t wr
  *                    with nin * vpt <= 16 (the loads in flight per lane).
  *   grid           : 0 = one block per row; else that many blocks striding
  *                    over the rows.
+ *   flags          : bit 0 (phased) stores the first output, then waits at
+ *                    a block barrier, then stores the others (a fused
+ *                    kernel's residual_out before its reduction, codes after
+ *                    it); bit 1 (mapped) stores an output whose row is 4 or 8
+ *                    bytes per input vector in those pieces, each by the lane
+ *                    holding that input vector (a fused kernel's code
+ *                    stores).  Other bits: -2.
+ *   lds_bytes      : dynamic LDS reserved per block and left unused
+ *                    (0..64 KiB, the default limit of a kernel's dynamic
+ *                    LDS): caps the blocks per CU (160 KiB of LDS each) as a
+ *                    fused kernel's own footprint does.
  */
 int rmsq_probe_rows(int64_t rows, int nin, const void* const* inputs, int64_t in_row_bytes, int nout,
                     void* const* outputs, const int64_t* out_row_bytes, int block, int vpt, int grid,
-                    hipStream_t stream);
+                    int flags, int lds_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -63,6 +63,8 @@ struct RowArgs {
     int64_t in_bytes;
     int64_t rows;
     int nout;
+    int phased;  // first output stored, a block barrier, then the others
+    int mapped;  // outputs in pieces matched to the input vectors (below)
 };
 
 // One block per row at a time: every input row's vectors of this lane loaded
@@ -88,9 +90,26 @@ __global__ void __launch_bounds__(1024) row_probe(const RowArgs a) {
             for (int i = 1; i < NIN; ++i) acc[k] ^= v[i][k];
         }
         for (int o = 0; o < a.nout; ++o) {
+            if (a.phased && o == 1) __syncthreads();  // uniform over the block
             const int64_t ob = a.out_bytes[o];
             char* base = a.out[o] + row * ob;
-            if (ob % 16 == 0) {
+            // mapped: the bytes of output o that belong to input vector idx
+            // (ob / nv of them: 4, 8 or 16) stored by the lane holding it,
+            // as a fused kernel stores a vector's codes
+            const int64_t piece = a.mapped && ob % nv == 0 ? ob / nv : 0;
+            if (piece == 4 || piece == 8) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int idx = tid + k * T;
+                    if (idx < nv) {
+                        const u32x4 v = acc[k] + (uint32_t)o;
+                        if (piece == 4)
+                            __builtin_nontemporal_store(v.x, reinterpret_cast<uint32_t*>(base) + idx);
+                        else
+                            __builtin_nontemporal_store(v.x | ((uint64_t)v.y << 32), reinterpret_cast<uint64_t*>(base) + idx);
+                    }
+                }
+            } else if (ob % 16 == 0) {
                 const int nvo = (int)(ob / 16);
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
@@ -107,17 +126,18 @@ __global__ void __launch_bounds__(1024) row_probe(const RowArgs a) {
 // at most 16 loads per lane in flight (nin * vpt <= 16, checked by the caller):
 // every one held in VGPRs without spilling under the 1024-thread bound
 template <int NIN, int VPT>
-void launch_row_probe(const RowArgs& a, int block, int grid, hipStream_t stream) {
-    if constexpr (NIN * VPT <= 16) hipLaunchKernelGGL((row_probe<NIN, VPT>), dim3(grid), dim3(block), 0, stream, a);
+void launch_row_probe(const RowArgs& a, int block, int grid, size_t lds, hipStream_t stream) {
+    if constexpr (NIN * VPT <= 16)
+        hipLaunchKernelGGL((row_probe<NIN, VPT>), dim3(grid), dim3(block), lds, stream, a);
 }
 
 template <int NIN>
-hipError_t launch_rows(const RowArgs& a, int vpt, int block, int grid, hipStream_t stream) {
+hipError_t launch_rows(const RowArgs& a, int vpt, int block, int grid, size_t lds, hipStream_t stream) {
     switch (vpt) {
-    case 1: launch_row_probe<NIN, 1>(a, block, grid, stream); break;
-    case 2: launch_row_probe<NIN, 2>(a, block, grid, stream); break;
-    case 4: launch_row_probe<NIN, 4>(a, block, grid, stream); break;
-    default: launch_row_probe<NIN, 8>(a, block, grid, stream); break;
+    case 1: launch_row_probe<NIN, 1>(a, block, grid, lds, stream); break;
+    case 2: launch_row_probe<NIN, 2>(a, block, grid, lds, stream); break;
+    case 4: launch_row_probe<NIN, 4>(a, block, grid, lds, stream); break;
+    default: launch_row_probe<NIN, 8>(a, block, grid, lds, stream); break;
     }
     return hipGetLastError();
 }
@@ -158,12 +178,13 @@ extern "C" int rmsq_probe_chunks(const void* src, int64_t read_bytes, void* dst,
 
 extern "C" int rmsq_probe_rows(int64_t rows, int nin, const void* const* inputs, int64_t in_row_bytes, int nout,
                                void* const* outputs, const int64_t* out_row_bytes, int block, int vpt, int grid,
-                               hipStream_t stream) {
+                               int flags, int lds_bytes, hipStream_t stream) {
     if (!inputs || !outputs || !out_row_bytes) return -1;
     if (rows < 0 || nin < 1 || nin > kMaxIn || nout < 1 || nout > kMaxOut || in_row_bytes <= 0 ||
-        in_row_bytes % 16 || block < 64 || block > 1024 || block % 64 || grid < 0)
+        in_row_bytes % 16 || block < 64 || block > 1024 || block % 64 || grid < 0 || lds_bytes < 0 ||
+        lds_bytes > 64 * 1024)
         return -2;
-    if ((vpt != 1 && vpt != 2 && vpt != 4 && vpt != 8) || nin * vpt > 16) return -2;
+    if ((vpt != 1 && vpt != 2 && vpt != 4 && vpt != 8) || nin * vpt > 16 || (flags & ~3)) return -2;
     if ((int64_t)block * vpt * 16 < in_row_bytes) return -2;
     RowArgs a{};
     for (int i = 0; i < nin; ++i) {
@@ -185,18 +206,20 @@ extern "C" int rmsq_probe_rows(int64_t rows, int nin, const void* const* inputs,
     a.in_bytes = in_row_bytes;
     a.rows = rows;
     a.nout = nout;
+    a.phased = flags & 1;
+    a.mapped = (flags >> 1) & 1;
     const int g = (int)std::min<int64_t>(grid > 0 ? std::min<int64_t>(grid, rows) : rows, INT32_MAX);
     hipError_t e;
     switch (nin) {
-    case 1: e = launch_rows<1>(a, vpt, block, g, stream); break;
-    case 2: e = launch_rows<2>(a, vpt, block, g, stream); break;
-    case 3: e = launch_rows<3>(a, vpt, block, g, stream); break;
-    case 4: e = launch_rows<4>(a, vpt, block, g, stream); break;
-    case 5: e = launch_rows<5>(a, vpt, block, g, stream); break;
-    case 6: e = launch_rows<6>(a, vpt, block, g, stream); break;
-    case 7: e = launch_rows<7>(a, vpt, block, g, stream); break;
-    case 8: e = launch_rows<8>(a, vpt, block, g, stream); break;
-    default: e = launch_rows<9>(a, vpt, block, g, stream); break;
+    case 1: e = launch_rows<1>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
+    case 2: e = launch_rows<2>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
+    case 3: e = launch_rows<3>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
+    case 4: e = launch_rows<4>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
+    case 5: e = launch_rows<5>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
+    case 6: e = launch_rows<6>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
+    case 7: e = launch_rows<7>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
+    case 8: e = launch_rows<8>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
+    default: e = launch_rows<9>(a, vpt, block, g, (size_t)lds_bytes, stream); break;
     }
     return e == hipSuccess ? 0 : -4;
 }

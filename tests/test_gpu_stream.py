@@ -35,19 +35,23 @@ def test_chunk_probe_writes_exactly_its_range(read_bytes, write_bytes, rv, wv, b
     assert not bool((v == 0xA5).all(dim=1).any())
 
 
-@pytest.mark.parametrize("rows,nin,row_bytes,outs,block,vpt,grid", [
-    (1, 1, 16, [16, 4], 64, 1, 0),
-    (300, 2, 16384, [16384, 8192, 4], 512, 2, 0),           # the residual FP8 layout (bf16 8192 wide)
-    (257, 1, 14336, [3584, 448], 256, 4, 64),               # the FP4 layout, a strided grid
-    (33, 9, 8192, [8192, 4096, 4], 512, 1, 0),              # eight summed inputs and the residual
-    (5, 2, 32768, [32768, 8192, 4], 1024, 2, 3),
+@pytest.mark.parametrize("rows,nin,row_bytes,outs,block,vpt,grid,phased,lds", [
+    (1, 1, 16, [16, 4], 64, 1, 0, 0, 0),
+    (300, 2, 16384, [16384, 8192, 4], 512, 2, 0, 3, 65536),  # the residual FP8 layout (bf16 8192 wide), phased, mapped
+    (257, 1, 14336, [3584, 448], 256, 4, 64, 2, 40960),      # the FP4 layout (4-byte code pieces), a strided grid
+    (33, 9, 8192, [8192, 4096, 4], 512, 1, 0, 1, 0),         # eight summed inputs and the residual
+    (5, 2, 32768, [32768, 8192, 4], 1024, 2, 3, 3, 54272),   # fp32 rows: 4-byte code pieces
+    (7, 1, 16384, [16384, 4096, 4], 256, 4, 0, 2, 0),
 ])
-def test_row_probe_writes_exactly_its_rows(rows, nin, row_bytes, outs, block, vpt, grid):
-    say(f"[row probe] rows {rows} nin {nin} row {row_bytes} outs {outs} block {block} vpt {vpt} grid {grid}")
+def test_row_probe_writes_exactly_its_rows(rows, nin, row_bytes, outs, block, vpt, grid, phased, lds):
+    """phased carries both flag bits: 1 = barrier after the first output, 2 = mapped pieces."""
+    say(f"[row probe] rows {rows} nin {nin} row {row_bytes} outs {outs} block {block} vpt {vpt} grid {grid} "
+        f"phased {phased} lds {lds}")
     ins = [torch.full((rows * row_bytes + GUARD,), 3 + i, dtype=torch.uint8, device=DEV) for i in range(nin)]
     ous = [torch.full((rows * b + GUARD,), 0xA5, dtype=torch.uint8, device=DEV) for b in outs]
     before = [t.clone() for t in ins]
-    probe.Rows(rows, ins, row_bytes, ous, outs, block=block, vpt=vpt, grid=grid)()
+    probe.Rows(rows, ins, row_bytes, ous, outs, block=block, vpt=vpt, grid=grid, phased=bool(phased & 1),
+               mapped=bool(phased & 2), lds_bytes=lds)()
     torch.cuda.synchronize()
     for t, b in zip(ins, before):
         assert torch.equal(t, b)

@@ -30,11 +30,11 @@ def test_row_probe_rejections():
     L = probe.lib()
     I64 = ctypes.c_int64
 
-    def call(rows=4, ins=(P(0),), row=1024, outs=(P(1 << 20),), ob=(512,), block=64, vpt=1, grid=0):
+    def call(rows=4, ins=(P(0),), row=1024, outs=(P(1 << 20),), ob=(512,), block=64, vpt=1, grid=0, phased=0, lds=0):
         ia = (ctypes.c_void_p * len(ins))(*ins)
         oa = (ctypes.c_void_p * len(outs))(*outs)
         ba = (I64 * len(ob))(*ob)
-        return L.rmsq_probe_rows(rows, len(ins), ia, row, len(outs), oa, ba, block, vpt, grid, None)
+        return L.rmsq_probe_rows(rows, len(ins), ia, row, len(outs), oa, ba, block, vpt, grid, phased, lds, None)
 
     assert call(rows=-1) == RANGE and call(row=1000) == RANGE and call(row=0) == RANGE
     assert call(ins=(ctypes.c_void_p(0),)) == NULL and call(outs=(ctypes.c_void_p(0),)) == NULL
@@ -45,4 +45,5 @@ def test_row_probe_rejections():
     assert call(ins=(P(0),) * 10) == RANGE and call(outs=(P(1 << 20),) * 4, ob=(16,) * 4) == RANGE
     assert call(ob=(2048,)) == RANGE                   # a vector output wider than the input row
     assert call(ob=(6,)) == RANGE and call(ob=(260,)) == RANGE  # not a multiple of 4; more than 4 x block
-    assert call(rows=0) == 0                           # nothing to do: no launch
+    assert call(lds=-1) == RANGE and call(lds=64 * 1024 + 1) == RANGE and call(phased=4) == RANGE
+    assert call(rows=0) == 0 and call(rows=0, phased=3, lds=65536) == 0  # nothing to do: no launch
