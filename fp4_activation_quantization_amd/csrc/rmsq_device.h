@@ -26,6 +26,16 @@ __device__ __forceinline__ uint4 load_stream(const void* base, int64_t i16) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + i16);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same load from base + byte_off where base is the same in every active
+// lane of the wavefront: base goes to scalar registers and the lanes add one
+// 32-bit offset, so several rows can share a lane's offset register.
+__device__ __forceinline__ uint4 load_stream_uniform(const void* base, uint32_t byte_off) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(u) + byte_off));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void store_stream(void* base, int64_t i16, const uint4& v) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(base) + i16);

@@ -78,6 +78,15 @@ __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
     __shared__ double red_sum[2][16];
     __shared__ uint64_t red_max[2][16];
 
+    // one vector per lane: the input buffers' bases, read from the kernel
+    // arguments once (the other forms read them per row, which keeps fewer
+    // registers live)
+    const char* in_base[VPT == 1 ? kMaxSumInputs : 1];
+    if constexpr (VPT == 1) {
+#pragma unroll
+        for (int j = 0; j < kMaxSumInputs; ++j) in_base[j] = static_cast<const char*>(sa.inputs[j < nin ? j : 0]);
+    }
+
     int parity = 0;
     for (int64_t row0 = (int64_t)blockIdx.x * rpb; row0 < a.rows; row0 += (int64_t)gridDim.x * rpb) {
         const int64_t row = row0 + slot;
@@ -86,6 +95,7 @@ __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
         float t[T32 ? VPT : 1][EPV];   // s * g' (exact in fp32)
         uint4 sv[VPT];                 // the row s (packed); held across the barrier by the other forms
         uint4 gp[T32 ? 1 : VPT];       // packed gamma (the other forms)
+        uint4 g1 = make_uint4(0, 0, 0, 0);  // gamma, loaded with the row at one vector per lane
         double ssq0 = 0.0, ssq1 = 0.0;
         float amax32 = 0.0f;
         double amax64 = 0.0;
@@ -95,9 +105,39 @@ __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
             // GRP at a time (8 up to 2 vectors per lane, 4 at 4, which keeps
             // the registers bounded), summed in fp64 and rounded once; every
             // load of the row comes before any store (residual_out may be
-            // residual)
+            // residual).  At one vector per lane every load of the vector --
+            // residual, inputs, gamma -- is issued before the first is used
+            // (1.3% faster on 8 inputs of 4096 bf16 elements than waiting for
+            // the residual first; at 2 and 4 vectors per lane the same order
+            // spills registers).
+            if constexpr (VPT == 1) {
+                sv[0] = make_uint4(0, 0, 0, 0);
+                if (live(0)) {
+                    const uint32_t voff = (uint32_t)lt * 16u;
+                    uint4 iv[kMaxSumInputs];
+                    const uint4 rk = load_stream_uniform(static_cast<const char*>(a.residual) + off, voff);
 #pragma unroll
-            for (int k = 0; k < VPT; ++k) {
+                    for (int j = 0; j < kMaxSumInputs; ++j)
+                        if (j < nin) iv[j] = load_stream_uniform(in_base[j] + off, voff);
+                    g1 = reinterpret_cast<const uint4*>(a.gamma)[lt];
+                    float f[EPV];
+                    double acc[EPV];
+                    V::unpack(rk, f);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[e] = (double)f[e];
+#pragma unroll
+                    for (int j = 0; j < kMaxSumInputs; ++j) {
+                        if (j < nin) {
+                            V::unpack(iv[j], f);
+#pragma unroll
+                            for (int e = 0; e < EPV; ++e) acc[e] += (double)f[e];
+                        }
+                    }
+                    sv[0] = round_sum<InT>(acc);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < (VPT == 1 ? 0 : VPT); ++k) {
                 sv[k] = make_uint4(0, 0, 0, 0);
                 if (!live(k)) continue;
                 const int d = lt + k * T;
@@ -128,7 +168,9 @@ __global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
                 if (live(k)) store_stream(ro, lt + k * T, sv[k]);
                 // gamma with the row (L2 hits)
                 float s[EPV], g[EPV];
-                const uint4 gv = live(k) ? reinterpret_cast<const uint4*>(a.gamma)[lt + k * T] : make_uint4(0, 0, 0, 0);
+                const uint4 gv = VPT == 1 ? g1
+                                 : live(k) ? reinterpret_cast<const uint4*>(a.gamma)[lt + k * T]
+                                           : make_uint4(0, 0, 0, 0);
                 V::unpack(gv, g);
                 V::unpack(sv[k], s);
                 sumsq64<EPV>(ssq0, ssq1, s);

@@ -70,7 +70,9 @@ struct GatedProduct {
 // type InT produced by `src`; outputs as rmsnorm_fp8: out [rows, hidden]
 // codes (16-byte aligned, rows adjacent), scales [rows] of scales_dtype.
 // hidden must be a multiple of 8 (16-bit) or 4 (fp32) and at most 4096
-// vectors; gamma [hidden] of InT, 16-byte aligned.  Returns an RMSQ_* status;
+// vectors; gamma [hidden] of InT, 16-byte aligned; out, scales and gamma
+// must not overlap (RMSQ_ERR_ALIAS), nor may what the source reads overlap
+// out or scales (not checked).  Returns an RMSQ_* status;
 // every check happens before the launch (RMSQ_ERR_LAUNCH after a failed one).
 // Enqueues one kernel on `stream`; the launch shape is rmsq_query_shape's
 // (path 0), so rmsq_set_tuning applies.
@@ -89,9 +91,14 @@ int rmsnorm_fp8_from(const Src& src, int64_t rows, int64_t hidden, const void* g
     if (rows == 0) return RMSQ_OK;
     if (!gamma || !out || !scales) return RMSQ_ERR_NULL;
     const int ssz = scales_dtype == RMSQ_F32 ? 4 : 2;
-    if (reinterpret_cast<uintptr_t>(gamma) % 16 || reinterpret_cast<uintptr_t>(out) % 16 ||
-        reinterpret_cast<uintptr_t>(scales) % ssz)
-        return RMSQ_ERR_ALIGN;
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out), sc = reinterpret_cast<uintptr_t>(scales),
+                    g = reinterpret_cast<uintptr_t>(gamma);
+    if (g % 16 || o % 16 || sc % ssz) return RMSQ_ERR_ALIGN;
+    // the outputs overlap neither each other nor gamma (what the source reads
+    // is the caller's to keep apart from them)
+    const auto overlap = [](uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) { return a < b + bn && b < a + an; };
+    const uintptr_t on = (uintptr_t)(rows * hidden), sn = (uintptr_t)(rows * ssz), gn = (uintptr_t)(hidden * esz);
+    if (overlap(o, on, sc, sn) || overlap(o, on, g, gn) || overlap(sc, sn, g, gn)) return RMSQ_ERR_ALIAS;
     Shape s{};
     if (int rc = rmsq_query_shape(rows, hidden, InTypeCode<InT>::value, 0, &s.waves, &s.vpt, &s.rpb)) return rc;
     s.grid = 0;

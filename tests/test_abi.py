@@ -539,3 +539,40 @@ def test_wide_rows_limits_and_shapes():
                 rq.query_shape(3, 65536, bf)
     finally:
         rq.set_tuning(1, 1, 0)
+
+
+def user_fp8(rows=4, hidden=4096, dt=rq.BF16, a=None, g=None, eps=1e-6, ub=1200.0, fmt=rq.E4M3FN, out=None,
+             sdt=rq.F32, sc=None):
+    """rmsq_fused.hpp's template, instantiated by a caller's translation unit
+    (tests/cpp_source/user_source.hip); its checks, like the library's, run
+    before any HIP call."""
+    path = os.path.join(ROOT, "tests", "cpp_source", "libuser_source.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: __graft_entry__.build() builds it")
+    L = ctypes.CDLL(path)
+    Pt, I64, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.user_abs_rmsnorm_fp8.argtypes = [I64, I64, I, Pt, Pt, F, F, F, I, Pt, I, Pt, Pt]
+    L.user_abs_rmsnorm_fp8.restype = I
+    a = P(0) if a is None else a
+    g = P(1) if g is None else g
+    out = P(2) if out is None else out
+    sc = P(3) if sc is None else sc
+    return L.user_abs_rmsnorm_fp8(rows, hidden, dt, a, g, eps, 0.0, ub, fmt, out, sdt, sc, None)
+
+
+def test_public_template_argument_errors():
+    assert user_fp8(sdt=5) == DTYPE and user_fp8(fmt=3) == DTYPE
+    assert user_fp8(rows=-1) == SHAPE and user_fp8(hidden=4100) == SHAPE
+    assert user_fp8(eps=-1.0) == VALUE and user_fp8(ub=0.0) == VALUE
+    assert user_fp8(hidden=8 * 4096 + 8) == UNSUP
+    z = ctypes.c_void_p(0)
+    assert user_fp8(rows=0, g=z, out=z, sc=z) == OK  # nothing to do
+    assert user_fp8(g=z) == NULL and user_fp8(out=z) == NULL and user_fp8(sc=z) == NULL
+    near = lambda i, k: ctypes.c_void_p(BASE + i * MB + k)  # noqa: E731
+    assert user_fp8(g=near(1, 8)) == ALIGN and user_fp8(out=near(2, 8)) == ALIGN
+    assert user_fp8(sc=near(3, 2)) == ALIGN
+    assert user_fp8(sc=near(2, 16)) == ALIAS     # scales inside the codes
+    assert user_fp8(out=near(1, 0)) == ALIAS     # codes over gamma
+    assert user_fp8(sc=near(1, 64)) == ALIAS     # scales inside gamma
+    assert user_fp8(sc=near(2, 4 * 4096)) == UNSUP   # scales right after the last code: adjacent, no overlap
+    assert user_fp8() == UNSUP
