@@ -18,7 +18,8 @@
 // lane l owns the 16-byte vectors l, l + 1024, ...  Pass 1 forms s (x, or
 // x + residual rounded once to the input type and stored to residual_out)
 // and accumulates sum(s^2) and, for FP8, max |s * g'| (g' = gamma +
-// weight_offset, read from L2); the block reduces both.  Pass 2 forms
+// weight_offset, read from L2 by the LDS form and from an LDS copy by the
+// register form); the block reduces both.  Pass 2 forms
 // s * g' again (the same products) and quantizes: FP8 with the
 // row's scale, FP4 per block, whose lanes are adjacent as in the FP4 kernel.
 // HBM traffic is that of the register kernels: every input element read
@@ -29,7 +30,11 @@
 //    158 KiB, read in chunks of U vectors per lane;
 //  - registers (wide_reg_kernel): NV packed vectors per lane, the raw
 //    16-byte words at 4 VGPRs each (NV = 10, 40 VGPRs, at the widest row),
-//    every load of the row in flight at once.
+//    every load of the row in flight at once; the LDS left free holds
+//    gamma, copied once per block, so the two passes' gamma reads (twice
+//    the row's bytes for 16-bit rows) stay off the L1/L2 path that carries
+//    the row (measured: 6-20% faster than reading gamma from L2 on rows of
+//    40000-65536 elements, outputs identical).
 // Measured on MI355X (A/B in one process, outputs identical): without a
 // residual the register form is 10-28% faster whenever the LDS form leaves
 // room for only one block per CU (rows above ~80 KiB), and 8% slower on
@@ -50,18 +55,19 @@ namespace wide_detail {
 
 // g' = gamma + weight_offset for vector d
 template <typename InT>
-__device__ __forceinline__ void gamma_of(const FusedArgs& a, int d, float (&g)[Vec<InT>::EPV]) {
-    Vec<InT>::unpack(static_cast<const uint4*>(a.gamma)[d], g);
+__device__ __forceinline__ void gamma_of(const FusedArgs& a, const uint4* gam, int d, float (&g)[Vec<InT>::EPV]) {
+    Vec<InT>::unpack(gam[d], g);
 #pragma unroll
     for (int e = 0; e < Vec<InT>::EPV; ++e) g[e] += a.weight_offset;
 }
 
 // t = s * g' for vector d of a row
 template <typename InT>
-__device__ __forceinline__ void product(const FusedArgs& a, int d, const uint4& s, float (&t)[Vec<InT>::EPV]) {
+__device__ __forceinline__ void product(const FusedArgs& a, const uint4* gam, int d, const uint4& s,
+                                        float (&t)[Vec<InT>::EPV]) {
     float g[Vec<InT>::EPV];
     Vec<InT>::unpack(s, t);
-    gamma_of<InT>(a, d, g);
+    gamma_of<InT>(a, gam, d, g);
 #pragma unroll
     for (int e = 0; e < Vec<InT>::EPV; ++e) t[e] *= g[e];
 }
@@ -97,15 +103,15 @@ __device__ __forceinline__ void block_reduce(double& ssq, double& amax, bool wit
 
 // FP8 codes of vector d (s packed) into the row's output
 template <typename InT, bool FNUZ>
-__device__ __forceinline__ void fp8_store(const FusedArgs& a, uint8_t* orow, int d, const uint4& s, const Fp8Row& r,
-                                          bool split) {
+__device__ __forceinline__ void fp8_store(const FusedArgs& a, const uint4* gam, uint8_t* orow, int d, const uint4& s,
+                                          const Fp8Row& r, bool split) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
     float q[EPV];
     const int prod = prod_of<InT>(a);
     if (prod == kProdF32) {
         float t[EPV];
-        product<InT>(a, d, s, t);
+        product<InT>(a, gam, d, s, t);
         if (split) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e) q[e] = fp8_q1(t[e], r);
@@ -116,7 +122,7 @@ __device__ __forceinline__ void fp8_store(const FusedArgs& a, uint8_t* orow, int
     } else {
         float sf[EPV], g[EPV];
         V::unpack(s, sf);
-        V::unpack(static_cast<const uint4*>(a.gamma)[d], g);
+        V::unpack(gam[d], g);
         if (prod == kProdTwo && split) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e) q[e] = fp8_q2(sf[e], g[e], r);
@@ -170,13 +176,14 @@ __device__ __forceinline__ Fp4Row fp4_row(const FusedArgs& a, int64_t row, doubl
 // count are multiples of the lanes per block), and past it (live false)
 // t = 0 and nothing is stored.
 template <typename InT, int BLOCK, bool UE8M0>
-__device__ __forceinline__ void fp4_store(const FusedArgs& a, const Fp4Row& r, int d, bool live, const uint4& s) {
+__device__ __forceinline__ void fp4_store(const FusedArgs& a, const uint4* gam, const Fp4Row& r, int d, bool live,
+                                          const uint4& s) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
     constexpr int LPB = BLOCK / EPV;  // lanes (vectors) per block
     float t[EPV];
     if (live) {
-        product<InT>(a, d, s, t);
+        product<InT>(a, gam, d, s, t);
         if (a.round_product) V::unpack(V::pack(t), t);
     } else {
 #pragma unroll
@@ -212,8 +219,8 @@ __device__ __forceinline__ void fp4_store(const FusedArgs& a, const Fp4Row& r, i
 // and stored to residual_out), its sum of squares (fp64) and, for FP8, its
 // max |s * g'| (exact)
 template <typename InT, bool RESID, bool FP8>
-__device__ __forceinline__ uint4 form_s(const FusedArgs& a, char* ro, int d, const uint4& xv, const uint4& rv,
-                                        double& ssq, double& amax) {
+__device__ __forceinline__ uint4 form_s(const FusedArgs& a, const uint4* gam, char* ro, int d, const uint4& xv,
+                                        const uint4& rv, double& ssq, double& amax) {
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
     uint4 s = xv;
@@ -239,13 +246,13 @@ __device__ __forceinline__ uint4 form_s(const FusedArgs& a, char* ro, int d, con
         ssq += s1;
         if (prod_of<InT>(a) != kProdF32) {
             float g[EPV];
-            V::unpack(static_cast<const uint4*>(a.gamma)[d], g);
+            V::unpack(gam[d], g);
             const double offd = (double)a.weight_offset;
 #pragma unroll
             for (int e = 0; e < EPV; ++e) amax = fmax(amax, abs_prod64(sf[e], g[e], offd));
         } else {
             float t[EPV];
-            product<InT>(a, d, s, t);
+            product<InT>(a, gam, d, s, t);
             amax = fmax(amax, (double)abs_max<EPV>(0.0f, t));
         }
     }
@@ -269,6 +276,7 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
     extern __shared__ uint4 row_s[];  // s of the current row: nvec vectors
     __shared__ double red_sum[16];
     __shared__ uint64_t red_max[16];
+    const uint4* gam = static_cast<const uint4*>(a.gamma);  // from L2
 
     const int tid = threadIdx.x;
     const int nvec = a.nvec;
@@ -296,7 +304,7 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int d = tid + (i * U + u) * T;
-                if (d < nvec) row_s[d] = form_s<InT, RESID, !FP4>(a, ro, d, xv[u], rv[u], ssq, amax);
+                if (d < nvec) row_s[d] = form_s<InT, RESID, !FP4>(a, gam, ro, d, xv[u], rv[u], ssq, amax);
             }
         }
 
@@ -314,7 +322,7 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int d = tid + (i * U + u) * T;
-                    if (d < nvec) fp8_store<InT, FNUZ>(a, orow, d, row_s[d], fr, split);
+                    if (d < nvec) fp8_store<InT, FNUZ>(a, gam, orow, d, row_s[d], fr, split);
                 }
             }
             if (tid == 0) store_scale(a.scales, row, a.scales_dtype, fr.sbits);
@@ -325,7 +333,7 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
                 for (int u = 0; u < U; ++u) {
                     const int d = tid + (i * U + u) * T;
                     const bool live = d < nvec;
-                    fp4_store<InT, BLOCK, UE8M0>(a, r, d, live, live ? row_s[d] : make_uint4(0, 0, 0, 0));
+                    fp4_store<InT, BLOCK, UE8M0>(a, gam, r, d, live, live ? row_s[d] : make_uint4(0, 0, 0, 0));
                 }
             }
         }
@@ -348,9 +356,14 @@ __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
     // reading the set it writes; one barrier per row
     __shared__ double red_sum[2][16];
     __shared__ uint64_t red_max[2][16];
+    // gamma, copied into LDS once per block (nvec vectors): both passes read
+    // it from there instead of from L2
+    extern __shared__ uint4 gam[];
 
     const int tid = threadIdx.x;
     const int nvec = a.nvec;
+    for (int d = tid; d < nvec; d += T) gam[d] = static_cast<const uint4*>(a.gamma)[d];
+    __syncthreads();
     int set = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, set ^= 1) {
         // ---- pass 1: the whole row's loads, then s's sums ----
@@ -365,7 +378,7 @@ __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int d = tid + k * T;
-            if (d < nvec) form_s<InT, false, !FP4>(a, nullptr, d, sv[k], sv[k], ssq, amax);
+            if (d < nvec) form_s<InT, false, !FP4>(a, gam, nullptr, d, sv[k], sv[k], ssq, amax);
         }
         block_reduce(ssq, amax, !FP4, red_sum[set], red_max[set]);
         const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
@@ -378,7 +391,7 @@ __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 const int d = tid + k * T;
-                if (d < nvec) fp8_store<InT, FNUZ>(a, orow, d, sv[k], fr, split);
+                if (d < nvec) fp8_store<InT, FNUZ>(a, gam, orow, d, sv[k], fr, split);
             }
             if (tid == 0) store_scale(a.scales, row, a.scales_dtype, fr.sbits);
         } else {
@@ -386,7 +399,7 @@ __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 const int d = tid + k * T;
-                fp4_store<InT, BLOCK, UE8M0>(a, r, d, d < nvec, sv[k]);
+                fp4_store<InT, BLOCK, UE8M0>(a, gam, r, d, d < nvec, sv[k]);
             }
         }
     }
@@ -418,7 +431,10 @@ hipError_t launch_reg(const FusedArgs& a, int grid_blocks, hipStream_t stream) {
                        : nv <= 8 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 8>)
                        : nv <= 9 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 9>)
                                  : reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 10>);
-    return launch_grid(kern, a, grid_blocks, 0, stream);
+    const size_t lds = (size_t)a.nvec * 16;
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    return launch_grid(kern, a, grid_blocks, lds, stream);
 }
 
 // The LDS row exceeds the default dynamic-LDS limit of a launch: the LDS
