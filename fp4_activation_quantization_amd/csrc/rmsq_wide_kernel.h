@@ -38,10 +38,11 @@
 // Measured on MI355X (A/B in one process, outputs identical): without a
 // residual the register form is 10-28% faster whenever the LDS form leaves
 // room for only one block per CU (rows above ~80 KiB), and 8% slower on
-// rows that let two LDS blocks share a CU; with a residual the LDS form is
-// faster (2-26%: the second input's loads push the register form to spill).
-// The launch takes the register form for rows without a residual on which
-// the occupancy API reports one resident LDS block per CU.
+// rows that let two LDS blocks share a CU; with a residual, whose second
+// input doubles the registers in flight, it is faster only up to 6 or 7
+// vectors per lane (kResidRegMaxNv).  The launch takes the register form
+// where the occupancy API reports one resident LDS block per CU, for rows
+// with a residual only up to kResidRegMaxNv vectors per lane.
 #pragma once
 
 #include "rmsq_device.h"
@@ -343,8 +344,8 @@ __global__ void __launch_bounds__(1024) wide_kernel(const FusedArgs a) {
 }
 
 // s held in registers between the passes: NV vectors per lane (nvec <=
-// NV * 1024), rows without a residual.
-template <typename InT, int OUT, int BLOCK, bool UE8M0, int NV>
+// NV * 1024).
+template <typename InT, bool RESID, int OUT, int BLOCK, bool UE8M0, int NV>
 __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
     using namespace wide_detail;
     constexpr int T = kWideThreads;
@@ -367,18 +368,23 @@ __global__ void __launch_bounds__(1024) wide_reg_kernel(const FusedArgs a) {
     int set = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, set ^= 1) {
         // ---- pass 1: the whole row's loads, then s's sums ----
+        // every load of the row comes before any store (residual_out may be
+        // x or residual itself; the lane that reads a vector writes it)
         const char* xr = static_cast<const char*>(a.x) + row * a.x_stride;
-        uint4 sv[NV];
+        const char* rr = RESID ? static_cast<const char*>(a.residual) + row * a.residual_stride : nullptr;
+        char* ro = RESID ? static_cast<char*>(a.residual_out) + row * a.residual_out_stride : nullptr;
+        uint4 sv[NV], rv[RESID ? NV : 1];
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int d = tid + k * T;
             sv[k] = d < nvec ? load_stream(xr, d) : make_uint4(0, 0, 0, 0);
+            if constexpr (RESID) rv[k] = d < nvec ? load_stream(rr, d) : make_uint4(0, 0, 0, 0);
         }
         double ssq = 0.0, amax = 0.0;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int d = tid + k * T;
-            if (d < nvec) form_s<InT, false, !FP4>(a, gam, nullptr, d, sv[k], sv[k], ssq, amax);
+            if (d < nvec) sv[k] = form_s<InT, RESID, !FP4>(a, gam, ro, d, sv[k], rv[RESID ? k : 0], ssq, amax);
         }
         block_reduce(ssq, amax, !FP4, red_sum[set], red_max[set]);
         const double rstd = rsqrt_refined(ssq * a.inv_hidden + (double)a.eps);
@@ -418,19 +424,34 @@ inline hipError_t launch_grid(const void* kern, const FusedArgs& a, int grid_blo
     return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kWideThreads), args, lds, stream);
 }
 
-template <typename InT, int OUT, int BLOCK, bool UE8M0>
+// The vectors per lane up to which the register form takes rows with a
+// residual (it loads two inputs per vector): measured against the LDS form
+// (A/B in one process), 16-bit FP8 rows were 5-9% faster at 5-7 vectors per
+// lane and 5% slower at 10, FP4 rows 2-4% faster at 5-6 and 3% slower at 8,
+// fp32 FP8 rows 3% faster at 5, even at 6 and 2-6% slower at 7-10.
+template <typename InT, int OUT>
+constexpr int kResidRegMaxNv = (Vec<InT>::BYTES == 2 && OUT != kWideFp4) ? 7 : 6;
+
+template <typename InT, bool RESID, int OUT, int BLOCK, bool UE8M0>
 hipError_t launch_reg(const FusedArgs& a, int grid_blocks, hipStream_t stream) {
     // NV = the vectors per lane the row needs (rows here exceed 4096
     // vectors, so 5 or more), each compiled: rounding NV up costs the
     // registers of the idle slots (measured: 9000-vector rows 13% slower at
-    // NV = 10 than at 9)
+    // NV = 10 than at 9); with a residual, NV <= kResidRegMaxNv
     const int nv = (a.nvec + kWideThreads - 1) / kWideThreads;
-    const void* kern = nv <= 5   ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 5>)
-                       : nv <= 6 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 6>)
-                       : nv <= 7 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 7>)
-                       : nv <= 8 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 8>)
-                       : nv <= 9 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 9>)
-                                 : reinterpret_cast<const void*>(wide_reg_kernel<InT, OUT, BLOCK, UE8M0, 10>);
+    const void* kern;
+    if constexpr (RESID) {
+        kern = nv <= 5   ? reinterpret_cast<const void*>(wide_reg_kernel<InT, true, OUT, BLOCK, UE8M0, 5>)
+               : nv <= 6 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, true, OUT, BLOCK, UE8M0, 6>)
+                         : reinterpret_cast<const void*>(wide_reg_kernel<InT, true, OUT, BLOCK, UE8M0, 7>);
+    } else {
+        kern = nv <= 5   ? reinterpret_cast<const void*>(wide_reg_kernel<InT, false, OUT, BLOCK, UE8M0, 5>)
+               : nv <= 6 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, false, OUT, BLOCK, UE8M0, 6>)
+               : nv <= 7 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, false, OUT, BLOCK, UE8M0, 7>)
+               : nv <= 8 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, false, OUT, BLOCK, UE8M0, 8>)
+               : nv <= 9 ? reinterpret_cast<const void*>(wide_reg_kernel<InT, false, OUT, BLOCK, UE8M0, 9>)
+                         : reinterpret_cast<const void*>(wide_reg_kernel<InT, false, OUT, BLOCK, UE8M0, 10>);
+    }
     const size_t lds = (size_t)a.nvec * 16;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -445,8 +466,10 @@ hipError_t launch(const FusedArgs& a, int grid_blocks, hipStream_t stream) {
     const size_t lds = (size_t)a.nvec * 16;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if constexpr (!RESID) {
-        if (blocks_per_cu(kern, kWideThreads, lds) < 2) return launch_reg<InT, OUT, BLOCK, UE8M0>(a, grid_blocks, stream);
+    if (blocks_per_cu(kern, kWideThreads, lds) < 2) {
+        const int nv = (a.nvec + kWideThreads - 1) / kWideThreads;
+        if (!RESID || nv <= kResidRegMaxNv<InT, OUT>)
+            return launch_reg<InT, RESID, OUT, BLOCK, UE8M0>(a, grid_blocks, stream);
     }
     return launch_grid(kern, a, grid_blocks, lds, stream);
 }

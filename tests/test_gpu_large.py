@@ -105,13 +105,14 @@ def test_residual_fp8_past_4gib():
     free()
 
 
-@pytest.mark.parametrize("resid", [False, True], ids=["registers", "lds"])
-def test_wide_fp8_past_4gib(resid):
-    """65536-wide rows (128 KiB each): held in registers without a residual,
-    staged in LDS with one."""
-    hidden = 65536
+@pytest.mark.parametrize("resid,hidden", [(False, 65536), (True, 65536), (True, 49152)],
+                         ids=["registers", "lds", "registers-residual"])
+def test_wide_fp8_past_4gib(resid, hidden):
+    """Wide rows: 65536 (128 KiB each) held in registers without a residual
+    and staged in LDS with one (8 vectors per lane); 49152 with a residual
+    held in registers (6 vectors per lane)."""
     rows = rows_past_4gib(hidden, 2, 37)
-    x = Tiled(rows, hidden, "bf16", 40, tag_cols=(3, 50000))
+    x = Tiled(rows, hidden, "bf16", 40, tag_cols=(3, hidden - 15536))  # column 50000 of a 65536 row
     r = Tiled(rows, hidden, "bf16", 41, tag_cols=(hidden - 1, 1234)) if resid else None
     g = torch.from_numpy(np.random.default_rng(42).uniform(0.5, 1.5, hidden)).to(torch.bfloat16)
     say(f"[large] wide FP8 bf16 {rows}x{hidden} residual={resid} ({rows * hidden * 2 / 2**30:.2f} GiB per tensor)")

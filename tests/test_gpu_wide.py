@@ -1,8 +1,9 @@
 """GPU: rows wider than the register-resident kernels hold (more than 4096
 16-byte vectors: 32768 16-bit or 16384 fp32 elements) run the wide-row
 kernels, up to 10112 vectors (80896 16-bit or 40448 fp32 elements): rows
-with a residual, and rows of up to ~80 KiB, stage the row in LDS; wider rows
-without a residual hold it in registers (5 to 10 vectors per lane).
+with a residual above 7 (16-bit FP8) or 6 (FP4, fp32) vectors per lane, and
+any row whose LDS form fits two blocks on a CU, stage the row in LDS; the
+others hold it in registers (5 to 10 vectors per lane, gamma in LDS).
 Against the oracle: FP8 (both formats, every scale type, with and without
 the residual, in place), FP4 (every block size, scale format and layout,
 with and without the residual), row strides, each register width with a
@@ -120,8 +121,8 @@ def test_fp4_rows_held_in_registers(block, fmt, swz):
 @pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "ue8m0")])
 def test_fp4_wide_round_product_and_offset(block, fmt):
     """The FlashInfer page's 16-bit x * w product (round_product) and a
-    weight offset on wide rows: registers (no residual, 65536), LDS (with a
-    residual, and f16 36000 without one: two LDS blocks fit a CU)."""
+    weight offset on wide rows: registers (no residual: 65536, f16 36000),
+    LDS (with a residual at 65536: 8 vectors per lane)."""
     for dt, rows, hidden, resid, off in (("bf16", 37, 65536, False, 0.0), ("bf16", 37, 65536, True, 1.0),
                                          ("f16", 21, 36000, False, 1.0)):
         op = "residual_rmsnorm_fp4" if resid else "rmsnorm_fp4"
@@ -132,6 +133,38 @@ def test_fp4_wide_round_product_and_offset(block, fmt):
             inp["gamma"] = (inp["gamma"].double() - 1.0).to(TD[dt])  # g' = gamma + 1 stays near 1
         say(f"[wide fp4 round_product] {op} {dt} {rows}x{hidden} block={block} {fmt} offset={off}")
         check_fp4(w, inp, _gs(inp, w), label=f"wide round_product {op} {dt} {rows}x{hidden} {block} {fmt}")
+
+
+# rows with a residual held in registers: 16-bit FP8 up to 7 vectors per
+# lane, FP4 and fp32 up to 6 (7125, 5632 and 6000 vectors)
+RESID_REG_ROWS = [("bf16", 57000, 7125), ("f16", 45056, 5632), ("f32", 24000, 6000)]
+
+
+@pytest.mark.parametrize("dt,hidden,nvec", RESID_REG_ROWS, ids=[f"{d}-{h}" for d, h, _ in RESID_REG_ROWS])
+def test_fp8_residual_rows_held_in_registers(dt, hidden, nvec):
+    assert hidden * {"bf16": 2, "f16": 2, "f32": 4}[dt] == nvec * 16
+    for rows, grid in ((37, 0), (300, 0), (37, 3)):
+        rq.set_tuning(0, 0, grid)  # 300 rows or 3 blocks: blocks loop over rows
+        w = workloads.Workload("wide", "residual_rmsnorm_fp8", rows, hidden, dt, 95, eps=1e-6)
+        inp = _inputs(rows, hidden, dt, seed=hidden + rows + grid, resid=True)
+        say(f"[wide fp8 registers, residual] {dt} {rows}x{hidden} grid={grid or 'auto'}")
+        check_fp8(w, inp, label=f"wide registers residual {dt} {rows}x{hidden} grid={grid}")
+    rq.set_tuning(0, 0, 0)
+    say(f"[wide fp8 registers, residual] {dt} residual_out over x, then over residual")
+    check_fp8(w, inp, in_place="x", label="wide registers in place over x")
+    check_fp8(w, inp, in_place="residual", label="wide registers in place over residual")
+
+
+@pytest.mark.parametrize("block,fmt,swz", [(16, "e4m3", False), (32, "ue8m0", True)])
+def test_fp4_residual_rows_held_in_registers(block, fmt, swz):
+    for dt, rows, hidden, grid in (("bf16", 300, 45056, 0), ("bf16", 37, 49152, 3), ("f32", 37, 24000, 0)):
+        rq.set_tuning(0, 0, grid)
+        w = workloads.Workload("wide", "residual_rmsnorm_fp4", rows, hidden, dt, 95, eps=1e-6, fp4_block=block,
+                               fp4_scale=fmt, fp4_swizzled=swz)
+        inp = _inputs(rows, hidden, dt, seed=hidden + block + rows, resid=True)
+        say(f"[wide fp4 registers, residual] {dt} {rows}x{hidden} block={block} {fmt} swizzled={swz} "
+            f"grid={grid or 'auto'}")
+        check_fp4(w, inp, _gs(inp, w), label=f"wide registers residual {dt} {rows}x{hidden} {block} {fmt}")
 
 
 def test_fp8_wide_strided_rows():
