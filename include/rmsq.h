@@ -91,9 +91,10 @@ enum {
  *                    row held in registers, up to 32768 16-bit / 16384 fp32
  *                    elements; wider rows up to 80896 / 40448 elements on the
  *                    wide-row kernels (one 1024-thread block per row, the
- *                    row staged in LDS, or held in registers for rows
- *                    without a residual that leave LDS room for only one
- *                    block per CU; the same results);
+ *                    row staged in LDS, or held in registers with gamma
+ *                    copied to LDS where LDS leaves room for only one
+ *                    block per CU -- rows with a residual only up to 7
+ *                    (16-bit FP8) or 6 vectors per lane; the same results);
  *                  - otherwise, rows that all sit at x's offset from the
  *                    16-byte grid (residual, residual_out: the same address
  *                    modulo 16 and row strides congruent modulo 16 bytes;
