@@ -55,7 +55,9 @@ def run_and_check(ins, r, g, dt, label, out_fmt="e4m3fn", sdt="f32", off=0.0, in
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
 def test_inputs_sum_matches_oracle(dt, n):
-    for rows, hidden in ((1, 512), (67, 4096), (300, 1032)):
+    # (37, 512): four rows per block at one vector per lane, the last block
+    # partly filled; (260, 4096): the large-batch shape, one vector per lane
+    for rows, hidden in ((1, 512), (37, 512), (67, 4096), (260, 4096), (300, 1032)):
         ins, r, g = _inputs(n, rows, hidden, dt, seed=n * 100 + rows)
         say(f"[allreduce] {dt} n={n} {rows}x{hidden}")
         run_and_check(ins, r, g, dt, f"{dt} n={n} {rows}x{hidden}")
