@@ -560,7 +560,18 @@ def user_fp8(rows=4, hidden=4096, dt=rq.BF16, a=None, g=None, eps=1e-6, ub=1200.
     return L.user_abs_rmsnorm_fp8(rows, hidden, dt, a, g, eps, 0.0, ub, fmt, out, sdt, sc, None)
 
 
-def test_public_template_argument_errors():
+@pytest.fixture
+def caller_links_no_launch():
+    """The caller's library resolves rmsq_query_shape from the librmsq.so it
+    was linked against, which is not the library the tests load when they run
+    against a sanitized build: force the one-wave shape there too."""
+    base = ctypes.CDLL(os.path.join(ROOT, "fp4_activation_quantization_amd", "librmsq.so"))
+    base.rmsq_set_tuning(1, 1, 0)
+    yield
+    base.rmsq_set_tuning(0, 0, 0)
+
+
+def test_public_template_argument_errors(caller_links_no_launch):
     assert user_fp8(sdt=5) == DTYPE and user_fp8(fmt=3) == DTYPE
     assert user_fp8(rows=-1) == SHAPE and user_fp8(hidden=4100) == SHAPE
     assert user_fp8(eps=-1.0) == VALUE and user_fp8(ub=0.0) == VALUE
