@@ -131,12 +131,14 @@ def test_residual_fp4_and_summed_inputs():
                    run_sum, outs8)
 
 
-@pytest.mark.parametrize("resid", [False, True], ids=["registers", "lds"])
-def test_wide_rows(resid):
-    """Rows above 4096 vectors: without a residual the row is held in
-    registers, with one it is staged in LDS (the launch raises the kernel's
-    dynamic-LDS limit and queries occupancy, host calls made during capture)."""
-    rows, hidden = 40, 65536
+@pytest.mark.parametrize("resid,hidden", [(False, 65536), (True, 65536), (True, 49152)],
+                         ids=["registers", "lds", "registers-residual"])
+def test_wide_rows(resid, hidden):
+    """Rows above 4096 vectors: held in registers with gamma in LDS (65536
+    without a residual, 49152 with one) or staged in LDS (65536 with a
+    residual); every launch raises the kernel's dynamic-LDS limit and queries
+    occupancy, host calls made during capture."""
+    rows = 40
     x = _rand((rows, hidden), torch.bfloat16, 13)
     r = _rand((rows, hidden), torch.bfloat16, 14) if resid else None
     g = _rand((hidden,), torch.bfloat16, 15)
