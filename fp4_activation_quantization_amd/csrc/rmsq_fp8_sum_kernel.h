@@ -50,8 +50,17 @@ __device__ __forceinline__ uint4 round_sum(const double (&acc)[Vec<InT>::EPV]) {
     return V::pack(f);
 }
 
+// Waves per SIMD the compiler must leave room for: six for the forms that
+// fit 80 VGPRs without spilling (one vector per lane, one row per block, no
+// fp64 product, e4m3fn), so that three 8-wave blocks share a CU instead of
+// two (8 inputs of 8192 x 4096 bf16: 118.5 -> 115.7 us, A/B in one process,
+// outputs identical); the other forms would spill at that budget.
+template <int VPT, bool ONE_ROW, int PROD, bool FNUZ>
+constexpr int kSumMinWaves = (VPT == 1 && ONE_ROW && PROD != kProdF64 && !FNUZ) ? 6 : 1;
+
 template <typename InT, bool FNUZ, int VPT, bool EXACT, bool ONE_ROW, int PROD>
-__global__ void __launch_bounds__(1024) fp8_sum_kernel(const SumArgs sa) {
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kSumMinWaves<VPT, ONE_ROW, PROD, FNUZ>)))
+fp8_sum_kernel(const SumArgs sa) {
     const FusedArgs& a = sa.a;
     using V = Vec<InT>;
     constexpr int EPV = V::EPV;
