@@ -190,6 +190,28 @@ def test_fp8_wide_strided_rows():
     say(f"  parity {w.op} strided: {rep}")
 
 
+def test_fp4_wide_strided_rows_with_residual():
+    """Strided 45056-wide rows with a residual through the FP4 entry point
+    (held in registers, 6 vectors per lane): byte-identical to the contiguous
+    call, nothing written outside the row views."""
+    rows, hidden, stride = 21, 45056, 46080
+    inp = _inputs(rows, hidden, "bf16", seed=12, resid=True)
+    buf = torch.zeros((rows, stride), dtype=torch.bfloat16, device=DEV)
+    rbuf = torch.zeros_like(buf)
+    obuf = torch.full((rows, stride // 2), 0xA5, dtype=torch.uint8, device=DEV)
+    x, r, out = buf[:, :hidden], rbuf[:, :hidden], obuf[:, :hidden // 2]
+    x.copy_(inp["x"].to(DEV))
+    r.copy_(inp["residual"].to(DEV))
+    g = inp["gamma"].to(DEV)
+    gs = torch.tensor([30.0], dtype=torch.float32, device=DEV)
+    say("[wide fp4 registers, residual] strided rows")
+    c_p, c_s, c_ro = rq.residual_rmsnorm_fp4quant(x.contiguous(), r.contiguous(), g, global_scale=gs)
+    s_p, s_s, s_ro = rq.rmsnorm_fp4quant_strided(x, g, residual=r, global_scale=gs, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(s_p, c_p) and torch.equal(s_s, c_s) and torch.equal(s_ro, c_ro)
+    assert bool((obuf[:, hidden // 2:] == 0xA5).all()), "codes written outside the row views"
+
+
 def test_fp8_strided_rows_held_in_registers():
     rows, hidden, stride = 21, 65536, 66560
     inp = _inputs(rows, hidden, "bf16", seed=10, resid=False)
