@@ -155,15 +155,17 @@ def test_fp8_residual_rows_held_in_registers(dt, hidden, nvec):
     check_fp8(w, inp, in_place="residual", label="wide registers in place over residual")
 
 
-@pytest.mark.parametrize("block,fmt,swz", [(16, "e4m3", False), (32, "ue8m0", True)])
-def test_fp4_residual_rows_held_in_registers(block, fmt, swz):
+@pytest.mark.parametrize("block,fmt,swz,rp", [(16, "e4m3", False, False), (32, "ue8m0", True, False),
+                                              (16, "e4m3", True, True)])
+def test_fp4_residual_rows_held_in_registers(block, fmt, swz, rp):
+    """rp: the FlashInfer page's 16-bit x * w product (round_product)."""
     for dt, rows, hidden, grid in (("bf16", 300, 45056, 0), ("bf16", 37, 49152, 3), ("f32", 37, 24000, 0)):
         rq.set_tuning(0, 0, grid)
         w = workloads.Workload("wide", "residual_rmsnorm_fp4", rows, hidden, dt, 95, eps=1e-6, fp4_block=block,
-                               fp4_scale=fmt, fp4_swizzled=swz)
+                               fp4_scale=fmt, fp4_swizzled=swz, fp4_round_product=rp)
         inp = _inputs(rows, hidden, dt, seed=hidden + block + rows, resid=True)
         say(f"[wide fp4 registers, residual] {dt} {rows}x{hidden} block={block} {fmt} swizzled={swz} "
-            f"grid={grid or 'auto'}")
+            f"round_product={rp} grid={grid or 'auto'}")
         check_fp4(w, inp, _gs(inp, w), label=f"wide registers residual {dt} {rows}x{hidden} {block} {fmt}")
 
 
